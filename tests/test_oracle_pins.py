@@ -1,0 +1,376 @@
+"""Pins of the CPU oracle to things other than itself (no GPU needed).
+
+Each test pins one part of oracle/llama.py against a closed form, an invariant the pages
+state, a library routine the special case reduces to (torch / scipy CPU ops), or a number
+the pages print (tests/golden/pages_worked_examples.json).  Together they are meant to make
+a plausible slip anywhere in the oracle fail: a dropped eps or residual, a wrong RoPE sign
+or pairing, a wrong attention scale, mask offset or GQA head map, swapped or transposed
+weights, a wrong SiLU.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import ModelArgs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_worked_examples.json")
+
+
+def small_args(**kw):
+    base = dict(dim=64, n_layers=2, n_heads=4, n_kv_heads=2, vocab_size=97,
+                hidden_dim=oracle.ffn_hidden_dim(64), norm_eps=1e-5, rope_theta=10000.0,
+                max_seq_len=40)
+    base.update(kw)
+    return ModelArgs(**base)
+
+
+def random_weights(a: ModelArgs, seed=0, scale=0.08, dtype=np.float64):
+    rng = np.random.default_rng(seed)
+    hd = a.head_dim
+
+    def m(r, c):
+        return (rng.standard_normal((r, c)) * scale).astype(dtype)
+
+    def v(n):
+        return (1.0 + 0.1 * rng.standard_normal(n)).astype(dtype)
+    layers = []
+    for _ in range(a.n_layers):
+        layers.append(dict(attention_norm=v(a.dim), wq=m(a.n_heads * hd, a.dim),
+                           wk=m(a.kv_heads * hd, a.dim), wv=m(a.kv_heads * hd, a.dim),
+                           wo=m(a.dim, a.n_heads * hd), ffn_norm=v(a.dim),
+                           w1=m(a.hidden_dim, a.dim), w2=m(a.dim, a.hidden_dim),
+                           w3=m(a.hidden_dim, a.dim)))
+    return dict(tok_embeddings=m(a.vocab_size, a.dim) * 10, norm=v(a.dim),
+                output=m(a.vocab_size, a.dim), layers=layers)
+
+
+# ----------------------------------------------------------------------------- pages' numbers
+
+def test_ffn_hidden_rule_matches_pages_cases():
+    g = json.load(open(GOLDEN))["ffn_hidden_rule"]
+    for case in g["cases"]:
+        assert oracle.ffn_hidden_dim(case["dim"]) == case["hidden"]
+    # the rule rounds up, never down, and lands on the multiple
+    for dim in (100, 333, 4096, 8192):
+        h = oracle.ffn_hidden_dim(dim, multiple_of=256)
+        assert h % 256 == 0 and h >= int(8 * dim / 3) and h - int(8 * dim / 3) < 256
+
+
+def test_kv_cache_footprint_worked_example():
+    g = json.load(open(GOLDEN))["kv_cache_7b_example"]
+    per = oracle.kv_cache_bytes(g["max_batch_size"], g["max_seq_len"], g["n_kv_heads"],
+                                g["head_dim"], g["bytes_per_element"])
+    assert per == 64 * 2 ** 20
+    assert abs(per - g["per_tensor_per_layer_bytes_approx"]) / per < 0.05
+    total = per * g["n_layers"] * 2
+    assert total == 4 * 2 ** 30
+    assert abs(total - g["total_k_and_v_bytes_approx"]) / total < 0.08
+
+
+# ----------------------------------------------------------------------------- RMSNorm
+
+def test_rmsnorm_constant_vector_closed_form():
+    eps = 1e-5
+    for c in (1e-3, 0.5, 3.0, -2.0):
+        x = np.full((3, 16), c, dtype=np.float64)
+        w = np.linspace(0.5, 1.5, 16)
+        y = oracle.rms_norm(x, w, eps)
+        np.testing.assert_allclose(y, np.broadcast_to(c / math.sqrt(c * c + eps) * w, y.shape), rtol=1e-14)
+
+
+def test_rmsnorm_matches_torch_library():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 48))
+    w = rng.standard_normal(48)
+    ref = F.rms_norm(torch.from_numpy(x), (48,), torch.from_numpy(w), eps=1e-5).numpy()
+    np.testing.assert_allclose(oracle.rms_norm(x, w, 1e-5), ref, rtol=1e-12, atol=1e-14)
+
+
+def test_rmsnorm_scale_invariance_and_unit_rms():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((4, 64))
+    ones = np.ones(64)
+    y = oracle.rms_norm(x, ones, 0.0)
+    np.testing.assert_allclose(oracle.rms_norm(7.5 * x, ones, 0.0), y, rtol=1e-13)
+    np.testing.assert_allclose(np.mean(y * y, axis=-1), 1.0, rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------- RoPE
+
+def test_rope_position_zero_is_identity():
+    x = np.random.default_rng(3).standard_normal((2, 1, 3, 16))
+    np.testing.assert_array_equal(oracle.apply_rope(x, [0], 10000.0), x)
+
+
+def test_rope_head_dim_2_is_plane_rotation_by_t():
+    x = np.random.default_rng(4).standard_normal((1, 5, 1, 2))
+    pos = [0, 1, 2, 7, 100]
+    y = oracle.apply_rope(x, pos, 10000.0)
+    for s, t in enumerate(pos):
+        z = complex(x[0, s, 0, 0], x[0, s, 0, 1]) * complex(math.cos(t), math.sin(t))
+        assert abs(y[0, s, 0, 0] - z.real) < 1e-12 and abs(y[0, s, 0, 1] - z.imag) < 1e-12
+
+
+def test_rope_is_complex_multiplication_of_adjacent_pairs():
+    """The pages: view q, k as pairs of reals, multiply as complex numbers by e^{i t f}."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 6, 3, 32))
+    pos = list(range(9, 15))
+    ang = torch.from_numpy(oracle.rope_angles(32, pos, 10000.0))
+    table = torch.polar(torch.ones_like(ang), ang)[None, :, None, :]
+    xc = torch.view_as_complex(torch.from_numpy(x).reshape(2, 6, 3, 16, 2).contiguous())
+    ref = torch.view_as_real(xc * table).reshape(2, 6, 3, 32).numpy()
+    np.testing.assert_allclose(oracle.apply_rope(x, pos, 10000.0), ref, atol=1e-13)
+
+
+def test_rope_preserves_norms_and_dot_depends_on_offset_only():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((1, 1, 1, 64))
+    k = rng.standard_normal((1, 1, 1, 64))
+    for t in (0, 5, 3000):
+        qr = oracle.apply_rope(q, [t], 10000.0)
+        pair_norm = np.hypot(qr[..., 0::2], qr[..., 1::2])
+        np.testing.assert_allclose(pair_norm, np.hypot(q[..., 0::2], q[..., 1::2]), rtol=1e-12)
+    d = []
+    for shift in (0, 17, 1000):
+        a = oracle.apply_rope(q, [10 + shift], 10000.0)
+        b = oracle.apply_rope(k, [3 + shift], 10000.0)
+        d.append(float(np.sum(a * b)))
+    np.testing.assert_allclose(d, d[0], rtol=1e-9)
+    # and it does depend on the offset
+    e = float(np.sum(oracle.apply_rope(q, [11], 10000.0) * oracle.apply_rope(k, [3], 10000.0)))
+    assert abs(e - d[0]) > 1e-6
+
+
+# ----------------------------------------------------------------------------- attention
+
+def _sdpa(q, k, v, start_pos):
+    """torch's scaled_dot_product_attention with its repeat-interleave GQA."""
+    S, ctx = q.shape[1], k.shape[1]
+    allowed = torch.arange(ctx)[None, :] <= (start_pos + torch.arange(S))[:, None]
+    t = lambda a: torch.from_numpy(a).permute(0, 2, 1, 3)  # noqa: E731
+    o = F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=allowed, enable_gqa=True)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+@pytest.mark.parametrize("H,KVH,S,start", [(4, 4, 7, 0), (8, 2, 5, 3), (8, 1, 1, 12), (6, 3, 9, 0)])
+def test_attention_matches_torch_sdpa(H, KVH, S, start):
+    rng = np.random.default_rng(7)
+    hd = 16
+    q = rng.standard_normal((2, S, H, hd))
+    k = rng.standard_normal((2, start + S, KVH, hd))
+    v = rng.standard_normal((2, start + S, KVH, hd))
+    out = oracle.attention(q, k, v, start, H // KVH)
+    np.testing.assert_allclose(out, _sdpa(q, k, v, start), rtol=1e-11, atol=1e-12)
+
+
+def test_attention_single_visible_key_returns_its_value():
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((1, 3, 2, 8))
+    k = rng.standard_normal((1, 3, 2, 8))
+    v = rng.standard_normal((1, 3, 2, 8))
+    out = oracle.attention(q, k, v, 0, 1)
+    np.testing.assert_allclose(out[:, 0], v[:, 0], rtol=1e-14)
+
+
+def test_attention_zero_query_averages_visible_values():
+    rng = np.random.default_rng(9)
+    S, start = 4, 2
+    q = np.zeros((1, S, 2, 8))
+    k = rng.standard_normal((1, start + S, 1, 8))
+    v = rng.standard_normal((1, start + S, 1, 8))
+    out = oracle.attention(q, k, v, start, 2)
+    for i in range(S):
+        np.testing.assert_allclose(out[0, i, 0], v[0, :start + i + 1, 0].mean(0), rtol=1e-12)
+
+
+def test_mask_shape_and_entries():
+    m = oracle.causal_mask(3, 2)
+    assert m.shape == (3, 5)
+    assert np.isneginf(m[0, 3]) and m[0, 2] == 0 and m[2, 4] == 0
+    assert (m[:, :2] == 0).all()
+
+
+# ----------------------------------------------------------------------------- SwiGLU
+
+def test_silu_matches_library_routines():
+    x = np.linspace(-30, 30, 601)
+    np.testing.assert_allclose(oracle.silu(x), x * scipy.special.expit(x), rtol=1e-12, atol=1e-300)
+    np.testing.assert_allclose(oracle.silu(x), F.silu(torch.from_numpy(x)).numpy(), rtol=1e-12, atol=1e-14)
+    assert oracle.silu(np.array([-200.0], dtype=np.float32))[0] == 0.0
+
+
+def test_feed_forward_gate_zero_and_linear_orientation():
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((3, 16))
+    w1, w3 = rng.standard_normal((24, 16)), rng.standard_normal((24, 16))
+    w2 = rng.standard_normal((16, 24))
+    assert np.all(oracle.feed_forward(x, w1, w2, np.zeros_like(w3)) == 0)
+    X, W1, W2, W3 = map(torch.from_numpy, (x, w1, w2, w3))
+    ref = F.linear(F.silu(F.linear(X, W1)) * F.linear(X, W3), W2).numpy()
+    np.testing.assert_allclose(oracle.feed_forward(x, w1, w2, w3), ref, rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------- whole model
+
+def torch_model_forward(a: ModelArgs, W: dict, tokens: np.ndarray) -> np.ndarray:
+    """The pre-norm block of the pages composed from torch library routines (F.embedding,
+    F.rms_norm, F.linear, complex RoPE via torch.polar, SDPA with repeat-interleave GQA,
+    F.silu), fp64, one causal pass from position 0."""
+    t = lambda x: torch.from_numpy(np.asarray(x, dtype=np.float64))  # noqa: E731
+    B, S = tokens.shape
+    hd = a.head_dim
+    freqs = 1.0 / (a.rope_theta ** (torch.arange(0, hd, 2, dtype=torch.float64) / hd))
+    ang = torch.outer(torch.arange(S, dtype=torch.float64), freqs)
+    cis = torch.polar(torch.ones_like(ang), ang)[None, :, None, :]
+
+    def rope(x):
+        xc = torch.view_as_complex(x.reshape(*x.shape[:-1], -1, 2).contiguous())
+        return torch.view_as_real(xc * cis).reshape(x.shape)
+    h = F.embedding(torch.from_numpy(tokens), t(W["tok_embeddings"]))
+    for L in W["layers"]:
+        x = F.rms_norm(h, (a.dim,), t(L["attention_norm"]), eps=a.norm_eps)
+        q = rope(F.linear(x, t(L["wq"])).view(B, S, a.n_heads, hd))
+        k = rope(F.linear(x, t(L["wk"])).view(B, S, a.kv_heads, hd))
+        v = F.linear(x, t(L["wv"])).view(B, S, a.kv_heads, hd)
+        o = F.scaled_dot_product_attention(q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2),
+                                           is_causal=True, enable_gqa=True)
+        h = h + F.linear(o.transpose(1, 2).reshape(B, S, -1), t(L["wo"]))
+        x = F.rms_norm(h, (a.dim,), t(L["ffn_norm"]), eps=a.norm_eps)
+        h = h + F.linear(F.silu(F.linear(x, t(L["w1"]))) * F.linear(x, t(L["w3"])), t(L["w2"]))
+    x = F.rms_norm(h, (a.dim,), t(W["norm"]), eps=a.norm_eps)
+    return F.linear(x, t(W["output"])).numpy()
+
+
+@pytest.mark.parametrize("kvh", [4, 2, 1])
+def test_model_matches_torch_library_composition(kvh):
+    a = small_args(n_kv_heads=kvh)
+    W = random_weights(a, seed=11)
+    tokens = np.random.default_rng(12).integers(0, a.vocab_size, size=(2, 9))
+    ref = torch_model_forward(a, W, tokens)
+    got = oracle.Oracle(a, W, 2, dtype=np.float64).forward(tokens, 0)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(oracle.teacher_forced_logits(a, W, tokens, np.float64), ref,
+                               rtol=1e-10, atol=1e-10)
+
+
+def test_identity_blocks_closed_form():
+    """wo = w2 = 0 makes each block the identity: logits = Wout (rmsnorm(E[tok]) * w_norm)."""
+    a = small_args()
+    W = random_weights(a, seed=13)
+    for L in W["layers"]:
+        L["wo"][:] = 0
+        L["w2"][:] = 0
+    tokens = np.array([[3, 50, 7, 7]])
+    E, wn, Wout = W["tok_embeddings"], W["norm"], W["output"]
+    x = E[tokens]
+    expect = (x / np.sqrt(np.mean(x * x, -1, keepdims=True) + a.norm_eps) * wn) @ Wout.T
+    got = oracle.Oracle(a, W, 1, dtype=np.float64).forward(tokens, 0)
+    np.testing.assert_allclose(got, expect, rtol=1e-12, atol=1e-13)
+
+
+def test_gqa_equals_mha_with_repeat_interleaved_kv_weights():
+    a = small_args(n_kv_heads=2)
+    W = random_weights(a, seed=14)
+    m = small_args(n_kv_heads=4)
+    Wm = {k: v for k, v in W.items() if k != "layers"}
+    Wm["layers"] = []
+    hd, n_rep = a.head_dim, a.n_rep
+    for L in W["layers"]:
+        L2 = dict(L)
+        for n in ("wk", "wv"):
+            blocks = L[n].reshape(a.kv_heads, hd, a.dim)
+            L2[n] = np.repeat(blocks, n_rep, axis=0).reshape(a.n_heads * hd, a.dim)
+        Wm["layers"].append(L2)
+    tokens = np.random.default_rng(15).integers(0, a.vocab_size, size=(2, 6))
+    g = oracle.Oracle(a, W, 2, dtype=np.float64).forward(tokens, 0)
+    h = oracle.Oracle(m, Wm, 2, dtype=np.float64).forward(tokens, 0)
+    np.testing.assert_allclose(g, h, rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_equals_incremental_decode_and_chunked_prefill():
+    """The mask's (seqlen, start_pos+seqlen) form is what lets the cache stream: the same
+    tokens give the same logits whether fed at once, in chunks, or one by one."""
+    a = small_args()
+    W = random_weights(a, seed=16)
+    tokens = np.random.default_rng(17).integers(0, a.vocab_size, size=(2, 12))
+    full = oracle.Oracle(a, W, 2, dtype=np.float64).forward(tokens, 0)
+    inc = oracle.Oracle(a, W, 2, dtype=np.float64)
+    steps = [inc.forward(tokens[:, j:j + 1], j)[:, 0] for j in range(12)]
+    np.testing.assert_allclose(np.stack(steps, 1), full, rtol=1e-9, atol=1e-9)
+    ch = oracle.Oracle(a, W, 2, dtype=np.float64)
+    parts = [ch.forward(tokens[:, 0:5], 0), ch.forward(tokens[:, 5:12], 5)]
+    np.testing.assert_allclose(np.concatenate(parts, 1), full, rtol=1e-9, atol=1e-9)
+
+
+def test_causality_and_batch_row_independence():
+    a = small_args()
+    W = random_weights(a, seed=18)
+    rng = np.random.default_rng(19)
+    tokens = rng.integers(0, a.vocab_size, size=(3, 8))
+    base = oracle.Oracle(a, W, 3, dtype=np.float64).forward(tokens, 0)
+    t2 = tokens.copy()
+    t2[:, 5:] = (t2[:, 5:] + 1) % a.vocab_size
+    pert = oracle.Oracle(a, W, 3, dtype=np.float64).forward(t2, 0)
+    np.testing.assert_allclose(pert[:, :5], base[:, :5], rtol=1e-13, atol=1e-13)
+    assert np.abs(pert[:, 5:] - base[:, 5:]).max() > 1e-6
+    alone = oracle.Oracle(a, W, 1, dtype=np.float64).forward(tokens[1:2], 0)
+    np.testing.assert_allclose(alone[0], base[1], rtol=1e-12, atol=1e-12)
+
+
+def test_fp32_oracle_close_to_fp64_on_tiny_workload():
+    import synth
+    wl = synth.WORKLOADS["tiny_fp32"]
+    a = oracle.args_from_workload(wl)
+    W = synth.gen_weights(wl)
+    pr = synth.prompts(wl)
+    tokens = np.array(pr)
+    l32 = oracle.teacher_forced_logits(a, W, tokens, np.float32)
+    l64 = oracle.teacher_forced_logits(a, W, tokens, np.float64)
+    assert np.abs(l32 - l64).max() < 1e-5
+
+
+# ----------------------------------------------------------------------------- greedy / generate
+
+def test_argmax_ties_go_to_lowest_index_and_nan_rejected():
+    x = np.array([[1.0, 3.0, 3.0, 2.0], [5.0, 5.0, 5.0, 5.0]])
+    assert oracle.argmax_lowest(x).tolist() == [1, 0]
+    with pytest.raises(ValueError):
+        oracle.argmax_lowest(np.array([1.0, np.nan]))
+
+
+def test_generate_keeps_prompts_and_matches_teacher_forcing():
+    a = small_args()
+    W = random_weights(a, seed=20)
+    prompts = [[5, 9, 11, 2, 40, 41, 42], [7, 8, 9]]
+    model = oracle.Oracle(a, W, 2, dtype=np.float64)
+    tokens, step_logits = oracle.greedy_generate(model, prompts, max_gen_len=6)
+    total = min(a.max_seq_len, 6 + 7)
+    assert tokens.shape == (2, total)
+    assert tokens[0, :7].tolist() == prompts[0] and tokens[1, :3].tolist() == prompts[1]
+    assert len(step_logits) == total - 3
+    tf = oracle.teacher_forced_logits(a, W, tokens[:, :-1], np.float64)
+    for i, cur in enumerate(range(3, total)):
+        np.testing.assert_allclose(step_logits[i], tf[:, cur - 1], rtol=1e-9, atol=1e-9)
+        expect = np.argmax(tf[:, cur - 1], -1)
+        for b, p in enumerate(prompts):
+            if cur >= len(p):
+                assert tokens[b, cur] == expect[b]
+
+
+def test_generate_stops_when_every_row_hit_eos():
+    a = small_args()
+    W = random_weights(a, seed=21)
+    model = oracle.Oracle(a, W, 1, dtype=np.float64)
+    tokens, _ = oracle.greedy_generate(model, [[1, 2, 3]], max_gen_len=8)
+    first = int(tokens[0, 3])
+    model = oracle.Oracle(a, W, 1, dtype=np.float64)
+    tokens2, logits2 = oracle.greedy_generate(model, [[1, 2, 3]], max_gen_len=8, eos_id=first)
+    assert len(logits2) == 1 and tokens2[0, 3] == first
