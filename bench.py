@@ -1,0 +1,251 @@
+"""Throughput of the Llama 2 decoder forward on one MI355X: greedy generate at the 7B shape.
+
+One step = one whole greedy generate of the workload (prefill of the prompt batch, then one
+single-token decode call per generated position, each followed by the on-device argmax and
+token select), with weights, prompts and KV cache already resident in HBM.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--skip-cpu-baseline]
+
+Prints one JSON line.  `value` is decode tokens/s (batch * decode calls / decode time);
+prefill tokens/s (batch * prompt_len / prefill time) is reported beside it.  `roofline` is
+the dominant decode kernel (the fused RMSNorm + [w1;w3] + SiLU-gate GEMV, 44.6% of the
+bytes a 7B decode step streams): algorithmic bytes per launch over its average launch
+duration, timed live with HIP events on the launch stream.  `cpu_baseline` is the NumPy
+oracle on this host's cores over a bounded sample (2 of the layers, scaled to all).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "decode tok/s + prefill tok/s, 7B shape, 1 MI355X; % HBM / MFMA roofline"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def decode_step_bytes(wl, ctx: int) -> float:
+    """Algorithmic HBM bytes of one decode call at context length ctx (weights once, K/V of
+    positions [0, ctx) read, one position written)."""
+    D, L, F, V = wl.dim, wl.n_layers, wl.hidden_dim, wl.vocab_size
+    hd, H, KVH, B = wl.head_dim, wl.n_heads, wl.n_kv_heads, wl.batch
+    e = 2 if wl.dtype == "bf16" else 4
+    per_layer = (H * hd * D + 2 * KVH * hd * D + D * H * hd + 3 * F * D + 2 * D) * e
+    weights = L * per_layer + V * D * e + D * e + B * D * e
+    kv = B * L * 2 * KVH * hd * e * (ctx + 1)
+    return weights + kv
+
+
+def prefill_flops(wl, B: int, S: int) -> float:
+    D, L, F, V = wl.dim, wl.n_layers, wl.hidden_dim, wl.vocab_size
+    hd, H, KVH = wl.head_dim, wl.n_heads, wl.n_kv_heads
+    per_layer = H * hd * D + 2 * KVH * hd * D + D * H * hd + 3 * F * D
+    return 2.0 * B * S * per_layer * L + 4.0 * hd * H * L * B * S * (S + 1) / 2 + 2.0 * B * V * D
+
+
+def w13_launch_bytes(wl) -> float:
+    """Per launch of the decode [w1;w3] GEMV: both weight matrices, the norm weight, the
+    residual rows read and the gated rows written."""
+    e = 2 if wl.dtype == "bf16" else 4
+    return 2 * wl.hidden_dim * wl.dim * e + wl.dim * e + wl.batch * wl.dim * 4 + wl.batch * wl.hidden_dim * 4
+
+
+def cpu_baseline(wl, dev_weights, prompts, sample_layers: int = 2, decode_steps: int = 4) -> dict:
+    """The oracle as it stands, on this host, over a bounded sample: the first
+    `sample_layers` layers over the full prompt (prefill) and `decode_steps` incremental
+    steps, plus the head (final norm + vocab projection) timed alone; layer time is scaled
+    to all layers."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count()
+
+    def hostw(name, layer):
+        t = dev_weights[name] if layer < 0 else dev_weights["layers"][layer][name]
+        return t.float().cpu().numpy()
+    cache = {}
+
+    def provider(name, layer):
+        k = (name, layer)
+        if k not in cache:
+            cache[k] = hostw(name, layer)
+        return cache[k]
+    tok = np.array([p[:min(len(x) for x in prompts)] for p in prompts])
+    B, S = tok.shape
+    base = oracle.args_from_workload(wl)
+    import dataclasses
+
+    def timed(n_layers):
+        a = dataclasses.replace(base, n_layers=n_layers, max_seq_len=S + decode_steps + 1)
+        m = oracle.Oracle(a, provider, B, np.float32)
+        t0 = time.perf_counter()
+        m.forward(tok, 0)
+        t1 = time.perf_counter()
+        nxt = tok[:, -1:]
+        for j in range(decode_steps):
+            m.forward(nxt, S + j)
+        t2 = time.perf_counter()
+        return t1 - t0, (t2 - t1) / decode_steps
+    timed(0)                                # warm the weight cache / BLAS
+    timed(sample_layers)
+    head_p, head_d = timed(0)
+    lay_p, lay_d = timed(sample_layers)
+    scale = wl.n_layers / sample_layers
+    t_prefill = head_p + (lay_p - head_p) * scale
+    t_decode = head_d + (lay_d - head_d) * scale
+    return {"value": B / t_decode, "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "prefill_tok_per_s": B * S / t_prefill,
+            "sample": (f"{wl.name}: oracle fp32 NumPy, {sample_layers} of {wl.n_layers} layers over the "
+                       f"{S}-token prefill and {decode_steps} decode steps, head timed alone, layer time "
+                       f"scaled x{scale:g}; host cpu_count={os.cpu_count()}")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="llama2_7b_b1")
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-class", default="gemv_w13")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    from decoder_only_transformer_amd import abi, runtime
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    abi.lib()
+    wl = synth.WORKLOADS[args.workload]
+    log(f"[bench] workload {wl}")
+    t0 = time.time()
+    W = synth.gen_weights(wl, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] weights generated on device in {time.time() - t0:.1f}s")
+    prompts = synth.prompts(wl)
+    model = runtime.LlamaModel(runtime.make_args(
+        wl.dim, wl.n_layers, wl.n_heads, wl.n_kv_heads, wl.vocab_size, wl.hidden_dim,
+        wl.norm_eps, wl.rope_theta, wl.batch, wl.max_seq_len, wl.dtype), W)
+    run = runtime.GreedyRun(model, prompts, wl.gen_steps, keep_logits=False)
+    B, S, n_dec = run.bsz, run.min_len, run.n_calls - 1
+
+    def one_step(ev=None):
+        run.reset()
+        if ev:
+            ev[0].record()
+        run.prefill()
+        if ev:
+            ev[1].record()
+        for i in range(1, run.n_calls):
+            run.decode(i)
+        if ev:
+            ev[2].record()
+
+    for w in range(args.warmup):
+        one_step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {w + 1}/{args.warmup} done")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        one_step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs)
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs)
+    log(f"[bench] timed {args.steps} steps: wall {wall:.3f}s prefill {pre_ms / args.steps:.3f} ms/step "
+        f"decode {dec_ms / args.steps:.3f} ms/step")
+    decode_tps = B * n_dec * args.steps / (dec_ms / 1e3)
+    prefill_tps = B * S * args.steps / (pre_ms / 1e3)
+    dec_bytes = sum(decode_step_bytes(wl, S + i) for i in range(n_dec))
+    decode_hbm_frac = dec_bytes * args.steps / (dec_ms / 1e3) / (HBM_PEAK_GBS * 1e9)
+    pf = prefill_flops(wl, B, S)
+    prefill_tflops = pf * args.steps / (pre_ms / 1e3) / 1e12
+
+    # Live per-kernel timing of the dominant decode kernel, same launch configuration.
+    kc = abi.KERNEL_CLASSES[args.profile_class]
+    runtime.check("profile_select", abi.llama_profile_select(model.ctx, kc))
+    one_step()
+    torch.cuda.synchronize()
+    st, n_launch, k_ms = abi.llama_profile_read(model.ctx)
+    runtime.check("profile_read", st)
+    abi.llama_profile_select(model.ctx, 0)
+    avg_us = k_ms / max(n_launch, 1) * 1e3
+    per_launch = w13_launch_bytes(wl)
+    achieved = per_launch / (avg_us * 1e-6) / 1e9
+    log(f"[bench] {args.profile_class}: {n_launch} launches, avg {avg_us:.2f} us, "
+        f"{per_launch / 1e6:.1f} MB/launch -> {achieved:.0f} GB/s")
+
+    # Plain device copy for context (bandwidth the HBM actually gives a trivial kernel).
+    buf = torch.empty(2 * 1024 ** 3, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(buf)
+    dst.copy_(buf)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(buf)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * buf.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del buf, dst
+
+    cpu = None
+    if not args.skip_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        t0 = time.time()
+        cpu = cpu_baseline(wl, W, prompts)
+        log(f"[bench] cpu baseline done in {time.time() - t0:.1f}s")
+
+    out = {
+        "metric": METRIC,
+        "value": round(decode_tps, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round((pre_ms + dec_ms) / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic: seeded N(0,0.02) weights, uniform random prompt ids",
+        "config": {"workload": wl.name, "batch": B, "prompt_len": S, "decode_calls": n_dec,
+                   "dim": wl.dim, "n_layers": wl.n_layers, "n_heads": wl.n_heads,
+                   "n_kv_heads": wl.n_kv_heads, "hidden_dim": wl.hidden_dim, "vocab": wl.vocab_size},
+        "decode_tok_per_s": round(decode_tps, 2),
+        "prefill_tok_per_s": round(prefill_tps, 1),
+        "decode_ms_per_call": round(dec_ms / args.steps / n_dec, 4),
+        "prefill_ms": round(pre_ms / args.steps, 3),
+        "decode_hbm_frac": round(decode_hbm_frac, 4),
+        "prefill_tflops": round(prefill_tflops, 2),
+        "prefill_mfma_frac": round(prefill_tflops / BF16_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": args.profile_class, "launches": n_launch, "avg_us": round(avg_us, 3),
+                     "bytes_per_launch": per_launch},
+        "copy_kernel_gbs": round(copy_gbs, 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    model.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,81 @@
+// Launch interface between the host library (llama_api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace llk {
+
+enum Epilogue : int {
+    EPI_QKV = 0,     // rows of [wq; wk; wv]: RoPE on q and k, q -> q buffer, k/v -> KV cache
+    EPI_RESID = 1,   // resid[m][n] += y
+    EPI_SWIGLU = 2,  // out[m][n] = silu(x.w1[n]) * (x.w3[n])
+    EPI_STORE = 3    // out[m][n] = y (fp32 logits)
+};
+
+// Row m of a call covers token (b = m / seqlen, position start_pos + m % seqlen).
+struct QkvTarget {
+    float* q;              // [M][nq] fp32
+    void* cache_k;         // this layer's K cache base: [max_batch][max_seq][n_kv_heads][head_dim]
+    void* cache_v;
+    const float2* rope;    // [max_seq][head_dim/2] (cos, sin)
+    int nq, nk;            // rows of wq and of wk (= n_heads*hd, n_kv_heads*hd)
+    int head_dim;
+    int max_seq;
+    int start_pos, seqlen;
+};
+
+// y[m][n] = sum_k x[m][k] * W[n][k]  (VALU, fp32 activations, weights streamed once per
+// M-chunk).  With norm_w, x is RMS-normalised on the fly: x * rsqrt(mean(x^2)+eps) * norm_w.
+struct GemvArgs {
+    const float* x; int64_t ldx;
+    int M, K, N;           // N = output columns (SWIGLU: hidden units)
+    const void* norm_w; float eps;
+    const void* w0;        // [N][K] (QKV: wq; SWIGLU: w1)
+    const void* w1;        // QKV: wk; SWIGLU: w3
+    const void* w2;        // QKV: wv
+    float* out; int64_t ldo;
+    float* resid; int64_t ldr;
+    QkvTarget qkv;
+};
+
+// C[m][n] = sum_k A[m][k] * W[n][k] on bf16 MFMA, fp32 accumulate.  A bf16 [M][lda].
+struct GemmArgs {
+    const void* a; int64_t lda;
+    int M, K, N;           // N = output columns (SWIGLU: hidden units)
+    const void* w0; const void* w1; const void* w2;
+    float* out; int64_t ldo;       // STORE (fp32)
+    void* out16; int64_t ldo16;    // SWIGLU (bf16)
+    float* resid; int64_t ldr;
+    QkvTarget qkv;
+};
+
+// Causal attention for a set of query rows against the KV cache (one query position per
+// row, all n_rep heads of one kv head per workgroup, keys split over gridDim.x).
+struct AttnArgs {
+    const float* q;        // [rows][n_heads*hd] fp32 (RoPE applied)
+    const void* cache_k;   // layer base
+    const void* cache_v;
+    void* out;             // [rows][n_heads*hd], fp32 or bf16 (out_bf16)
+    int out_bf16;
+    float* part;           // [rows][n_heads][n_split][hd + 2] partials when n_split > 1
+    int rows, n_heads, n_kv_heads, head_dim, max_seq;
+    int row0;              // first row of this launch (launches are split at 65535 rows)
+    int start_pos, seqlen; // row t -> b = t / seqlen, position start_pos + t % seqlen
+    int n_split, chunk;    // keys per split (multiple of 16)
+    float scale;           // 1/sqrt(head_dim)
+};
+
+hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, const void* table,
+                        int wbf16, int vocab, int dim, float* h, hipStream_t s);
+hipError_t launch_rmsnorm_bf16(const float* h, int64_t ldh, int rows, int dim, const void* w,
+                               float eps, void* out, int64_t ldo, hipStream_t s);
+hipError_t launch_gemv(int wbf16, int epi, const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
+hipError_t launch_attn_rows(int kv_bf16, const AttnArgs& a, hipStream_t s);
+hipError_t launch_argmax(const float* logits, int bsz, int vocab, int64_t stride, int32_t* out,
+                         hipStream_t s);
+hipError_t launch_select(const int32_t* next, int32_t* tokens, int64_t ld, int cur_pos,
+                         const int32_t* prompt_len, int bsz, hipStream_t s);
+
+}  // namespace llk

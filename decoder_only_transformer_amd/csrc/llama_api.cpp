@@ -1,0 +1,452 @@
+// Host side of the C ABI declared in include/llama_mi355x.h: argument validation, workspace
+// carve-up, RoPE table, and the per-call launch plan of Transformer.forward.
+//
+// Launch plan ("Llama 2 Reference Implementation -- Administrator & Developer Guide",
+// section 8.4: embed -> n_layers pre-norm blocks -> final norm -> output projection):
+//   prefill, bf16:  embed | per layer: rmsnorm->bf16, MFMA [wq;wk;wv] (+RoPE, KV append),
+//                   attention, MFMA wo (+residual), rmsnorm->bf16, MFMA [w1;w3] (+SiLU gate),
+//                   MFMA w2 (+residual) | final norm fused into the vocab projection.
+//   decode (and the fp32 path): embed | per layer: GEMV [wq;wk;wv] with fused RMSNorm,
+//                   split attention (+merge), GEMV wo (+residual), GEMV [w1;w3] with fused
+//                   RMSNorm (+SiLU gate), GEMV w2 (+residual) | fused final norm + vocab GEMV.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/llama_mi355x.h"
+#include "kernels.h"
+
+using namespace llk;
+
+namespace {
+
+constexpr int kMaxSplit = 32;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    size_t k_cache, v_cache, rope, h32, q32, o32, g32, act16, g16, part, total;
+    size_t kv_layer_elems;   // elements of one layer's K (or V) cache
+};
+
+int head_dim_of(const llama_args& a) { return a.dim / a.n_heads; }
+
+llama_status check_args(const llama_args* a) {
+    if (!a) return LLAMA_ERR_INVALID_ARG;
+    if (a->dim <= 0 || a->n_layers <= 0 || a->n_heads <= 0 || a->n_kv_heads <= 0 ||
+        a->vocab_size <= 0 || a->hidden_dim <= 0 || a->max_batch_size <= 0 ||
+        a->max_seq_len <= 0)
+        return LLAMA_ERR_INVALID_ARG;
+    if (!(a->norm_eps >= 0.f) || !(a->rope_theta > 0.f)) return LLAMA_ERR_INVALID_ARG;
+    if (a->dtype != LLAMA_BF16 && a->dtype != LLAMA_FP32) return LLAMA_ERR_INVALID_ARG;
+    if (a->dim % a->n_heads != 0) return LLAMA_ERR_INVALID_ARG;
+    if (a->n_heads % a->n_kv_heads != 0) return LLAMA_ERR_INVALID_ARG;
+    const int hd = head_dim_of(*a);
+    if (hd != 32 && hd != 64 && hd != 128) return LLAMA_ERR_UNSUPPORTED;
+    const int n_rep = a->n_heads / a->n_kv_heads;
+    if (n_rep != 1 && n_rep != 2 && n_rep != 4 && n_rep != 8) return LLAMA_ERR_UNSUPPORTED;
+    if (a->dim % 64 != 0 || a->hidden_dim % 64 != 0 || (a->n_heads * hd) % 64 != 0)
+        return LLAMA_ERR_UNSUPPORTED;
+    if (a->vocab_size % 2 != 0) return LLAMA_ERR_UNSUPPORTED;
+    if (a->max_seq_len > 65536) return LLAMA_ERR_UNSUPPORTED;
+    return LLAMA_OK;
+}
+
+Layout layout_of(const llama_args& a) {
+    Layout L{};
+    const size_t esz = a.dtype == LLAMA_BF16 ? 2 : 4;
+    const size_t hd = head_dim_of(a);
+    const size_t nq = (size_t)a.n_heads * hd;
+    const size_t maxB = a.max_batch_size, maxS = a.max_seq_len;
+    const size_t maxT = maxB * maxS;
+    const bool fp32 = a.dtype == LLAMA_FP32;
+    const size_t rows32 = fp32 ? maxT : maxB;
+    L.kv_layer_elems = maxB * maxS * (size_t)a.n_kv_heads * hd;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    L.k_cache = take(L.kv_layer_elems * a.n_layers * esz);
+    L.v_cache = take(L.kv_layer_elems * a.n_layers * esz);
+    L.rope = take(maxS * (hd / 2) * sizeof(float) * 2);
+    L.h32 = take(maxT * a.dim * sizeof(float));
+    L.q32 = take(maxT * nq * sizeof(float));
+    L.o32 = take(rows32 * nq * sizeof(float));
+    L.g32 = take(rows32 * (size_t)a.hidden_dim * sizeof(float));
+    L.act16 = fp32 ? off : take(maxT * (size_t)(a.dim > (int)nq ? a.dim : (int)nq) * 2);
+    L.g16 = fp32 ? off : take(maxT * (size_t)a.hidden_dim * 2);
+    L.part = take(maxB * (size_t)a.n_heads * kMaxSplit * (hd + 2) * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+struct llama_ctx {
+    llama_args a;
+    llama_weights w;
+    std::vector<llama_layer_weights> layers;
+    Layout L;
+    char* ws;
+    int hd, nq, nk;
+    bool bf16;
+
+    // diagnostics: events bracketing launches of one kernel class
+    int prof_class = 0;
+    std::vector<hipEvent_t> ev;     // pairs (start, stop)
+    size_t ev_used = 0;
+    bool ev_failed = false;
+
+    template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
+    size_t esz() const { return bf16 ? 2 : 4; }
+    void* kcache(int l) const { return ws + L.k_cache + (size_t)l * L.kv_layer_elems * esz(); }
+    void* vcache(int l) const { return ws + L.v_cache + (size_t)l * L.kv_layer_elems * esz(); }
+};
+
+#define HIP_TRY(expr)                                   \
+    do {                                                \
+        if ((expr) != hipSuccess) return LLAMA_ERR_HIP; \
+    } while (0)
+
+namespace {
+
+// Records a diagnostics event if launches of class `kc` are being bracketed.
+void prof_mark(llama_ctx* c, int kc, hipStream_t s) {
+    if (c->prof_class != kc || kc == 0) return;
+    if (c->ev_used == c->ev.size()) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) {
+            c->ev_failed = true;
+            return;
+        }
+        c->ev.push_back(e);
+    }
+    if (hipEventRecord(c->ev[c->ev_used++], s) != hipSuccess) c->ev_failed = true;
+}
+
+}  // namespace
+
+// Launch `expr` (a hipError_t expression) bracketed for kernel class kc.
+#define LAUNCH(c, kc, s, expr)                                 \
+    do {                                                       \
+        prof_mark(const_cast<llama_ctx*>(c), (kc), (s));      \
+        const hipError_t e_ = (expr);                          \
+        prof_mark(const_cast<llama_ctx*>(c), (kc), (s));      \
+        if (e_ != hipSuccess) return LLAMA_ERR_HIP;            \
+    } while (0)
+
+namespace {
+
+QkvTarget qkv_target(const llama_ctx* c, int l, int start_pos, int seqlen) {
+    QkvTarget t{};
+    t.q = c->at<float>(c->L.q32);
+    t.cache_k = c->kcache(l);
+    t.cache_v = c->vcache(l);
+    t.rope = c->at<const float2>(c->L.rope);
+    t.nq = c->nq;
+    t.nk = c->nk;
+    t.head_dim = c->hd;
+    t.max_seq = c->a.max_seq_len;
+    t.start_pos = start_pos;
+    t.seqlen = seqlen;
+    return t;
+}
+
+// Attention over `rows` query rows (row t = batch t / seqlen, position start_pos + t % seqlen).
+llama_status run_attention(const llama_ctx* c, int l, int rows, int seqlen, int start_pos,
+                           void* out, bool out_bf16, bool allow_split, hipStream_t s) {
+    AttnArgs at{};
+    at.q = c->at<const float>(c->L.q32);
+    at.cache_k = c->kcache(l);
+    at.cache_v = c->vcache(l);
+    at.out = out;
+    at.out_bf16 = out_bf16 ? 1 : 0;
+    at.part = c->at<float>(c->L.part);
+    at.rows = rows;
+    at.n_heads = c->a.n_heads;
+    at.n_kv_heads = c->a.n_kv_heads;
+    at.head_dim = c->hd;
+    at.max_seq = c->a.max_seq_len;
+    at.start_pos = start_pos;
+    at.seqlen = seqlen;
+    at.scale = 1.0f / std::sqrt((float)c->hd);
+    const int ctx = start_pos + seqlen;   // longest visible prefix among the rows
+    int n_split = 1;
+    if (allow_split) {
+        const int base = rows * c->a.n_kv_heads;
+        const int want = (1024 + base - 1) / base;
+        const int by_len = (ctx + 63) / 64;
+        n_split = std::max(1, std::min(kMaxSplit, std::min(want, by_len)));
+    }
+    int chunk = (ctx + n_split - 1) / n_split;
+    chunk = (chunk + 15) / 16 * 16;
+    n_split = (ctx + chunk - 1) / chunk;
+    at.n_split = n_split;
+    at.chunk = chunk;
+    LAUNCH(c, seqlen == 1 ? LLAMA_KC_ATTN_DECODE : LLAMA_KC_ATTN_PREFILL, s, launch_attn_rows(c->bf16 ? 1 : 0, at, s));
+    return LLAMA_OK;
+}
+
+// One transformer block on the GEMV (VALU) path for M activation rows.
+llama_status block_gemv(const llama_ctx* c, int l, int M, int seqlen, int start_pos,
+                        bool allow_split, hipStream_t s) {
+    const llama_layer_weights& W = c->layers[l];
+    const int D = c->a.dim, F = c->a.hidden_dim;
+    float* h = c->at<float>(c->L.h32);
+    float* o32 = c->at<float>(c->L.o32);
+    float* g32 = c->at<float>(c->L.g32);
+    const int wb = c->bf16 ? 1 : 0;
+
+    GemvArgs g{};
+    g.x = h; g.ldx = D; g.M = M; g.K = D; g.N = c->nq + 2 * c->nk;
+    g.norm_w = W.attention_norm; g.eps = c->a.norm_eps;
+    g.w0 = W.wq; g.w1 = W.wk; g.w2 = W.wv;
+    g.qkv = qkv_target(c, l, start_pos, seqlen);
+    LAUNCH(c, LLAMA_KC_GEMV_QKV, s, launch_gemv(wb, EPI_QKV, g, s));
+
+    llama_status st = run_attention(c, l, M, seqlen, start_pos, o32, false, allow_split, s);
+    if (st != LLAMA_OK) return st;
+
+    g = GemvArgs{};
+    g.x = o32; g.ldx = c->nq; g.M = M; g.K = c->nq; g.N = D;
+    g.w0 = W.wo; g.resid = h; g.ldr = D;
+    LAUNCH(c, LLAMA_KC_GEMV_WO, s, launch_gemv(wb, EPI_RESID, g, s));
+
+    g = GemvArgs{};
+    g.x = h; g.ldx = D; g.M = M; g.K = D; g.N = F;
+    g.norm_w = W.ffn_norm; g.eps = c->a.norm_eps;
+    g.w0 = W.w1; g.w1 = W.w3; g.out = g32; g.ldo = F;
+    LAUNCH(c, LLAMA_KC_GEMV_W13, s, launch_gemv(wb, EPI_SWIGLU, g, s));
+
+    g = GemvArgs{};
+    g.x = g32; g.ldx = F; g.M = M; g.K = F; g.N = D;
+    g.w0 = W.w2; g.resid = h; g.ldr = D;
+    LAUNCH(c, LLAMA_KC_GEMV_W2, s, launch_gemv(wb, EPI_RESID, g, s));
+    return LLAMA_OK;
+}
+
+// One transformer block on the bf16 MFMA path for T = bsz*seqlen prefill rows.
+llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_pos, hipStream_t s) {
+    const llama_layer_weights& W = c->layers[l];
+    const int D = c->a.dim, F = c->a.hidden_dim;
+    float* h = c->at<float>(c->L.h32);
+    void* act = c->at<void>(c->L.act16);
+    void* g16 = c->at<void>(c->L.g16);
+
+    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.attention_norm, c->a.norm_eps, act, D, s));
+    GemmArgs g{};
+    g.a = act; g.lda = D; g.M = T; g.K = D; g.N = c->nq + 2 * c->nk;
+    g.w0 = W.wq; g.w1 = W.wk; g.w2 = W.wv;
+    g.qkv = qkv_target(c, l, start_pos, seqlen);
+    LAUNCH(c, LLAMA_KC_GEMM_QKV, s, launch_gemm(EPI_QKV, g, s));
+
+    llama_status st = run_attention(c, l, T, seqlen, start_pos, act, true, false, s);
+    if (st != LLAMA_OK) return st;
+
+    g = GemmArgs{};
+    g.a = act; g.lda = c->nq; g.M = T; g.K = c->nq; g.N = D;
+    g.w0 = W.wo; g.resid = h; g.ldr = D;
+    LAUNCH(c, LLAMA_KC_GEMM_WO, s, launch_gemm(EPI_RESID, g, s));
+
+    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.ffn_norm, c->a.norm_eps, act, D, s));
+    g = GemmArgs{};
+    g.a = act; g.lda = D; g.M = T; g.K = D; g.N = F;
+    g.w0 = W.w1; g.w1 = W.w3; g.out16 = g16; g.ldo16 = F;
+    LAUNCH(c, LLAMA_KC_GEMM_W13, s, launch_gemm(EPI_SWIGLU, g, s));
+
+    g = GemmArgs{};
+    g.a = g16; g.lda = F; g.M = T; g.K = F; g.N = D;
+    g.w0 = W.w2; g.resid = h; g.ldr = D;
+    LAUNCH(c, LLAMA_KC_GEMM_W2, s, launch_gemm(EPI_RESID, g, s));
+    return LLAMA_OK;
+}
+
+// Final RMSNorm + output projection for `rows` rows of h spaced `ldx` floats apart.
+llama_status final_logits(const llama_ctx* c, const float* x, int64_t ldx, int rows, float* logits,
+                          hipStream_t s) {
+    GemvArgs g{};
+    g.x = x; g.ldx = ldx; g.M = rows; g.K = c->a.dim; g.N = c->a.vocab_size;
+    g.norm_w = c->w.norm; g.eps = c->a.norm_eps;
+    g.w0 = c->w.output; g.out = logits; g.ldo = c->a.vocab_size;
+    LAUNCH(c, LLAMA_KC_GEMV_OUT, s, launch_gemv(c->bf16 ? 1 : 0, EPI_STORE, g, s));
+    return LLAMA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+llama_status llama_check_args(const llama_args* a) { return check_args(a); }
+
+size_t llama_workspace_bytes(const llama_args* a) {
+    if (check_args(a) != LLAMA_OK) return 0;
+    return layout_of(*a).total;
+}
+
+llama_status llama_init(const llama_args* a, const llama_weights* w, void* d_workspace,
+                        size_t workspace_bytes, void* stream, llama_ctx** out) {
+    if (out) *out = nullptr;
+    if (!out || !w) return LLAMA_ERR_INVALID_ARG;
+    const llama_status st = check_args(a);
+    if (st != LLAMA_OK) return st;
+    if (!w->tok_embeddings || !w->norm || !w->output || !w->layers) return LLAMA_ERR_INVALID_ARG;
+    for (int l = 0; l < a->n_layers; ++l) {
+        const llama_layer_weights& L = w->layers[l];
+        const void* p[9] = {L.attention_norm, L.wq, L.wk, L.wv, L.wo, L.ffn_norm, L.w1, L.w2, L.w3};
+        for (const void* q : p)
+            if (!q || (reinterpret_cast<uintptr_t>(q) & 15)) return LLAMA_ERR_INVALID_ARG;
+    }
+    const Layout L = layout_of(*a);
+    if (!d_workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(d_workspace) % kAlign))
+        return LLAMA_ERR_WORKSPACE;
+
+    llama_ctx* c = new (std::nothrow) llama_ctx();
+    if (!c) return LLAMA_ERR_INVALID_ARG;
+    c->a = *a;
+    c->w = *w;
+    c->layers.assign(w->layers, w->layers + a->n_layers);
+    c->w.layers = c->layers.data();
+    c->L = L;
+    c->ws = static_cast<char*>(d_workspace);
+    c->hd = head_dim_of(*a);
+    c->nq = a->n_heads * c->hd;
+    c->nk = a->n_kv_heads * c->hd;
+    c->bf16 = a->dtype == LLAMA_BF16;
+
+    // RoPE table: entry (t, i) = (cos, sin) of t * theta^(-2i/hd), computed in float64.
+    const int half = c->hd / 2;
+    std::vector<float> tab((size_t)a->max_seq_len * half * 2);
+    for (int t = 0; t < a->max_seq_len; ++t)
+        for (int i = 0; i < half; ++i) {
+            const double f = std::pow((double)a->rope_theta, -2.0 * i / c->hd);
+            const double ang = (double)t * f;
+            tab[((size_t)t * half + i) * 2] = (float)std::cos(ang);
+            tab[((size_t)t * half + i) * 2 + 1] = (float)std::sin(ang);
+        }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(c->ws + L.rope, tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess) {
+        delete c;
+        return LLAMA_ERR_HIP;
+    }
+    *out = c;
+    return LLAMA_OK;
+}
+
+llama_status llama_prefill(llama_ctx* c, const int32_t* d_tokens, int64_t ld_tokens, int32_t bsz,
+                           int32_t seqlen, int32_t start_pos, float* d_logits,
+                           int32_t all_positions, void* stream) {
+    if (!c || !d_tokens || !d_logits) return LLAMA_ERR_INVALID_ARG;
+    if (bsz < 1 || bsz > c->a.max_batch_size || seqlen < 1 || start_pos < 0 ||
+        (int64_t)start_pos + seqlen > c->a.max_seq_len || ld_tokens < seqlen)
+        return LLAMA_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int D = c->a.dim;
+    const int T = bsz * seqlen;
+    float* h = c->at<float>(c->L.h32);
+    HIP_TRY(launch_embed(d_tokens, ld_tokens, bsz, seqlen, c->w.tok_embeddings, c->bf16 ? 1 : 0,
+                         c->a.vocab_size, D, h, s));
+    for (int l = 0; l < c->a.n_layers; ++l) {
+        const llama_status st = c->bf16 ? block_mfma(c, l, T, seqlen, start_pos, s)
+                                        : block_gemv(c, l, T, seqlen, start_pos, false, s);
+        if (st != LLAMA_OK) return st;
+    }
+    if (!all_positions) return final_logits(c, h + (size_t)(seqlen - 1) * D, (int64_t)seqlen * D, bsz, d_logits, s);
+    if (!c->bf16) return final_logits(c, h, D, T, d_logits, s);
+    void* act = c->at<void>(c->L.act16);
+    HIP_TRY(launch_rmsnorm_bf16(h, D, T, D, c->w.norm, c->a.norm_eps, act, D, s));
+    GemmArgs g{};
+    g.a = act; g.lda = D; g.M = T; g.K = D; g.N = c->a.vocab_size;
+    g.w0 = c->w.output; g.out = d_logits; g.ldo = c->a.vocab_size;
+    HIP_TRY(launch_gemm(EPI_STORE, g, s));
+    return LLAMA_OK;
+}
+
+llama_status llama_decode_step(llama_ctx* c, const int32_t* d_tokens, int64_t ld_tokens,
+                               int32_t bsz, int32_t start_pos, float* d_logits, void* stream) {
+    if (!c || !d_tokens || !d_logits) return LLAMA_ERR_INVALID_ARG;
+    if (bsz < 1 || bsz > c->a.max_batch_size || start_pos < 0 || start_pos >= c->a.max_seq_len ||
+        ld_tokens < 1)
+        return LLAMA_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int D = c->a.dim;
+    float* h = c->at<float>(c->L.h32);
+    HIP_TRY(launch_embed(d_tokens, ld_tokens, bsz, 1, c->w.tok_embeddings, c->bf16 ? 1 : 0,
+                         c->a.vocab_size, D, h, s));
+    for (int l = 0; l < c->a.n_layers; ++l) {
+        const llama_status st = block_gemv(c, l, bsz, 1, start_pos, true, s);
+        if (st != LLAMA_OK) return st;
+    }
+    return final_logits(c, h, D, bsz, d_logits, s);
+}
+
+llama_status llama_argmax(const float* d_logits, int32_t bsz, int32_t vocab, int64_t row_stride,
+                          int32_t* d_out, void* stream) {
+    if (!d_logits || !d_out || bsz < 1 || vocab < 1 || row_stride < vocab) return LLAMA_ERR_INVALID_ARG;
+    HIP_TRY(launch_argmax(d_logits, bsz, vocab, row_stride, d_out, static_cast<hipStream_t>(stream)));
+    return LLAMA_OK;
+}
+
+llama_status llama_select_next(const int32_t* d_next, int32_t* d_tokens, int64_t ld_tokens,
+                               int32_t cur_pos, const int32_t* d_prompt_len, int32_t bsz,
+                               void* stream) {
+    if (!d_next || !d_tokens || !d_prompt_len || bsz < 1 || cur_pos < 0 || cur_pos >= ld_tokens)
+        return LLAMA_ERR_INVALID_ARG;
+    HIP_TRY(launch_select(d_next, d_tokens, ld_tokens, cur_pos, d_prompt_len, bsz,
+                          static_cast<hipStream_t>(stream)));
+    return LLAMA_OK;
+}
+
+llama_status llama_profile_select(llama_ctx* c, int32_t kernel_class) {
+    if (!c || kernel_class < 0 || kernel_class >= LLAMA_KC_COUNT) return LLAMA_ERR_INVALID_ARG;
+    c->prof_class = kernel_class;
+    return LLAMA_OK;
+}
+
+llama_status llama_profile_read(llama_ctx* c, int64_t* launches, double* total_ms) {
+    if (!c || !launches || !total_ms) return LLAMA_ERR_INVALID_ARG;
+    double ms = 0.0;
+    const size_t pairs = c->ev_used / 2;
+    for (size_t i = 0; i < pairs; ++i) {
+        float t = 0.f;
+        if (hipEventSynchronize(c->ev[2 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&t, c->ev[2 * i], c->ev[2 * i + 1]) != hipSuccess)
+            return LLAMA_ERR_HIP;
+        ms += t;
+    }
+    *launches = (int64_t)pairs;
+    *total_ms = ms;
+    c->ev_used = 0;
+    if (c->ev_failed) {
+        c->ev_failed = false;
+        return LLAMA_ERR_HIP;
+    }
+    return LLAMA_OK;
+}
+
+void llama_destroy(llama_ctx* c) {
+    if (!c) return;
+    for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
+    delete c;
+}
+
+const char* llama_status_str(llama_status st) {
+    switch (st) {
+        case LLAMA_OK: return "LLAMA_OK";
+        case LLAMA_ERR_INVALID_ARG: return "LLAMA_ERR_INVALID_ARG";
+        case LLAMA_ERR_UNSUPPORTED: return "LLAMA_ERR_UNSUPPORTED";
+        case LLAMA_ERR_WORKSPACE: return "LLAMA_ERR_WORKSPACE";
+        case LLAMA_ERR_HIP: return "LLAMA_ERR_HIP";
+    }
+    return "LLAMA_STATUS_UNKNOWN";
+}
+
+}  // extern "C"

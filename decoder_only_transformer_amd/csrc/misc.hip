@@ -1,0 +1,125 @@
+// Small bandwidth kernels: embedding gather, RMSNorm to a bf16 GEMM operand, greedy argmax,
+// and the generate loop's prompt-preserving token select.
+#include "common.h"
+#include "kernels.h"
+
+namespace llk {
+namespace {
+
+// h[b*seqlen + s][:] = E[tokens[b*ld + s]][:] as fp32 (the residual stream is fp32).
+template <typename WT>
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* tokens, int64_t ld, int seqlen,
+                                                    const WT* table, int vocab, int dim, float* h) {
+    const int t = blockIdx.x;
+    const int b = t / seqlen, s = t - b * seqlen;
+    int tok = tokens[(size_t)b * ld + s];
+    tok = min(max(tok, 0), vocab - 1);   // out-of-range ids are a caller error; never read outside E
+    const WT* row = table + (size_t)tok * dim;
+    float* out = h + (size_t)t * dim;
+    for (int k = threadIdx.x; k < dim; k += blockDim.x) out[k] = Elem<WT>::load(row, k);
+}
+
+// out[r][:] = bf16( h[r][:] * rsqrt(mean(h[r]^2) + eps) * w ), fp32 reduction.
+template <typename WT>
+__global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const float* h, int64_t ldh, int dim,
+                                                           const WT* w, float eps, uint16_t* out,
+                                                           int64_t ldo) {
+    __shared__ float red[4];
+    const float* x = h + (size_t)blockIdx.x * ldh;
+    float ss = 0.f;
+    for (int k = threadIdx.x * 4; k < dim; k += 256 * 4) {
+        const float4 v = *reinterpret_cast<const float4*>(x + k);
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float r = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)dim + eps);
+    uint16_t* o = out + (size_t)blockIdx.x * ldo;
+    for (int k = threadIdx.x * 4; k < dim; k += 256 * 4) {
+        const float4 v = *reinterpret_cast<const float4*>(x + k);
+        uint2 p;
+        p.x = pack_bf16x2(v.x * r * Elem<WT>::load(w, k), v.y * r * Elem<WT>::load(w, k + 1));
+        p.y = pack_bf16x2(v.z * r * Elem<WT>::load(w, k + 2), v.w * r * Elem<WT>::load(w, k + 3));
+        *reinterpret_cast<uint2*>(o + k) = p;
+    }
+}
+
+// Better of two (value, index) candidates: larger value wins, ties -> lower index, NaN never wins.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
+    if (i2 < 0) return;
+    if (i < 0 || v2 > v || (v2 == v && i2 < i)) {
+        v = v2;
+        i = i2;
+    }
+}
+
+__global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int vocab, int64_t stride,
+                                                     int32_t* out) {
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    const float* x = logits + (size_t)blockIdx.x * stride;
+    float best = 0.f;
+    int bi = -1;
+    for (int k = threadIdx.x; k < vocab; k += 256) {
+        const float v = x[k];
+        if (v == v) argmax_merge(best, bi, v, k);   // skips NaN
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float v2 = __shfl_xor(best, o, kWave);
+        const int i2 = __shfl_xor(bi, o, kWave);
+        argmax_merge(best, bi, v2, i2);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        sv[threadIdx.x >> 6] = best;
+        si[threadIdx.x >> 6] = bi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < 4; ++w) argmax_merge(best, bi, sv[w], si[w]);
+        out[blockIdx.x] = bi;
+    }
+}
+
+__global__ void select_kernel(const int32_t* next, int32_t* tokens, int64_t ld, int cur_pos,
+                              const int32_t* prompt_len, int bsz) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < bsz && cur_pos >= prompt_len[b]) tokens[(size_t)b * ld + cur_pos] = next[b];
+}
+
+}  // namespace
+
+hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, const void* table,
+                        int wbf16, int vocab, int dim, float* h, hipStream_t s) {
+    const dim3 grid(bsz * seqlen), block(256);
+    if (wbf16)
+        hipLaunchKernelGGL(embed_kernel<bf16>, grid, block, 0, s, tokens, ld, seqlen,
+                           static_cast<const bf16*>(table), vocab, dim, h);
+    else
+        hipLaunchKernelGGL(embed_kernel<float>, grid, block, 0, s, tokens, ld, seqlen,
+                           static_cast<const float*>(table), vocab, dim, h);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_bf16(const float* h, int64_t ldh, int rows, int dim, const void* w,
+                               float eps, void* out, int64_t ldo, hipStream_t s) {
+    hipLaunchKernelGGL(rmsnorm_bf16_kernel<bf16>, dim3(rows), dim3(256), 0, s, h, ldh, dim,
+                       static_cast<const bf16*>(w), eps, static_cast<uint16_t*>(out), ldo);
+    return hipGetLastError();
+}
+
+hipError_t launch_argmax(const float* logits, int bsz, int vocab, int64_t stride, int32_t* out,
+                         hipStream_t s) {
+    hipLaunchKernelGGL(argmax_kernel, dim3(bsz), dim3(256), 0, s, logits, vocab, stride, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_select(const int32_t* next, int32_t* tokens, int64_t ld, int cur_pos,
+                         const int32_t* prompt_len, int bsz, hipStream_t s) {
+    hipLaunchKernelGGL(select_kernel, dim3((bsz + 63) / 64), dim3(64), 0, s, next, tokens, ld,
+                       cur_pos, prompt_len, bsz);
+    return hipGetLastError();
+}
+
+}  // namespace llk

@@ -59,7 +59,8 @@ typedef enum llama_dtype {
  * max_batch_size and max_seq_len size the KV cache, which persists across calls
  * (section 6.2 "KV cache footprint").
  *
- * Supported: head_dim in {64, 128} (and 32 for LLAMA_FP32), dim, hidden_dim and
+ * Supported: head_dim in {32, 64, 128}, n_heads / n_kv_heads in {1, 2, 4, 8}, even
+ * vocab_size, dim, hidden_dim and
  * n_heads*head_dim multiples of 64, max_seq_len <= 65536.
  */
 typedef struct llama_args {
@@ -160,6 +161,34 @@ llama_status llama_argmax(const float *d_logits, int32_t bsz, int32_t vocab,
 llama_status llama_select_next(const int32_t *d_next, int32_t *d_tokens, int64_t ld_tokens,
                                int32_t cur_pos, const int32_t *d_prompt_len, int32_t bsz,
                                void *stream);
+
+/*
+ * Diagnostics: device time of one class of kernel launches.  llama_profile_select(c, k)
+ * makes the ctx bracket every later launch of kernel class k (LLAMA_KC_*, 0 = none) with
+ * a pair of HIP events recorded on the launch stream; llama_profile_read waits for those
+ * events, returns the number of bracketed launches and their summed duration in
+ * milliseconds, and forgets them.  Meant for measurement runs only: the events add a few
+ * microseconds around each bracketed launch.
+ * Errors: INVALID_ARG for a NULL ctx/pointer or an unknown class; HIP on event failure.
+ */
+enum llama_kernel_class {
+    LLAMA_KC_NONE = 0,
+    LLAMA_KC_GEMV_QKV = 1,    /* decode: fused RMSNorm + [wq;wk;wv] + RoPE + KV append */
+    LLAMA_KC_ATTN_DECODE = 2, /* decode: split attention (+ merge) */
+    LLAMA_KC_GEMV_WO = 3,     /* decode: wo + residual */
+    LLAMA_KC_GEMV_W13 = 4,    /* decode: fused RMSNorm + [w1;w3] + SiLU gate */
+    LLAMA_KC_GEMV_W2 = 5,     /* decode: w2 + residual */
+    LLAMA_KC_GEMV_OUT = 6,    /* final RMSNorm + vocab projection (decode and prefill) */
+    LLAMA_KC_GEMM_QKV = 7,    /* prefill: MFMA [wq;wk;wv] + RoPE + KV append */
+    LLAMA_KC_ATTN_PREFILL = 8,/* prefill: causal attention */
+    LLAMA_KC_GEMM_WO = 9,     /* prefill: MFMA wo + residual */
+    LLAMA_KC_GEMM_W13 = 10,   /* prefill: MFMA [w1;w3] + SiLU gate */
+    LLAMA_KC_GEMM_W2 = 11,    /* prefill: MFMA w2 + residual */
+    LLAMA_KC_RMSNORM = 12,    /* prefill: RMSNorm to bf16 */
+    LLAMA_KC_COUNT = 13
+};
+llama_status llama_profile_select(llama_ctx *c, int32_t kernel_class);
+llama_status llama_profile_read(llama_ctx *c, int64_t *launches, double *total_ms);
 
 /* Releases the ctx (host memory only; the workspace and weights stay the caller's).
  * Waits for nothing: the caller must not destroy a ctx with work still in flight. */
