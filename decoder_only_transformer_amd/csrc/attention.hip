@@ -1,10 +1,12 @@
 // Causal grouped-query attention of individual query rows against the KV cache
 // (flash-decode style).  One workgroup handles one query position, one kv head and all
 // n_rep query heads that read it (GQA without materialising repeat_kv), over one split of
-// the visible keys [0, pos].  Sixteen lanes share one key (head_dim/16 elements each), a
-// wave walks four keys at a time, and each 16-lane group keeps a running (max, sum, acc)
-// online softmax per head in fp32.  The sixteen groups are merged through LDS; with more
-// than one split per row a second kernel merges the per-split partials.
+// the visible keys [0, pos].  Sixteen lanes share one key (head_dim/16 elements each); each
+// 16-lane group loads four keys' K and V rows before using any of them and keeps a running
+// (max, sum, acc) online softmax per head in fp32.  The sixteen groups are merged through
+// LDS.  With more than one split per row, every workgroup stores its partial (m, l, acc)
+// and the last one to arrive (per-row counter) merges all splits in split order and
+// resets the counter, so no second launch is needed and the result is deterministic.
 #include "common.h"
 #include "kernels.h"
 
@@ -12,20 +14,43 @@ namespace llk {
 namespace {
 
 constexpr int kSlots = 16;   // 4 waves x 4 lane groups
+constexpr int kMaxSplitMerge = 32;   // largest split count the in-kernel merge handles
 
+// N elements of a K or V row as raw bits (4, 8, 16 or 32 bytes), unpacked later so the
+// loads of several keys are in flight together.
 template <typename KT, int N>
-__device__ __forceinline__ void load_row(const KT* p, float* out) {
-    constexpr int bytes = N * (int)sizeof(KT);
-    if constexpr (bytes == 32) {
-        Elem<KT>::unpack(ld16(p), out);
-        Elem<KT>::unpack(ld16(p + 16 / sizeof(KT)), out + 16 / sizeof(KT));
-    } else if constexpr (bytes == 16) {
-        Elem<KT>::unpack(ld16(p), out);
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; ++i) out[i] = Elem<KT>::load(p, i);
+struct RawRow {
+    static constexpr int kWords = N * (int)sizeof(KT) / 4;
+    uint32_t w[kWords];
+    __device__ __forceinline__ void load(const KT* p) {
+        if constexpr (kWords == 8) {
+            const uint4 a = ld16(p), b = ld16(reinterpret_cast<const char*>(p) + 16);
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+        } else if constexpr (kWords == 4) {
+            const uint4 a = ld16(p);
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        } else if constexpr (kWords == 2) {
+            const uint2 a = *reinterpret_cast<const uint2*>(p);
+            w[0] = a.x; w[1] = a.y;
+        } else {
+            w[0] = *reinterpret_cast<const uint32_t*>(p);
+        }
     }
-}
+    __device__ __forceinline__ void unpack(float* out) const {
+        if constexpr (sizeof(KT) == 4) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) out[i] = __uint_as_float(w[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < N / 2; ++i) {
+                out[2 * i] = bf16lo(w[i]);
+                out[2 * i + 1] = bf16hi(w[i]);
+            }
+        }
+    }
+};
+
+
 
 template <typename KT, int HD, int NREP, bool OUT_BF16>
 __global__ __launch_bounds__(256) void attn_rows_kernel(AttnArgs a) {
@@ -65,23 +90,37 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnArgs a) {
     const size_t base = (size_t)b * a.max_seq * kv_row + (size_t)kvh * HD + gl * EPL;
     const KT* kb = static_cast<const KT*>(a.cache_k) + base;
     const KT* vb = static_cast<const KT*>(a.cache_v) + base;
-    for (int j = j0 + slot; j < j1; j += kSlots) {
-        float kf[EPL], vf[EPL];
-        load_row<KT, EPL>(kb + (size_t)j * kv_row, kf);
-        load_row<KT, EPL>(vb + (size_t)j * kv_row, vf);
+    constexpr int PF = 4;   // keys per group whose loads are in flight together
+    for (int j = j0 + slot; j < j1; j += PF * kSlots) {
+        RawRow<KT, EPL> kr[PF], vr[PF];
 #pragma unroll
-        for (int r = 0; r < NREP; ++r) {
-            float s = 0.f;
+        for (int u = 0; u < PF; ++u) {
+            const int jj = j + u * kSlots;
+            if (jj < j1) {
+                kr[u].load(kb + (size_t)jj * kv_row);
+                vr[u].load(vb + (size_t)jj * kv_row);
+            }
+        }
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) s += q[r][e] * kf[e];
-            s = group_sum<16>(s);
-            const float mn = fmaxf(m[r], s);
-            const float sc = __expf(m[r] - mn);
-            const float p = __expf(s - mn);
-            l[r] = l[r] * sc + p;
+        for (int u = 0; u < PF; ++u) {
+            if (j + u * kSlots >= j1) break;
+            float kf[EPL], vf[EPL];
+            kr[u].unpack(kf);
+            vr[u].unpack(vf);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[r][e] = acc[r][e] * sc + p * vf[e];
-            m[r] = mn;
+            for (int r = 0; r < NREP; ++r) {
+                float s = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) s += q[r][e] * kf[e];
+                s = group_sum<16>(s);
+                const float mn = fmaxf(m[r], s);
+                const float sc = __expf(m[r] - mn);
+                const float p = __expf(s - mn);
+                l[r] = l[r] * sc + p;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[r][e] = acc[r][e] * sc + p * vf[e];
+                m[r] = mn;
+            }
         }
     }
 
@@ -126,28 +165,52 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnArgs a) {
             }
         }
     }
-}
+    if (a.n_split == 1) return;
 
-template <int HD, bool OUT_BF16>
-__global__ void attn_merge_kernel(AttnArgs a) {
-    const int t = a.row0 + blockIdx.x, h = blockIdx.y, d = threadIdx.x;
-    const float* pp = a.part + ((size_t)t * a.n_heads + h) * a.n_split * (HD + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, pp[s * (HD + 2) + HD]);
-    float L = 0.f, A = 0.f;
-    for (int s = 0; s < a.n_split; ++s) {
-        const float ms = pp[s * (HD + 2) + HD];
-        if (ms == -INFINITY) continue;
-        const float w = __expf(ms - M);
-        L += pp[s * (HD + 2) + HD + 1] * w;
-        A += pp[s * (HD + 2) + d] * w;
+    // Last workgroup of this (row, kv head) to arrive merges the splits.
+    __shared__ int s_last;
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const int old = atomicAdd(&a.counters[(size_t)t * a.n_kv_heads + kvh], 1);
+        s_last = (old == a.n_split - 1);
     }
-    const float o = A / L;
-    const size_t idx = (size_t)t * a.n_heads * HD + h * HD + d;
-    if (OUT_BF16)
-        static_cast<uint16_t*>(a.out)[idx] = f32_to_bf16(o);
-    else
-        static_cast<float*>(a.out)[idx] = o;
+    __syncthreads();
+    if (!s_last) return;
+    // acquire: the other splits' partials (released by their fence before the counter
+    // increment) are visible to ordinary loads from here on
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    for (int idx = tid; idx < NREP * HD; idx += blockDim.x) {
+        const int r = idx / HD, d = idx - r * HD;
+        const int h = kvh * NREP + r;
+        const float* pp = a.part + ((size_t)t * a.n_heads + h) * a.n_split * (HD + 2);
+        float ms[kMaxSplitMerge], ls[kMaxSplitMerge], as[kMaxSplitMerge];
+        float M = -INFINITY;
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplitMerge; ++sp) {
+            if (sp < a.n_split) {
+                ms[sp] = pp[sp * (HD + 2) + HD];
+                ls[sp] = pp[sp * (HD + 2) + HD + 1];
+                as[sp] = pp[sp * (HD + 2) + d];
+                M = fmaxf(M, ms[sp]);
+            }
+        }
+        float L = 0.f, A = 0.f;
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplitMerge; ++sp) {
+            if (sp < a.n_split && ms[sp] != -INFINITY) {
+                const float w = __expf(ms[sp] - M);
+                L += ls[sp] * w;
+                A += as[sp] * w;
+            }
+        }
+        const float o = A / L;
+        if (OUT_BF16)
+            static_cast<uint16_t*>(a.out)[(size_t)t * qstride + h * HD + d] = f32_to_bf16(o);
+        else
+            static_cast<float*>(a.out)[(size_t)t * qstride + h * HD + d] = o;
+    }
+    if (tid == 0) a.counters[(size_t)t * a.n_kv_heads + kvh] = 0;
 }
 
 template <typename KT, int HD, int NREP, bool OB>
@@ -159,13 +222,8 @@ hipError_t launch4(const AttnArgs& args, hipStream_t s) {
         const int n = min(kMaxZ, args.rows - r0);
         hipLaunchKernelGGL((attn_rows_kernel<KT, HD, NREP, OB>), dim3(a.n_split, a.n_kv_heads, n),
                            dim3(256), 0, s, a);
-        hipError_t e = hipGetLastError();
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        if (a.n_split > 1) {
-            hipLaunchKernelGGL((attn_merge_kernel<HD, OB>), dim3(n, a.n_heads), dim3(HD), 0, s, a);
-            e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
     }
     return hipSuccess;
 }

@@ -2,13 +2,18 @@
 //
 // C[m][n] = sum_k A[m][k] * W[n][k], A = bf16 activations [M][lda], W = nn.Linear weight
 // [N][K] bf16 (row-major, so both operands are K-contiguous and load as 16-byte chunks).
-// 256 threads = 2x2 waves; a workgroup owns a BM x BN tile, each wave (BM/2) x (BN/2) as a
-// grid of 16x16 MFMA accumulators.  K advances 64 at a time through double-buffered LDS
-// tiles (rows padded by 16 bytes so the 16-lane fragment reads hit distinct banks); the
-// next tile's global loads are issued before the current tile's MFMAs.
+// A workgroup of WGM x WGN waves owns a BM x BN tile, each wave (BM/WGM) x (BN/WGN) as a grid
+// of 16x16 MFMA accumulators.  K advances 64 at a time through double-buffered LDS tiles
+// (rows padded by 16 bytes so the 16-lane fragment reads hit distinct banks); the next
+// tile's global loads are issued before the current tile's MFMAs.  Workgroups are mapped to
+// tiles XCD-aware: the dispatcher deals workgroup ids round-robin over the 8 XCDs, so each
+// XCD is given a contiguous share of the tile space, walked in groups of 8 M-tiles so the
+// workgroups resident on one XCD share A and B tiles in its L2.
 // Epilogues: RoPE + q store + KV-cache append ([wq; wk; wv]), residual add (wo, w2),
 // SiLU gate (w1 and w3 interleaved in one B tile so each wave holds matching gate/up
 // accumulators), fp32 store (logits).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -21,13 +26,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int BK = 64;
 constexpr int LDK = BK + 8;   // padded LDS row (elements)
 
-template <int BN, int EPI>
+// Weight row feeding row `brow` of the B tile.  For the SiLU gate each wave column's share
+// of the tile is half w1 rows and half the matching w3 rows.
+template <int BN, int WGN, int EPI>
 __device__ __forceinline__ const uint16_t* b_row_ptr(const GemmArgs& a, int tile_n, int brow, bool& ok) {
     int n;
     const uint16_t* mat;
     if (EPI == EPI_SWIGLU) {
-        constexpr int half = BN / 4;
-        const int wn = brow / (BN / 2), jj = brow % (BN / 2);
+        constexpr int half = BN / WGN / 2;
+        const int wn = brow / (BN / WGN), jj = brow % (BN / WGN);
         n = tile_n * (BN / 2) + wn * half + (jj % half);
         mat = static_cast<const uint16_t*>(jj < half ? a.w0 : a.w1);
     } else if (EPI == EPI_QKV) {
@@ -46,25 +53,51 @@ __device__ __forceinline__ const uint16_t* b_row_ptr(const GemmArgs& a, int tile
     return mat + (size_t)(ok ? n : 0) * a.K;
 }
 
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
-    constexpr int WM = BM / 2, WN = BN / 2;
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+
+// Tile (tm, tn) of linear workgroup id `id` (see the header comment).  The grid is padded to
+// kXcds * ceil(total / kXcds) workgroups, on which id -> t is a bijection; returns false for
+// the few ids whose t falls past the last tile.
+__device__ __forceinline__ bool tile_of(int id, int n_tm, int n_tn, int& tm, int& tn) {
+    const int total = n_tm * n_tn;
+    const int per_xcd = (total + kXcds - 1) / kXcds;
+    const int t = (id % kXcds) * per_xcd + id / kXcds;
+    if (t >= total) return false;
+    const int group = t / (kGroupM * n_tn);
+    const int first_m = group * kGroupM;
+    const int gsize = min(kGroupM, n_tm - first_m);
+    const int r = t - group * kGroupM * n_tn;
+    tm = first_m + r % gsize;
+    tn = r / gsize;
+    return true;
+}
+
+template <int BM, int BN, int WGM, int WGN, int EPI>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs a, int n_tm, int n_tn) {
+    constexpr int NT = 64 * WGM * WGN;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int TM = WM / 16, TN = WN / 16;
-    constexpr int A_LD = BM * 8 / 256, B_LD = BN * 8 / 256;
+    constexpr int A_LD = BM * 8 / NT, B_LD = BN * 8 / NT;
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDK];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LDK];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int wm = wid >> 1, wn = wid & 1;
-    const int tile_n = blockIdx.x, tile_m = blockIdx.y;
+    const int wm = wid / WGN, wn = wid % WGN;
+    int tile_m, tile_n;
+    if (!tile_of(blockIdx.x, n_tm, n_tn, tile_m, tile_n)) return;
     const int m0 = tile_m * BM;
+    // K range of this workgroup (split-K over gridDim.z, in BK steps)
+    const int nk_all = a.K / BK;
+    const int kt0 = (int)((int64_t)nk_all * blockIdx.z / gridDim.z);
+    const int kt1 = (int)((int64_t)nk_all * (blockIdx.z + 1) / gridDim.z);
 
     const uint16_t* ap[A_LD];
     bool aok[A_LD];
     int arow[A_LD], acol[A_LD];
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
-        const int c = tid + 256 * i;
+        const int c = tid + NT * i;
         arow[i] = c >> 3;
         acol[i] = (c & 7) * 8;
         const int gm = m0 + arow[i];
@@ -76,11 +109,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     int brow[B_LD], bcol[B_LD];
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-        const int c = tid + 256 * i;
+        const int c = tid + NT * i;
         brow[i] = c >> 3;
         bcol[i] = (c & 7) * 8;
         bool ok = true;
-        bp[i] = b_row_ptr<BN, EPI>(a, tile_n, brow[i], ok) + bcol[i];
+        bp[i] = b_row_ptr<BN, WGN, EPI>(a, tile_n, brow[i], ok) + bcol[i];
         bok[i] = ok;
     }
 
@@ -105,14 +138,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         for (int i = 0; i < B_LD; ++i) *reinterpret_cast<uint4*>(&Bs[buf][brow[i]][bcol[i]]) = rb[i];
     };
 
-    const int nk = a.K / BK;
-    gload(0);
+    gload(kt0);
     lstore(0);
     __syncthreads();
     const int fr = lane & 15, fk = (lane >> 4) * 8;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
+    for (int kt = kt0; kt < kt1; ++kt) {
+        const int buf = (kt - kt0) & 1;
+        if (kt + 1 < kt1) gload(kt + 1);
 #pragma unroll
         for (int ks = 0; ks < BK; ks += 32) {
             bf16x8_t af[TM], bfr[TN];
@@ -128,14 +160,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < nk) lstore(buf ^ 1);
+        if (kt + 1 < kt1) lstore(buf ^ 1);
         __syncthreads();
     }
 
     // Epilogue.  Lane holds C[row0 + e][col] for e = 0..3 of each 16x16 tile.
     const int rq = (lane >> 4) * 4;
     if (EPI == EPI_SWIGLU) {
-        constexpr int half = BN / 4;
+        constexpr int half = BN / WGN / 2;
         uint16_t* out = static_cast<uint16_t*>(a.out16);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -171,7 +203,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                         v = (n & 1) ? partner * cs.y + v * cs.x : v * cs.x - partner * cs.y;
                     }
                     if (n < t.nq) {
-                        t.q[(size_t)m * t.nq + n] = v;
+                        t.q[(size_t)m * t.nq + n] = round_bf16(v);
                     } else {
                         const bool is_k = n < t.nq + t.nk;
                         const int c = is_k ? n - t.nq : n - t.nq - t.nk;
@@ -179,29 +211,53 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                         cache[((size_t)b * t.max_seq + pos) * (size_t)t.nk + c] = f32_to_bf16(v);
                     }
                 } else if (m < a.M && n < a.N) {
-                    if (EPI == EPI_RESID)
-                        a.resid[(size_t)m * a.ldr + n] += v;
-                    else
+                    if (EPI == EPI_RESID) {
+                        if (gridDim.z > 1)
+                            a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = v;
+                        else
+                            a.resid[(size_t)m * a.ldr + n] += v;
+                    } else {
                         a.out[(size_t)m * a.ldo + n] = v;
+                    }
                 }
             }
         }
 }
 
-template <int BM, int BN, int EPI>
+// resid[m][n] += sum over splits of part[z][m][n], in split order.
+__global__ void splitk_reduce_kernel(const float* part, int splits, int M, int N, float* resid,
+                                     int64_t ldr) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)M * N) return;
+    const int m = (int)(i / N), n = (int)(i - (size_t)m * N);
+    float v = 0.f;
+    for (int z = 0; z < splits; ++z) v += part[(size_t)z * M * N + i];
+    resid[(size_t)m * ldr + n] += v;
+}
+
+template <int BM, int BN, int WGM, int WGN, int EPI>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     const int ncols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-    const dim3 grid((a.N + ncols - 1) / ncols, (a.M + BM - 1) / BM);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI>), grid, dim3(256), 0, s, a);
+    const int splits = (EPI == EPI_RESID && a.part) ? std::max(1, a.splits) : 1;
+    const int n_tn = (a.N + ncols - 1) / ncols, n_tm = (a.M + BM - 1) / BM;
+    const int per_xcd = (n_tn * n_tm + kXcds - 1) / kXcds;
+    const dim3 grid(per_xcd * kXcds, 1, splits);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM, WGN, EPI>), grid, dim3(64 * WGM * WGN), 0, s, a, n_tm, n_tn);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    const size_t n = (size_t)a.M * a.N;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       a.part, splits, a.M, a.N, a.resid, a.ldr);
     return hipGetLastError();
 }
 
 template <int EPI>
 hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
     // Small M (short prefill): narrower tiles so enough workgroups stream the weights.
-    if (a.M <= 64) return launch_tile<64, 64, EPI>(a, s);
-    if (a.M <= 256) return launch_tile<128, 64, EPI>(a, s);
-    return launch_tile<128, 128, EPI>(a, s);
+    if (a.M <= 64) return launch_tile<64, 64, 2, 2, EPI>(a, s);
+    if (a.M <= 256) return launch_tile<128, 64, 2, 2, EPI>(a, s);
+    if (a.M <= 2048) return launch_tile<128, 128, 2, 2, EPI>(a, s);
+    return launch_tile<256, 256, 4, 2, EPI>(a, s);
 }
 
 }  // namespace

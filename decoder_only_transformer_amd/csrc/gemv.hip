@@ -8,6 +8,9 @@
 // once per workgroup in LDS as fp32.  Epilogues fuse what follows each projection in the
 // block: RoPE + KV-cache append for [wq; wk; wv], residual add for wo / w2, the SiLU gate
 // for [w1; w3], and the fp32 logits store for the output projection.
+// With bf16 weights the activations are rounded to bf16 as they are staged, and q is
+// rounded before it is stored: the decode path stores the same bf16 tensors as the MFMA
+// prefill path (normalised operands, q, K/V, attention output, gated FFN activation).
 #include "common.h"
 #include "kernels.h"
 
@@ -16,7 +19,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
-constexpr int kSeg = 4096;   // activation elements staged per LDS segment
+
+template <typename WT> constexpr bool kIsBf16 = false;
+template <> constexpr bool kIsBf16<bf16> = true;
 
 template <typename WT>
 __device__ __forceinline__ const WT* qkv_row(const GemvArgs& a, int n) {
@@ -40,6 +45,10 @@ __device__ __forceinline__ void qkv_store(const QkvTarget& t, int m, int n0, flo
         y1 = r1;
     }
     if (n0 < t.nq) {
+        if (kIsBf16<WT>) {
+            y0 = round_bf16(y0);
+            y1 = round_bf16(y1);
+        }
         t.q[(size_t)m * t.nq + n0] = y0;
         t.q[(size_t)m * t.nq + n0 + 1] = y1;
         return;
@@ -52,53 +61,65 @@ __device__ __forceinline__ void qkv_store(const QkvTarget& t, int m, int n0, flo
     Elem<WT>::store(cache, off + 1, y1);
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not for its
+// outstanding global loads (which __syncthreads' release fence would drain), so weight
+// loads issued before it stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <typename WT, int MB, int EPI, bool NORM>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
     constexpr int VEC = Elem<WT>::kPer16B;
-    constexpr int U = 8;
-    __shared__ float xs[MB][kSeg];
+    constexpr int U = 8;                       // 16-byte chunks per lane per row per segment
+    constexpr int SEG = U * kWave * VEC;       // K elements per segment (bf16: 4096, fp32: 2048)
+    constexpr int XPT = SEG / 4 / kThreads;    // activation float4s per thread per row per segment
+    __shared__ float xs[MB][SEG];
     __shared__ float red[kWavesPerBlock][MB];
-    __shared__ float rstd_s[MB];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wid = tid >> 6;
-    const int unit = blockIdx.x * kWavesPerBlock + wid;
     const int n_units = (EPI == EPI_SWIGLU) ? a.N : a.N / 2;
-    const bool active = unit < n_units;
+    const int unit_raw = blockIdx.x * kWavesPerBlock + wid;
+    const bool active = unit_raw < n_units;
+    // Inactive waves (tail of the last workgroup) stream a valid row and discard it, so every
+    // load below is unconditional and the wait counts stay exact.
+    const int unit = active ? unit_raw : n_units - 1;
+    const bool one_seg = a.K <= SEG;
 
-    // The two weight rows this wave streams.
-    const WT* row0 = nullptr;
-    const WT* row1 = nullptr;
-    int n0 = 0;
-    if (active) {
-        if (EPI == EPI_SWIGLU) {
-            n0 = unit;
-            row0 = static_cast<const WT*>(a.w0) + (size_t)unit * a.K;
-            row1 = static_cast<const WT*>(a.w1) + (size_t)unit * a.K;
-        } else if (EPI == EPI_QKV) {
-            n0 = 2 * unit;
-            row0 = qkv_row<WT>(a, n0);
-            row1 = row0 + a.K;
-        } else {
-            n0 = 2 * unit;
-            row0 = static_cast<const WT*>(a.w0) + (size_t)n0 * a.K;
-            row1 = row0 + a.K;
-        }
+    const WT* row0;
+    const WT* row1;
+    int n0;
+    if (EPI == EPI_SWIGLU) {
+        n0 = unit;
+        row0 = static_cast<const WT*>(a.w0) + (size_t)unit * a.K;
+        row1 = static_cast<const WT*>(a.w1) + (size_t)unit * a.K;
+    } else if (EPI == EPI_QKV) {
+        n0 = 2 * unit;
+        row0 = qkv_row<WT>(a, n0);
+        row1 = row0 + a.K;
+    } else {
+        n0 = 2 * unit;
+        row0 = static_cast<const WT*>(a.w0) + (size_t)n0 * a.K;
+        row1 = row0 + a.K;
     }
 
     for (int m0 = 0; m0 < a.M; m0 += MB) {
-        if (NORM) {
+        float rstd[MB];
+#pragma unroll
+        for (int m = 0; m < MB; ++m) rstd[m] = 1.f;
+        if (NORM && !one_seg) {
+            // rows longer than one segment: statistics in a pass of their own
             float ss[MB];
 #pragma unroll
             for (int m = 0; m < MB; ++m) ss[m] = 0.f;
             for (int k = tid * 4; k < a.K; k += kThreads * 4) {
 #pragma unroll
                 for (int m = 0; m < MB; ++m) {
-                    if (m0 + m < a.M) {
-                        const float4 v = *reinterpret_cast<const float4*>(a.x + (size_t)(m0 + m) * a.ldx + k);
-                        ss[m] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-                    }
+                    const int row = min(m0 + m, a.M - 1);
+                    const float4 v = *reinterpret_cast<const float4*>(a.x + (size_t)row * a.ldx + k);
+                    ss[m] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
                 }
             }
 #pragma unroll
@@ -106,83 +127,144 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
                 const float t = wave_sum(ss[m]);
                 if (lane == 0) red[wid][m] = t;
             }
-            __syncthreads();
-            if (tid < MB) {
+            lds_barrier();
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
                 float t = 0.f;
-                for (int w = 0; w < kWavesPerBlock; ++w) t += red[w][tid];
-                rstd_s[tid] = rsqrtf(t / (float)a.K + a.eps);
+#pragma unroll
+                for (int w = 0; w < kWavesPerBlock; ++w) t += red[w][m];
+                rstd[m] = rsqrtf(t / (float)a.K + a.eps);
             }
-            __syncthreads();
+            lds_barrier();
         }
 
         float acc[MB][2];
 #pragma unroll
         for (int m = 0; m < MB; ++m) acc[m][0] = acc[m][1] = 0.f;
 
-        for (int k0 = 0; k0 < a.K; k0 += kSeg) {
-            const int klen = min(kSeg, a.K - k0);
-            __syncthreads();
-            for (int i = tid; i < MB * (klen / 4); i += kThreads) {
-                const int m = i / (klen / 4);
-                const int k = (i - m * (klen / 4)) * 4;
-                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (m0 + m < a.M) {
-                    v = *reinterpret_cast<const float4*>(a.x + (size_t)(m0 + m) * a.ldx + k0 + k);
+        for (int k0 = 0; k0 < a.K; k0 += SEG) {
+            const int klen = min(SEG, a.K - k0);
+            const int nchunks = klen / VEC;
+            // 1. activation (and norm weight) loads of this segment; addresses are clamped
+            //    in range so every load is unconditional
+            float4 xv[MB][XPT];
+            uint2 nv[XPT];
+            float4 nvf[XPT];
+#pragma unroll
+            for (int i = 0; i < XPT; ++i) {
+                const int k = min((tid + i * kThreads) * 4, klen - 4);
+#pragma unroll
+                for (int m = 0; m < MB; ++m) {
+                    const int row = min(m0 + m, a.M - 1);
+                    xv[m][i] = *reinterpret_cast<const float4*>(a.x + (size_t)row * a.ldx + k0 + k);
+                }
+                if (NORM) {
+                    if (kIsBf16<WT>)
+                        nv[i] = *reinterpret_cast<const uint2*>(static_cast<const WT*>(a.norm_w) + k0 + k);
+                    else
+                        nvf[i] = *reinterpret_cast<const float4*>(static_cast<const WT*>(a.norm_w) + k0 + k);
+                }
+            }
+            // 2. weight loads: in flight while the activations are normalised and staged
+            uint4 w0v[U], w1v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int cc = min(lane + kWave * u, nchunks - 1);
+                w0v[u] = ld16_stream(row0 + k0 + (size_t)cc * VEC);
+                w1v[u] = ld16_stream(row1 + k0 + (size_t)cc * VEC);
+            }
+            asm volatile("" ::: "memory");   // keep the weight loads issued before the staging
+            // 3. norm weights to fp32; 0/1 factors for rows past M and (for the statistics)
+            //    for duplicated loads past the segment end -- arithmetic, no branches
+            float kin[XPT];
+#pragma unroll
+            for (int i = 0; i < XPT; ++i) {
+                kin[i] = (tid + i * kThreads) * 4 < klen ? 1.f : 0.f;
+                if (NORM && kIsBf16<WT>)
+                    nvf[i] = make_float4(bf16lo(nv[i].x), bf16hi(nv[i].x), bf16lo(nv[i].y), bf16hi(nv[i].y));
+            }
+            float scale[MB];
+#pragma unroll
+            for (int m = 0; m < MB; ++m) scale[m] = (m0 + m < a.M) ? rstd[m] : 0.f;
+            // 4. RMS statistics when the whole row is this segment
+            if (NORM && one_seg) {
+#pragma unroll
+                for (int m = 0; m < MB; ++m) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int i = 0; i < XPT; ++i)
+                        ss += kin[i] * (xv[m][i].x * xv[m][i].x + xv[m][i].y * xv[m][i].y +
+                                        xv[m][i].z * xv[m][i].z + xv[m][i].w * xv[m][i].w);
+                    ss = wave_sum(ss);
+                    if (lane == 0) red[wid][m] = ss;
+                }
+                lds_barrier();
+#pragma unroll
+                for (int m = 0; m < MB; ++m) {
+                    float t = 0.f;
+#pragma unroll
+                    for (int w = 0; w < kWavesPerBlock; ++w) t += red[w][m];
+                    scale[m] = (m0 + m < a.M) ? rsqrtf(t / (float)a.K + a.eps) : 0.f;
+                }
+            }
+            // 5. normalise, round to the stored precision, stage in LDS (positions past the
+            //    segment end hold duplicates and are never read)
+#pragma unroll
+            for (int i = 0; i < XPT; ++i) {
+                const int k = (tid + i * kThreads) * 4;
+#pragma unroll
+                for (int m = 0; m < MB; ++m) {
+                    float4 v = xv[m][i];
                     if (NORM) {
-                        const WT* nw = static_cast<const WT*>(a.norm_w) + k0 + k;
-                        const float r = rstd_s[m];
-                        v.x = v.x * r * Elem<WT>::load(nw, 0);
-                        v.y = v.y * r * Elem<WT>::load(nw, 1);
-                        v.z = v.z * r * Elem<WT>::load(nw, 2);
-                        v.w = v.w * r * Elem<WT>::load(nw, 3);
+                        v.x = v.x * scale[m] * nvf[i].x;
+                        v.y = v.y * scale[m] * nvf[i].y;
+                        v.z = v.z * scale[m] * nvf[i].z;
+                        v.w = v.w * scale[m] * nvf[i].w;
+                    } else {
+                        v.x *= scale[m];
+                        v.y *= scale[m];
+                        v.z *= scale[m];
+                        v.w *= scale[m];
                     }
+                    if (kIsBf16<WT>) {
+                        v.x = round_bf16(v.x);
+                        v.y = round_bf16(v.y);
+                        v.z = round_bf16(v.z);
+                        v.w = round_bf16(v.w);
+                    }
+                    *reinterpret_cast<float4*>(&xs[m][k]) = v;
                 }
-                *reinterpret_cast<float4*>(&xs[m][k]) = v;
             }
-            __syncthreads();
-            if (active) {
-                const int nchunks = klen / VEC;
-                const WT* p0 = row0 + k0;
-                const WT* p1 = row1 + k0;
-                for (int c = lane; c < nchunks; c += kWave * U) {
-                    uint4 w0v[U], w1v[U];
+            lds_barrier();
+            // 6. dot products (chunks past the row end were loaded clamped and are skipped)
 #pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int cc = c + kWave * u;
-                        if (cc < nchunks) {
-                            w0v[u] = ld16_stream(p0 + (size_t)cc * VEC);
-                            w1v[u] = ld16_stream(p1 + (size_t)cc * VEC);
-                        }
-                    }
+            for (int u = 0; u < U; ++u) {
+                const int cc = lane + kWave * u;
+                if (cc < nchunks) {
+                    float f0[VEC], f1[VEC];
+                    Elem<WT>::unpack(w0v[u], f0);
+                    Elem<WT>::unpack(w1v[u], f1);
 #pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int cc = c + kWave * u;
-                        if (cc < nchunks) {
-                            float f0[VEC], f1[VEC];
-                            Elem<WT>::unpack(w0v[u], f0);
-                            Elem<WT>::unpack(w1v[u], f1);
+                    for (int m = 0; m < MB; ++m) {
+                        const float* xp = &xs[m][cc * VEC];
 #pragma unroll
-                            for (int m = 0; m < MB; ++m) {
-                                const float* xp = &xs[m][cc * VEC];
-#pragma unroll
-                                for (int j = 0; j < VEC; j += 4) {
-                                    const float4 xv = *reinterpret_cast<const float4*>(xp + j);
-                                    acc[m][0] += f0[j] * xv.x + f0[j + 1] * xv.y + f0[j + 2] * xv.z + f0[j + 3] * xv.w;
-                                    acc[m][1] += f1[j] * xv.x + f1[j + 1] * xv.y + f1[j + 2] * xv.z + f1[j + 3] * xv.w;
-                                }
-                            }
+                        for (int j = 0; j < VEC; j += 4) {
+                            const float4 xq = *reinterpret_cast<const float4*>(xp + j);
+                            acc[m][0] += f0[j] * xq.x + f0[j + 1] * xq.y + f0[j + 2] * xq.z + f0[j + 3] * xq.w;
+                            acc[m][1] += f1[j] * xq.x + f1[j + 1] * xq.y + f1[j + 2] * xq.z + f1[j + 3] * xq.w;
                         }
                     }
                 }
             }
+            lds_barrier();   // xs and red are rewritten next
         }
 
-        if (active) {
 #pragma unroll
-            for (int m = 0; m < MB; ++m) {
-                acc[m][0] = wave_sum(acc[m][0]);
-                acc[m][1] = wave_sum(acc[m][1]);
-            }
+        for (int m = 0; m < MB; ++m) {
+            acc[m][0] = wave_sum(acc[m][0]);
+            acc[m][1] = wave_sum(acc[m][1]);
+        }
+        if (active) {
 #pragma unroll
             for (int m = 0; m < MB; ++m) {
                 const int row = m0 + m;

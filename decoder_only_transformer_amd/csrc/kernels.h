@@ -48,6 +48,8 @@ struct GemmArgs {
     void* out16; int64_t ldo16;    // SWIGLU (bf16)
     float* resid; int64_t ldr;
     QkvTarget qkv;
+    int splits;            // K splits (RESID only): partials [splits][M][N] -> `part`, then reduced
+    float* part;
 };
 
 // Causal attention for a set of query rows against the KV cache (one query position per
@@ -59,6 +61,7 @@ struct AttnArgs {
     void* out;             // [rows][n_heads*hd], fp32 or bf16 (out_bf16)
     int out_bf16;
     float* part;           // [rows][n_heads][n_split][hd + 2] partials when n_split > 1
+    int* counters;         // [rows][n_kv_heads] arrival counters (zero between launches)
     int rows, n_heads, n_kv_heads, head_dim, max_seq;
     int row0;              // first row of this launch (launches are split at 65535 rows)
     int start_pos, seqlen; // row t -> b = t / seqlen, position start_pos + t % seqlen

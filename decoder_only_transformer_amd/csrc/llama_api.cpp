@@ -26,12 +26,14 @@ using namespace llk;
 namespace {
 
 constexpr int kMaxSplit = 32;
+constexpr int kMaxSplitK = 8;      // K splits of a residual GEMM at small prefill sizes
+constexpr int kSplitKRows = 512;   // prefill rows up to which split-K is considered
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t k_cache, v_cache, rope, h32, q32, o32, g32, act16, g16, part, total;
+    size_t k_cache, v_cache, rope, h32, q32, o32, g32, act16, g16, part, counters, splitk, total;
     size_t kv_layer_elems;   // elements of one layer's K (or V) cache
 };
 
@@ -84,6 +86,9 @@ Layout layout_of(const llama_args& a) {
     L.act16 = fp32 ? off : take(maxT * (size_t)(a.dim > (int)nq ? a.dim : (int)nq) * 2);
     L.g16 = fp32 ? off : take(maxT * (size_t)a.hidden_dim * 2);
     L.part = take(maxB * (size_t)a.n_heads * kMaxSplit * (hd + 2) * sizeof(float));
+    L.counters = take(maxB * (size_t)a.n_kv_heads * sizeof(int));
+    // split-K partials of the residual GEMMs, used while a prefill has at most kSplitKRows rows
+    L.splitk = fp32 ? off : take((size_t)kMaxSplitK * std::min(maxT, (size_t)kSplitKRows) * a.dim * sizeof(float));
     L.total = off;
     return L;
 }
@@ -170,6 +175,7 @@ llama_status run_attention(const llama_ctx* c, int l, int rows, int seqlen, int 
     at.out = out;
     at.out_bf16 = out_bf16 ? 1 : 0;
     at.part = c->at<float>(c->L.part);
+    at.counters = c->at<int>(c->L.counters);
     at.rows = rows;
     at.n_heads = c->a.n_heads;
     at.n_kv_heads = c->a.n_kv_heads;
@@ -182,7 +188,7 @@ llama_status run_attention(const llama_ctx* c, int l, int rows, int seqlen, int 
     int n_split = 1;
     if (allow_split) {
         const int base = rows * c->a.n_kv_heads;
-        const int want = (1024 + base - 1) / base;
+        const int want = (512 + base - 1) / base;
         const int by_len = (ctx + 63) / 64;
         n_split = std::max(1, std::min(kMaxSplit, std::min(want, by_len)));
     }
@@ -233,6 +239,17 @@ llama_status block_gemv(const llama_ctx* c, int l, int M, int seqlen, int start_
     return LLAMA_OK;
 }
 
+// K splits for a residual GEMM of T rows and N = dim columns: enough workgroups to cover the
+// chip (~2 per CU) while keeping at least 8 BK-steps per split.
+int residual_splits(const llama_ctx* c, int T, int K) {
+    if (T > kSplitKRows) return 1;
+    const int bm = T <= 64 ? 64 : 128, bn = 64;
+    const int tiles = ((T + bm - 1) / bm) * ((c->a.dim + bn - 1) / bn);
+    int sp = (512 + tiles - 1) / tiles;
+    sp = std::min(sp, std::max(1, K / 64 / 8));
+    return std::max(1, std::min(sp, kMaxSplitK));
+}
+
 // One transformer block on the bf16 MFMA path for T = bsz*seqlen prefill rows.
 llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_pos, hipStream_t s) {
     const llama_layer_weights& W = c->layers[l];
@@ -254,6 +271,7 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
     g = GemmArgs{};
     g.a = act; g.lda = c->nq; g.M = T; g.K = c->nq; g.N = D;
     g.w0 = W.wo; g.resid = h; g.ldr = D;
+    g.splits = residual_splits(c, T, c->nq); g.part = c->at<float>(c->L.splitk);
     LAUNCH(c, LLAMA_KC_GEMM_WO, s, launch_gemm(EPI_RESID, g, s));
 
     LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.ffn_norm, c->a.norm_eps, act, D, s));
@@ -265,6 +283,7 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
     g = GemmArgs{};
     g.a = g16; g.lda = F; g.M = T; g.K = F; g.N = D;
     g.w0 = W.w2; g.resid = h; g.ldr = D;
+    g.splits = residual_splits(c, T, F); g.part = c->at<float>(c->L.splitk);
     LAUNCH(c, LLAMA_KC_GEMM_W2, s, launch_gemm(EPI_RESID, g, s));
     return LLAMA_OK;
 }
@@ -333,6 +352,7 @@ llama_status llama_init(const llama_args* a, const llama_weights* w, void* d_wor
         }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (hipMemcpyAsync(c->ws + L.rope, tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipMemsetAsync(c->ws + L.counters, 0, (size_t)a->max_batch_size * a->n_kv_heads * sizeof(int), s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess) {
         delete c;
         return LLAMA_ERR_HIP;

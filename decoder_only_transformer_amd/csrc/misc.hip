@@ -54,14 +54,28 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2)
     }
 }
 
-__global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int vocab, int64_t stride,
-                                                     int32_t* out) {
-    __shared__ float sv[4];
-    __shared__ int si[4];
+// One 1024-thread workgroup per row; 16-byte loads when the row is 16-byte aligned.
+__global__ __launch_bounds__(1024) void argmax_kernel(const float* logits, int vocab, int64_t stride,
+                                                      int32_t* out) {
+    __shared__ float sv[16];
+    __shared__ int si[16];
     const float* x = logits + (size_t)blockIdx.x * stride;
     float best = 0.f;
     int bi = -1;
-    for (int k = threadIdx.x; k < vocab; k += 256) {
+    const bool vec = ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+    int k0 = 0;
+    if (vec) {
+        const int n4 = vocab / 4;
+        for (int i = threadIdx.x; i < n4; i += 1024) {
+            const float4 v = reinterpret_cast<const float4*>(x)[i];
+            if (v.x == v.x) argmax_merge(best, bi, v.x, 4 * i);
+            if (v.y == v.y) argmax_merge(best, bi, v.y, 4 * i + 1);
+            if (v.z == v.z) argmax_merge(best, bi, v.z, 4 * i + 2);
+            if (v.w == v.w) argmax_merge(best, bi, v.w, 4 * i + 3);
+        }
+        k0 = n4 * 4;
+    }
+    for (int k = k0 + threadIdx.x; k < vocab; k += 1024) {
         const float v = x[k];
         if (v == v) argmax_merge(best, bi, v, k);   // skips NaN
     }
@@ -77,7 +91,7 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* logits, int vo
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        for (int w = 1; w < 4; ++w) argmax_merge(best, bi, sv[w], si[w]);
+        for (int w = 1; w < 16; ++w) argmax_merge(best, bi, sv[w], si[w]);
         out[blockIdx.x] = bi;
     }
 }
@@ -111,7 +125,7 @@ hipError_t launch_rmsnorm_bf16(const float* h, int64_t ldh, int rows, int dim, c
 
 hipError_t launch_argmax(const float* logits, int bsz, int vocab, int64_t stride, int32_t* out,
                          hipStream_t s) {
-    hipLaunchKernelGGL(argmax_kernel, dim3(bsz), dim3(256), 0, s, logits, vocab, stride, out);
+    hipLaunchKernelGGL(argmax_kernel, dim3(bsz), dim3(1024), 0, s, logits, vocab, stride, out);
     return hipGetLastError();
 }
 

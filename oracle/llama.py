@@ -21,6 +21,13 @@ Readings taken where the pages leave a step open (each also listed in the design doc)
   R11 prompts are left-aligned in the token rectangle, pads after (generate's layout).
   R12 total_len = min(max_seq_len, max_gen_len + max_prompt_len).
   R16 argmax ties go to the lowest index.
+  R18 storage precision: with storage="bf16" the tensors the bf16 method stores in 16 bits
+      -- the normalised GEMM operands, q, the cached k and v, the attention output and the
+      gated FFN activation -- are rounded to bf16 (round-to-nearest-even) where they are
+      produced; every operation still computes in the working precision.  The pages run
+      the reference with 16-bit activations throughout (fp16, [AG] 6.4 and the loader
+      description in [ST]); the bf16 method keeps the residual stream and all accumulation
+      in fp32 and rounds only at these points.  storage=None is the plain definition.
 """
 from __future__ import annotations
 
@@ -72,6 +79,22 @@ def kv_cache_bytes(max_batch_size: int, max_seq_len: int, n_kv_heads: int, head_
     """Size of one cache tensor of one layer ([AG] 6.2): the cache is a dense
     (max_batch_size, max_seq_len, n_kv_heads, head_dim) array allocated up front."""
     return max_batch_size * max_seq_len * n_kv_heads * head_dim * bytes_per_element
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest bf16 value (8 significant bits, ties to even), kept in x's
+    dtype.  Written from the format's definition: with x = m * 2^e, 0.5 <= |m| < 1, keep
+    m to 8 bits."""
+    m, e = np.frexp(x)
+    return np.ldexp(np.round(m * 256.0) / 256.0, e).astype(x.dtype, copy=False)
+
+
+def _storage_fn(storage: Optional[str]):
+    if storage is None:
+        return lambda x: x
+    if storage == "bf16":
+        return round_bf16
+    raise ValueError(storage)
 
 
 def rms_norm(x: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
@@ -186,9 +209,11 @@ class Oracle:
     `weights` is the dict layout of synth.gen_weights (torch or numpy arrays), or a
     callable (name, layer) -> array with layer = -1 for the global tensors."""
 
-    def __init__(self, args: ModelArgs, weights, max_batch_size: int, dtype=np.float32):
+    def __init__(self, args: ModelArgs, weights, max_batch_size: int, dtype=np.float32,
+                 storage: Optional[str] = None):
         self.args = args
         self.dtype = dtype
+        self.st = _storage_fn(storage)
         self.w: WeightFn = weights if callable(weights) else _dense_weights(weights, dtype)
         shape = (args.n_layers, max_batch_size, args.max_seq_len, args.kv_heads, args.head_dim)
         self.cache_k = np.zeros(shape, dtype=dtype)
@@ -202,24 +227,26 @@ class Oracle:
         assert start_pos + S <= a.max_seq_len and B <= self.cache_k.shape[1]
         hd, H, KVH = a.head_dim, a.n_heads, a.kv_heads
         positions = list(range(start_pos, start_pos + S))
+        st = self.st
         h = self.w("tok_embeddings", -1)[tokens]                       # (B, S, D)
         for l in range(a.n_layers):
             w = lambda n: self.w(n, l)  # noqa: E731
-            x = rms_norm(h, w("attention_norm"), a.norm_eps)
+            x = st(rms_norm(h, w("attention_norm"), a.norm_eps))
             q = (x @ w("wq").T).reshape(B, S, H, hd)
             k = (x @ w("wk").T).reshape(B, S, KVH, hd)
             v = (x @ w("wv").T).reshape(B, S, KVH, hd)
-            q = apply_rope(q, positions, a.rope_theta)
-            k = apply_rope(k, positions, a.rope_theta)
+            q = st(apply_rope(q, positions, a.rope_theta))
+            k = st(apply_rope(k, positions, a.rope_theta))
             self.cache_k[l, :B, start_pos:start_pos + S] = k
-            self.cache_v[l, :B, start_pos:start_pos + S] = v
+            self.cache_v[l, :B, start_pos:start_pos + S] = st(v)
             keys = self.cache_k[l, :B, :start_pos + S]
             vals = self.cache_v[l, :B, :start_pos + S]
-            o = attention(q, keys, vals, start_pos, a.n_rep).reshape(B, S, H * hd)
+            o = st(attention(q, keys, vals, start_pos, a.n_rep).reshape(B, S, H * hd))
             h = h + o @ w("wo").T
-            x = rms_norm(h, w("ffn_norm"), a.norm_eps)
-            h = h + feed_forward(x, w("w1"), w("w2"), w("w3"))
-        x = rms_norm(h, self.w("norm", -1), a.norm_eps)
+            x = st(rms_norm(h, w("ffn_norm"), a.norm_eps))
+            g = st(silu(x @ w("w1").T) * (x @ w("w3").T))
+            h = h + g @ w("w2").T
+        x = st(rms_norm(h, self.w("norm", -1), a.norm_eps))
         return x @ self.w("output", -1).T
 
 
@@ -264,13 +291,14 @@ def greedy_generate(model: Oracle, prompts: List[List[int]], max_gen_len: int,
 
 
 def teacher_forced_logits(args: ModelArgs, weights, tokens: np.ndarray,
-                          dtype=np.float32, layer_hook: Optional[Callable[[int], None]] = None
-                          ) -> np.ndarray:
+                          dtype=np.float32, layer_hook: Optional[Callable[[int], None]] = None,
+                          storage: Optional[str] = None) -> np.ndarray:
     """Logits at every position of a fixed token sequence in one causal pass from position 0,
     computed layer by layer (each layer's weights are touched once).  By the causal mask
     ([AG] 8.4 note), position j's logits equal what an incremental run would emit at the
     call that ends at j.  tokens (B, T) -> logits (B, T, vocab)."""
     wf: WeightFn = weights if callable(weights) else _dense_weights(weights, dtype)
+    st = _storage_fn(storage)
     tokens = np.asarray(tokens)
     B, T = tokens.shape
     hd, H, KVH = args.head_dim, args.n_heads, args.kv_heads
@@ -280,15 +308,16 @@ def teacher_forced_logits(args: ModelArgs, weights, tokens: np.ndarray,
         if layer_hook is not None:
             layer_hook(l)
         w = lambda n: wf(n, l)  # noqa: E731
-        x = rms_norm(h, w("attention_norm"), args.norm_eps)
-        q = apply_rope((x @ w("wq").T).reshape(B, T, H, hd), positions, args.rope_theta)
-        k = apply_rope((x @ w("wk").T).reshape(B, T, KVH, hd), positions, args.rope_theta)
-        v = (x @ w("wv").T).reshape(B, T, KVH, hd)
-        o = attention(q, k, v, 0, args.n_rep).reshape(B, T, H * hd)
+        x = st(rms_norm(h, w("attention_norm"), args.norm_eps))
+        q = st(apply_rope((x @ w("wq").T).reshape(B, T, H, hd), positions, args.rope_theta))
+        k = st(apply_rope((x @ w("wk").T).reshape(B, T, KVH, hd), positions, args.rope_theta))
+        v = st((x @ w("wv").T).reshape(B, T, KVH, hd))
+        o = st(attention(q, k, v, 0, args.n_rep).reshape(B, T, H * hd))
         h = h + o @ w("wo").T
-        x = rms_norm(h, w("ffn_norm"), args.norm_eps)
-        h = h + feed_forward(x, w("w1"), w("w2"), w("w3"))
-    x = rms_norm(h, wf("norm", -1), args.norm_eps)
+        x = st(rms_norm(h, w("ffn_norm"), args.norm_eps))
+        g = st(silu(x @ w("w1").T) * (x @ w("w3").T))
+        h = h + g @ w("w2").T
+    x = st(rms_norm(h, wf("norm", -1), args.norm_eps))
     return x @ wf("output", -1).T
 
 

@@ -374,3 +374,42 @@ def test_generate_stops_when_every_row_hit_eos():
     model = oracle.Oracle(a, W, 1, dtype=np.float64)
     tokens2, logits2 = oracle.greedy_generate(model, [[1, 2, 3]], max_gen_len=8, eos_id=first)
     assert len(logits2) == 1 and tokens2[0, 3] == first
+
+
+# ----------------------------------------------------------------------------- bf16 storage mode
+
+def test_round_bf16_matches_torch_rne():
+    rng = np.random.default_rng(30)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
+    # exact ties: values halfway between two bf16 numbers, both parities
+    base = torch.tensor(rng.standard_normal(1000), dtype=torch.float32).to(torch.bfloat16).float().numpy()
+    ties = (base.view(np.uint32) | np.uint32(0x8000)).view(np.float32)
+    x = np.concatenate([x, ties, np.array([0.0, -0.0, 1.0, -3.5], dtype=np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    got = oracle.round_bf16(x)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    # float64 input: result is a bf16 value within half a bf16 ulp, and idempotent
+    y = rng.standard_normal(10000) * 3
+    r = oracle.round_bf16(y)
+    assert np.array_equal(oracle.round_bf16(r), r)
+    assert np.array_equal(r.astype(np.float32), torch.from_numpy(r.astype(np.float32)).to(torch.bfloat16).float().numpy())
+    m, e = np.frexp(y)
+    assert np.all(np.abs(r - y) <= np.ldexp(1.0 / 512, e) * (1 + 1e-12))
+
+
+def test_bf16_storage_keeps_prefill_equal_to_decode_and_cache_in_bf16():
+    a = small_args()
+    W = random_weights(a, seed=31)
+    tokens = np.random.default_rng(32).integers(0, a.vocab_size, size=(2, 10))
+    full = oracle.Oracle(a, W, 2, dtype=np.float64, storage="bf16")
+    lf = full.forward(tokens, 0)
+    inc = oracle.Oracle(a, W, 2, dtype=np.float64, storage="bf16")
+    steps = np.stack([inc.forward(tokens[:, j:j + 1], j)[:, 0] for j in range(10)], 1)
+    np.testing.assert_allclose(steps, lf, rtol=1e-9, atol=1e-9)
+    kv = full.cache_k[:, :, :10]
+    assert np.array_equal(oracle.round_bf16(kv), kv)
+    tf = oracle.teacher_forced_logits(a, W, tokens, np.float64, storage="bf16")
+    np.testing.assert_allclose(tf, lf, rtol=1e-9, atol=1e-9)
+    plain = oracle.Oracle(a, W, 2, dtype=np.float64).forward(tokens, 0)
+    d = np.abs(plain - lf).max()
+    assert 1e-6 < d < 5e-2     # rounding changes the logits, a little
