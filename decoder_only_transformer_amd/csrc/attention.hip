@@ -13,7 +13,6 @@
 namespace llk {
 namespace {
 
-constexpr int kSlots = 16;   // 4 waves x 4 lane groups
 constexpr int kMaxSplitMerge = 32;   // largest split count the in-kernel merge handles
 
 // N elements of a K or V row as raw bits (4, 8, 16 or 32 bytes), unpacked later so the
@@ -52,12 +51,35 @@ struct RawRow {
 
 
 
-template <typename KT, int HD, int NREP, bool OUT_BF16>
-__global__ __launch_bounds__(256) void attn_rows_kernel(AttnArgs a) {
+// Merge running softmax state (m, l, acc) with the one held by lane ^ `o`.
+template <int NREP, int EPL>
+__device__ __forceinline__ void merge_with_lane(float (&m)[NREP], float (&l)[NREP],
+                                                float (&acc)[NREP][EPL], int o) {
+#pragma unroll
+    for (int r = 0; r < NREP; ++r) {
+        const float mo = __shfl_xor(m[r], o, kWave);
+        const float lo = __shfl_xor(l[r], o, kWave);
+        const float M = fmaxf(m[r], mo);
+        const float a1 = (M == -INFINITY) ? 0.f : __expf(m[r] - M);
+        const float a2 = (M == -INFINITY) ? 0.f : __expf(mo - M);
+        l[r] = l[r] * a1 + lo * a2;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const float ao = __shfl_xor(acc[r][e], o, kWave);
+            acc[r][e] = acc[r][e] * a1 + ao * a2;
+        }
+        m[r] = M;
+    }
+}
+
+template <typename KT, int HD, int NREP, bool OUT_BF16, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(AttnArgs a) {
     constexpr int EPL = HD / 16;
-    __shared__ float s_m[kSlots][NREP];
-    __shared__ float s_l[kSlots][NREP];
-    __shared__ float s_acc[kSlots][NREP][HD];
+    constexpr int SLOTS = WAVES * 4;     // 16-lane groups, one key each at a time
+    constexpr int PF = 4;                // keys per group whose loads are in flight together
+    __shared__ float s_m[WAVES][NREP];
+    __shared__ float s_l[WAVES][NREP];
+    __shared__ float s_acc[WAVES][NREP][HD];
 
     const int split = blockIdx.x, kvh = blockIdx.y, t = a.row0 + blockIdx.z;
     const int b = t / a.seqlen;
@@ -71,12 +93,18 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnArgs a) {
     const int qstride = a.n_heads * HD;
     const int64_t kv_row = (int64_t)a.n_kv_heads * HD;
 
+    const size_t base = (size_t)b * a.max_seq * kv_row + (size_t)kvh * HD + gl * EPL;
+    const KT* kb = static_cast<const KT*>(a.cache_k) + base;
+    const KT* vb = static_cast<const KT*>(a.cache_v) + base;
+
+    // q stays unscaled; 1/sqrt(hd) is applied to each score.  Its loads are independent of
+    // the K/V loads below and complete under them.
     float q[NREP][EPL];
 #pragma unroll
     for (int r = 0; r < NREP; ++r)
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
-            q[r][e] = a.q[(size_t)t * qstride + (kvh * NREP + r) * HD + gl * EPL + e] * a.scale;
+            q[r][e] = a.q[(size_t)t * qstride + (kvh * NREP + r) * HD + gl * EPL + e];
 
     float m[NREP], l[NREP], acc[NREP][EPL];
 #pragma unroll
@@ -87,23 +115,17 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnArgs a) {
         for (int e = 0; e < EPL; ++e) acc[r][e] = 0.f;
     }
 
-    const size_t base = (size_t)b * a.max_seq * kv_row + (size_t)kvh * HD + gl * EPL;
-    const KT* kb = static_cast<const KT*>(a.cache_k) + base;
-    const KT* vb = static_cast<const KT*>(a.cache_v) + base;
-    constexpr int PF = 4;   // keys per group whose loads are in flight together
-    for (int j = j0 + slot; j < j1; j += PF * kSlots) {
+    for (int j = j0 + slot; j < j1; j += PF * SLOTS) {
         RawRow<KT, EPL> kr[PF], vr[PF];
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
-            const int jj = j + u * kSlots;
-            if (jj < j1) {
-                kr[u].load(kb + (size_t)jj * kv_row);
-                vr[u].load(vb + (size_t)jj * kv_row);
-            }
+            const int jj = min(j + u * SLOTS, j1 - 1);   // clamped: unconditional loads
+            kr[u].load(kb + (size_t)jj * kv_row);
+            vr[u].load(vb + (size_t)jj * kv_row);
         }
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
-            if (j + u * kSlots >= j1) break;
+            if (j + u * SLOTS >= j1) break;
             float kf[EPL], vf[EPL];
             kr[u].unpack(kf);
             vr[u].unpack(vf);
@@ -112,7 +134,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnArgs a) {
                 float s = 0.f;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) s += q[r][e] * kf[e];
-                s = group_sum<16>(s);
+                s = group_sum<16>(s) * a.scale;
                 const float mn = fmaxf(m[r], s);
                 const float sc = __expf(m[r] - mn);
                 const float p = __expf(s - mn);
@@ -124,13 +146,18 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnArgs a) {
         }
     }
 
+    // the four 16-lane groups of a wave hold the same d range: merge them by shuffles
+    merge_with_lane<NREP, EPL>(m, l, acc, 16);
+    merge_with_lane<NREP, EPL>(m, l, acc, 32);
+    if (grp == 0) {
 #pragma unroll
-    for (int r = 0; r < NREP; ++r) {
+        for (int r = 0; r < NREP; ++r) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) s_acc[slot][r][gl * EPL + e] = acc[r][e];
-        if (gl == 0) {
-            s_m[slot][r] = m[r];
-            s_l[slot][r] = l[r];
+            for (int e = 0; e < EPL; ++e) s_acc[wid][r][gl * EPL + e] = acc[r][e];
+            if (gl == 0) {
+                s_m[wid][r] = m[r];
+                s_l[wid][r] = l[r];
+            }
         }
     }
     __syncthreads();
@@ -139,14 +166,14 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnArgs a) {
         const int r = idx / HD, d = idx - r * HD;
         float M = -INFINITY;
 #pragma unroll
-        for (int sl = 0; sl < kSlots; ++sl) M = fmaxf(M, s_m[sl][r]);
+        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][r]);
         float L = 0.f, A = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
-            for (int sl = 0; sl < kSlots; ++sl) {
-                const float w = __expf(s_m[sl][r] - M);
-                L += s_l[sl][r] * w;
-                A += s_acc[sl][r][d] * w;
+            for (int w = 0; w < WAVES; ++w) {
+                const float wt = __expf(s_m[w][r] - M);
+                L += s_l[w][r] * wt;
+                A += s_acc[w][r][d] * wt;
             }
         }
         const int h = kvh * NREP + r;
@@ -213,6 +240,11 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnArgs a) {
     if (tid == 0) a.counters[(size_t)t * a.n_kv_heads + kvh] = 0;
 }
 
+// Waves per workgroup: many for single-token rows (decode: one workgroup covers a short
+// context in one round of loads), four for prefill rows; capped so that the per-lane state
+// of NREP heads fits the register budget.
+template <int NREP> constexpr int kDecodeWaves = NREP <= 2 ? 16 : 8;
+
 template <typename KT, int HD, int NREP, bool OB>
 hipError_t launch4(const AttnArgs& args, hipStream_t s) {
     constexpr int kMaxZ = 65535;
@@ -220,8 +252,12 @@ hipError_t launch4(const AttnArgs& args, hipStream_t s) {
         AttnArgs a = args;
         a.row0 = r0;
         const int n = min(kMaxZ, args.rows - r0);
-        hipLaunchKernelGGL((attn_rows_kernel<KT, HD, NREP, OB>), dim3(a.n_split, a.n_kv_heads, n),
-                           dim3(256), 0, s, a);
+        const dim3 grid(a.n_split, a.n_kv_heads, n);
+        if (a.seqlen == 1)
+            hipLaunchKernelGGL((attn_rows_kernel<KT, HD, NREP, OB, kDecodeWaves<NREP>>), grid,
+                               dim3(64 * kDecodeWaves<NREP>), 0, s, a);
+        else
+            hipLaunchKernelGGL((attn_rows_kernel<KT, HD, NREP, OB, 4>), grid, dim3(256), 0, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

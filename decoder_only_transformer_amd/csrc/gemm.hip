@@ -256,7 +256,8 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
     // Small M (short prefill): narrower tiles so enough workgroups stream the weights.
     if (a.M <= 64) return launch_tile<64, 64, 2, 2, EPI>(a, s);
     if (a.M <= 256) return launch_tile<128, 64, 2, 2, EPI>(a, s);
-    if (a.M <= 2048) return launch_tile<128, 128, 2, 2, EPI>(a, s);
+    // (the RoPE/KV-append epilogue does not fit 256x256 tiles without spilling)
+    if (a.M <= 2048 || EPI == EPI_QKV) return launch_tile<128, 128, 2, 2, EPI>(a, s);
     return launch_tile<256, 256, 4, 2, EPI>(a, s);
 }
 

@@ -187,9 +187,13 @@ llama_status run_attention(const llama_ctx* c, int l, int rows, int seqlen, int 
     const int ctx = start_pos + seqlen;   // longest visible prefix among the rows
     int n_split = 1;
     if (allow_split) {
-        const int base = rows * c->a.n_kv_heads;
-        const int want = (512 + base - 1) / base;
-        const int by_len = (ctx + 63) / 64;
+        // split the keys only when there are too few (row, kv head) pairs to fill the chip,
+        // and never below one round of loads per workgroup (slots x 4 keys)
+        const int n_rep = c->a.n_heads / c->a.n_kv_heads;
+        const int slots = 4 * (n_rep <= 2 ? 16 : 8);
+        const int pairs = rows * c->a.n_kv_heads;
+        const int want = (512 + pairs - 1) / pairs;
+        const int by_len = (ctx + 4 * slots - 1) / (4 * slots);
         n_split = std::max(1, std::min(kMaxSplit, std::min(want, by_len)));
     }
     int chunk = (ctx + n_split - 1) / n_split;
