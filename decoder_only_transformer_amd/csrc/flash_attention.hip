@@ -1,0 +1,197 @@
+// Causal grouped-query attention for prefill on bf16 MFMA (gfx950 v_mfma_f32_16x16x32_bf16).
+//
+// A workgroup owns one batch row, one kv head and 64 query rows, a query row being a
+// (position, head) pair of the n_rep heads that read this kv head (GQA is never
+// materialised: the K/V tile in LDS serves all of them).  Four waves own 16 rows each.
+// K/V advance in tiles of 64 keys up to the last position any row of the workgroup sees.
+//
+//  S^T = K Q^T    keys are the MFMA M dimension, so after the product each lane holds
+//                 4 consecutive keys of one query; per-query max and sum need only two
+//                 cross-lane steps (lanes l, l^16, l^32, l^48 share a query).
+//  O^T += V^T P^T the K dimension of this product is taken in a permuted order: lane group
+//                 g feeds keys {4g..4g+3} of the first 16-key half and {16+4g..16+4g+3} of
+//                 the second, exactly the 8 scores the lane already holds, so P never moves
+//                 between lanes.  V is staged transposed in LDS to match.
+//  P is split into a bf16 high part and a bf16 remainder (two MFMAs), so the weights keep
+//  ~16 significant bits and the attention is computed with fp32-softmax semantics; Q and K
+//  are bf16 tensors already (they are stored in bf16 by the projection).
+#include "common.h"
+#include "kernels.h"
+
+namespace llk {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kRows = 64;     // query rows per workgroup
+constexpr int kKeys = 64;     // keys per tile
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u16x8_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+template <int HD>
+__global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
+    constexpr int KS = HD / 32;            // MFMA k-steps over head_dim
+    constexpr int DT = HD / 16;            // 16-row tiles of head_dim in O^T
+    constexpr int KLD = HD + 8;            // padded K row (elements)
+    constexpr int VLD = kKeys + 8;         // padded V^T row (elements)
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[kKeys][KLD];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[HD][VLD];
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int fr = lane & 15, g = lane >> 4;
+    const int qtile = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int n_rep = a.n_heads / a.n_kv_heads;
+    const int qstride = a.n_heads * HD;
+    const int64_t kv_row = (int64_t)a.n_kv_heads * HD;
+
+    // This lane's query row (column fr of the wave's S^T tile).
+    const int r_local = qtile * kRows + wid * 16 + fr;
+    const int s_idx = r_local / n_rep;                     // position within the prompt
+    const int head = kvh * n_rep + r_local % n_rep;
+    const bool row_ok = s_idx < a.seqlen;
+    const int qpos = a.start_pos + (row_ok ? s_idx : a.seqlen - 1);   // absolute position
+
+    // Q fragments (bf16-valued fp32 in the q buffer -> exact bf16).
+    bf16x8_t qf[KS];
+    {
+        const float* qp = a.q + ((size_t)b * a.seqlen + (row_ok ? s_idx : 0)) * qstride + head * HD;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u16x8_t v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = f32_to_bf16(qp[ks * 32 + g * 8 + e]);
+            qf[ks] = as_bf16x8(v);
+        }
+    }
+
+    // Keys visible to the workgroup: up to the largest position among its rows.
+    const int last_row = min(qtile * kRows + kRows - 1, a.seqlen * n_rep - 1);
+    const int kend = a.start_pos + last_row / n_rep + 1;     // exclusive
+    const int first_row = qtile * kRows;
+    const int kfull = a.start_pos + first_row / n_rep + 1;   // keys < kfull are visible to all rows
+
+    float m = -INFINITY, l = 0.f;
+    f32x4 o[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.cache_k) + (size_t)b * a.max_seq * kv_row + (size_t)kvh * HD;
+    const uint16_t* vbase = static_cast<const uint16_t*>(a.cache_v) + (size_t)b * a.max_seq * kv_row + (size_t)kvh * HD;
+    const float scale = a.scale;
+
+    for (int k0 = 0; k0 < kend; k0 += kKeys) {
+        // ---- stage K (row-major) and V (transposed) of keys [k0, k0+64) in LDS
+        __syncthreads();
+        constexpr int CH = HD / 8;                   // 16-byte chunks per key row
+        for (int c = tid; c < kKeys * CH; c += 256) {
+            const int key = c % kKeys, d8 = (c / kKeys) * 8;   // key-fastest: V^T stores spread over banks
+            const int kk = min(k0 + key, kend - 1);   // clamp: rows past kend are masked anyway
+            const uint4 kv = ld16(kbase + (size_t)kk * kv_row + d8);
+            *reinterpret_cast<uint4*>(&Ks[key][d8]) = kv;
+            const uint4 vv = ld16(vbase + (size_t)kk * kv_row + d8);
+            const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Vt[d8 + 2 * i][key] = static_cast<uint16_t>(w[i] & 0xffffu);
+                Vt[d8 + 2 * i + 1][key] = static_cast<uint16_t>(w[i] >> 16);
+            }
+        }
+        __syncthreads();
+
+        // ---- S^T for 4 key tiles of 16: lane holds keys k0 + 16j + 4g + e, query fr
+        f32x4 st[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            st[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&Ks[16 * j + fr][ks * 32 + g * 8]);
+                st[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], st[j], 0, 0, 0);
+            }
+        }
+        // ---- scale, causal mask, online softmax (per query = per lane column)
+        const bool need_mask = (k0 + kKeys > kfull) || !row_ok;
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float v = st[j][e] * scale;
+                if (need_mask) {
+                    const int key = k0 + 16 * j + 4 * g + e;
+                    if (key > qpos || key >= kend || !row_ok) v = -INFINITY;
+                }
+                st[j][e] = v;
+                tmax = fmaxf(tmax, v);
+            }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+        const float mn = fmaxf(m, tmax);
+        const float alpha = (mn == -INFINITY) ? 1.f : __expf(m - mn);
+        float psum = 0.f;
+        u16x8_t phi[2], plo[2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p = (mn == -INFINITY) ? 0.f : __expf(st[j][e] - mn);
+                psum += p;
+                const uint16_t hi = f32_to_bf16(p);
+                const uint16_t lo = f32_to_bf16(p - bf16_to_f32(hi));
+                // k-slot of this key in the permuted PV order: tile pair kk = j / 2,
+                // slot (j % 2) * 4 + e within the lane group's 8
+                phi[j >> 1][(j & 1) * 4 + e] = hi;
+                plo[j >> 1][(j & 1) * 4 + e] = lo;
+            }
+        psum += __shfl_xor(psum, 16, kWave);
+        psum += __shfl_xor(psum, 32, kWave);
+        l = l * alpha + psum;
+        m = mn;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) o[t] *= alpha;
+
+        // ---- O^T += V^T P^T over the two 32-key halves (permuted k order)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                const uint16_t* vr = &Vt[16 * t + fr][32 * kk];
+                const uint2 v0 = *reinterpret_cast<const uint2*>(vr + 4 * g);
+                const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * g);
+                u16x8_t vv;
+                vv[0] = v0.x & 0xffffu; vv[1] = v0.x >> 16; vv[2] = v0.y & 0xffffu; vv[3] = v0.y >> 16;
+                vv[4] = v1.x & 0xffffu; vv[5] = v1.x >> 16; vv[6] = v1.y & 0xffffu; vv[7] = v1.y >> 16;
+                const bf16x8_t vf = as_bf16x8(vv);
+                o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, as_bf16x8(phi[kk]), o[t], 0, 0, 0);
+                o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, as_bf16x8(plo[kk]), o[t], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- O = O^T / l, stored bf16 at [b*seqlen + s][head*hd + d]
+    if (!row_ok) return;
+    const float inv = 1.f / l;
+    uint16_t* out = static_cast<uint16_t*>(a.out) + ((size_t)b * a.seqlen + s_idx) * qstride + head * HD;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[16 * t + 4 * g + e] = f32_to_bf16(o[t][e] * inv);
+}
+
+}  // namespace
+
+hipError_t launch_flash_prefill(const FlashArgs& a, hipStream_t s) {
+    const int n_rep = a.n_heads / a.n_kv_heads;
+    const dim3 grid((a.seqlen * n_rep + kRows - 1) / kRows, a.n_kv_heads, a.bsz);
+    if (a.head_dim == 128)
+        hipLaunchKernelGGL(flash_prefill_kernel<128>, grid, dim3(256), 0, s, a);
+    else if (a.head_dim == 64)
+        hipLaunchKernelGGL(flash_prefill_kernel<64>, grid, dim3(256), 0, s, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace llk

@@ -69,6 +69,18 @@ struct AttnArgs {
     float scale;           // 1/sqrt(head_dim)
 };
 
+// Causal GQA attention of a prefill (bf16 MFMA): rows b*seqlen + s at positions start_pos + s.
+struct FlashArgs {
+    const float* q;        // [bsz*seqlen][n_heads*hd] (bf16-valued fp32)
+    const void* cache_k;   // layer base, bf16
+    const void* cache_v;
+    void* out;             // [bsz*seqlen][n_heads*hd] bf16
+    int bsz, seqlen, start_pos;
+    int n_heads, n_kv_heads, head_dim, max_seq;
+    float scale;
+};
+
+hipError_t launch_flash_prefill(const FlashArgs& a, hipStream_t s);
 hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, const void* table,
                         int wbf16, int vocab, int dim, float* h, hipStream_t s);
 hipError_t launch_rmsnorm_bf16(const float* h, int64_t ldh, int rows, int dim, const void* w,

@@ -226,6 +226,35 @@ def test_small_bf16_prefill_equals_token_by_token_decode():
     model.close()
 
 
+@pytest.mark.parametrize("name", ["gqa8", "mha"])
+def test_small_bf16_chunked_prefill_all_positions(name):
+    """Prefill in two chunks (the second at start_pos > 0, ragged against the 64-row tiles)
+    against the oracle's full forward, every position."""
+    wl = SMALL_BF16[name]
+    say(f"case {wl.name}: chunked prefill")
+    W = synth.gen_weights(wl, device="cuda")
+    P = synth.prompts(wl)
+    S = min(len(p) for p in P)
+    tok = np.array([p[:S] for p in P], dtype=np.int32)
+    B = tok.shape[0]
+    c = min(37, S - 7)
+    model = runtime.LlamaModel(args_of(wl), W)
+    dtok = torch.from_numpy(tok).cuda()
+    a = torch.empty((B, c, wl.vocab_size), device="cuda")
+    b = torch.empty((B, S - c, wl.vocab_size), device="cuda")
+    model.prefill(dtok, B, c, 0, a, all_positions=True)
+    model.prefill(dtok, B, S - c, c, b, all_positions=True, col=c)
+    torch.cuda.synchronize()
+    got = np.concatenate([a.cpu().numpy(), b.cpu().numpy()], 1)
+    ref = oracle.Oracle(oracle.args_from_workload(wl), host_weights(wl, W), B, np.float32,
+                        storage="bf16").forward(tok, 0)
+    d = np.abs(got - ref).max()
+    cos = ((got * ref).sum(-1) / np.linalg.norm(got, axis=-1) / np.linalg.norm(ref, axis=-1)).min()
+    say(f"  max|dlogit|={d:.3e} min cos={cos:.6f}")
+    assert d <= BF16_TOL and cos >= COS_MIN
+    model.close()
+
+
 def test_generator_bit_identical_on_gpu_and_cpu():
     wl = synth.WORKLOADS["llama2_7b_b1"]
     g = synth.gen_tensor(wl, "w2", 7, device="cuda").cpu()
