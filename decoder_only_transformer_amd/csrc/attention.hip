@@ -83,10 +83,14 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(AttnArgs a) {
 
     const int split = blockIdx.x, kvh = blockIdx.y, t = a.row0 + blockIdx.z;
     const int b = t / a.seqlen;
-    const int pos = a.start_pos + (t - b * a.seqlen);
+    const int start_pos = a.st ? a.st->pos : a.start_pos;
+    const int pos = start_pos + (t - b * a.seqlen);
     const int ctx = pos + 1;
-    const int j0 = split * a.chunk;
-    const int j1 = min(ctx, j0 + a.chunk);
+    // keys per split: given, or (graph replay) derived from this step's context as the host
+    // would: ceil(ctx / n_split) rounded up to 16
+    const int chunk = a.chunk ? a.chunk : ((start_pos + a.seqlen + a.n_split - 1) / a.n_split + 15) / 16 * 16;
+    const int j0 = split * chunk;
+    const int j1 = min(ctx, j0 + chunk);
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int grp = lane >> 4, gl = lane & 15;
     const int slot = wid * 4 + grp;

@@ -35,7 +35,7 @@ __device__ __forceinline__ const WT* qkv_row(const GemvArgs& a, int n) {
 template <typename WT>
 __device__ __forceinline__ void qkv_store(const QkvTarget& t, int m, int n0, float y0, float y1) {
     const int b = m / t.seqlen;
-    const int pos = t.start_pos + m % t.seqlen;
+    const int pos = (t.st ? t.st->pos : t.start_pos) + m % t.seqlen;
     const int hd = t.head_dim;
     if (n0 < t.nq + t.nk) {
         const float2 cs = t.rope[(size_t)pos * (hd / 2) + (n0 % hd) / 2];
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
                     } else if (EPI == EPI_SWIGLU) {
                         a.out[(size_t)row * a.ldo + n0] = silu(y0) * y1;
                     } else {
-                        float* o = a.out + (size_t)row * a.ldo + n0;
+                        float* o = (a.st ? a.st->logits : a.out) + (size_t)row * a.ldo + n0;
                         o[0] = y0;
                         o[1] = y1;
                     }

@@ -10,7 +10,18 @@ enum Epilogue : int {
     EPI_QKV = 0,     // rows of [wq; wk; wv]: RoPE on q and k, q -> q buffer, k/v -> KV cache
     EPI_RESID = 1,   // resid[m][n] += y
     EPI_SWIGLU = 2,  // out[m][n] = silu(x.w1[n]) * (x.w3[n])
-    EPI_STORE = 3    // out[m][n] = y (fp32 logits)
+    EPI_STORE = 3,   // out[m][n] = y (fp32 logits)
+    EPI_STORE_QKV = 4  // plain fp32 store of the [wq; wk; wv] rows (B rows picked as for EPI_QKV)
+};
+
+// Per-call values of a decode step kept in device memory, so one captured graph serves
+// every position: written by a one-thread kernel before the graph is launched.
+struct StepState {
+    int32_t pos;            // start_pos of the step
+    int32_t pad;
+    int64_t ld;             // token row stride
+    const int32_t* tokens;  // token of row b at tokens[b * ld]
+    float* logits;          // [bsz][vocab]
 };
 
 // Row m of a call covers token (b = m / seqlen, position start_pos + m % seqlen).
@@ -23,6 +34,7 @@ struct QkvTarget {
     int head_dim;
     int max_seq;
     int start_pos, seqlen;
+    const StepState* st;   // if set, start_pos comes from st->pos
 };
 
 // y[m][n] = sum_k x[m][k] * W[n][k]  (VALU, fp32 activations, weights streamed once per
@@ -37,6 +49,7 @@ struct GemvArgs {
     float* out; int64_t ldo;
     float* resid; int64_t ldr;
     QkvTarget qkv;
+    const StepState* st;   // if set, the STORE epilogue writes st->logits
 };
 
 // C[m][n] = sum_k A[m][k] * W[n][k] on bf16 MFMA, fp32 accumulate.  A bf16 [M][lda].
@@ -52,6 +65,17 @@ struct GemmArgs {
     float* part;
 };
 
+// y = x W^T for M <= 32 rows on bf16 MFMA (decode with batch > 4); x bf16 [M][ldx].
+struct SkinnyArgs {
+    const void* x; int64_t ldx;
+    int M, K, N;           // N = output rows (SWIGLU: hidden units)
+    const void* w0; const void* w1; const void* w2;
+    float* out; void* out16; int64_t ldo;   // STORE (fp32) / SWIGLU (bf16)
+    float* resid; int64_t ldr;
+    QkvTarget qkv;
+    const StepState* st;   // if set, the STORE epilogue writes st->logits
+};
+
 // Causal attention for a set of query rows against the KV cache (one query position per
 // row, all n_rep heads of one kv head per workgroup, keys split over gridDim.x).
 struct AttnArgs {
@@ -65,8 +89,9 @@ struct AttnArgs {
     int rows, n_heads, n_kv_heads, head_dim, max_seq;
     int row0;              // first row of this launch (launches are split at 65535 rows)
     int start_pos, seqlen; // row t -> b = t / seqlen, position start_pos + t % seqlen
-    int n_split, chunk;    // keys per split (multiple of 16)
+    int n_split, chunk;    // keys per split (multiple of 16); chunk 0: derived from st
     float scale;           // 1/sqrt(head_dim)
+    const StepState* st;   // if set, start_pos comes from st->pos
 };
 
 // Causal GQA attention of a prefill (bf16 MFMA): rows b*seqlen + s at positions start_pos + s.
@@ -81,12 +106,16 @@ struct FlashArgs {
 };
 
 hipError_t launch_flash_prefill(const FlashArgs& a, hipStream_t s);
+hipError_t launch_rope_scatter(const float* y, int T, const QkvTarget& t, hipStream_t s);
 hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, const void* table,
-                        int wbf16, int vocab, int dim, float* h, hipStream_t s);
+                        int wbf16, int vocab, int dim, float* h, const StepState* st, hipStream_t s);
+hipError_t launch_set_step(StepState* st, int pos, int64_t ld, const int32_t* tokens, float* logits,
+                           hipStream_t s);
 hipError_t launch_rmsnorm_bf16(const float* h, int64_t ldh, int rows, int dim, const void* w,
                                float eps, void* out, int64_t ldo, hipStream_t s);
 hipError_t launch_gemv(int wbf16, int epi, const GemvArgs& a, hipStream_t s);
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
+hipError_t launch_skinny(int epi, const SkinnyArgs& a, hipStream_t s);
 hipError_t launch_attn_rows(int kv_bf16, const AttnArgs& a, hipStream_t s);
 hipError_t launch_argmax(const float* logits, int bsz, int vocab, int64_t stride, int32_t* out,
                          hipStream_t s);

@@ -15,7 +15,10 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <cstdlib>
+#include <map>
 #include <new>
+#include <utility>
 #include <vector>
 
 #include "../../include/llama_mi355x.h"
@@ -28,12 +31,14 @@ namespace {
 constexpr int kMaxSplit = 32;
 constexpr int kMaxSplitK = 8;      // K splits of a residual GEMM at small prefill sizes
 constexpr int kSplitKRows = 512;   // prefill rows up to which split-K is considered
+constexpr int kPlainQkvRows = 2048; // above this many prefill rows the QKV GEMM stores plainly
+constexpr int kSkinnyRows = 4;      // bf16 decode batches above this use the skinny MFMA kernel
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t k_cache, v_cache, rope, h32, q32, o32, g32, act16, g16, part, counters, splitk, total;
+    size_t k_cache, v_cache, rope, h32, q32, o32, g32, act16, g16, part, counters, splitk, qkv32, step, total;
     size_t kv_layer_elems;   // elements of one layer's K (or V) cache
 };
 
@@ -89,6 +94,9 @@ Layout layout_of(const llama_args& a) {
     L.counters = take(maxB * (size_t)a.n_kv_heads * sizeof(int));
     // split-K partials of the residual GEMMs, used while a prefill has at most kSplitKRows rows
     L.splitk = fp32 ? off : take((size_t)kMaxSplitK * std::min(maxT, (size_t)kSplitKRows) * a.dim * sizeof(float));
+    // fp32 [wq;wk;wv] projections of long prefills (RoPE and bf16 storage in a second pass)
+    L.qkv32 = (fp32 || maxT <= (size_t)kPlainQkvRows) ? off : take(maxT * (nq + 2 * (size_t)a.n_kv_heads * hd) * sizeof(float));
+    L.step = take(sizeof(StepState));
     L.total = off;
     return L;
 }
@@ -103,6 +111,11 @@ struct llama_ctx {
     char* ws;
     int hd, nq, nk;
     bool bf16;
+
+    // decode graphs: one per (bsz, key splits), captured on a private stream
+    hipStream_t cap_stream = nullptr;
+    std::map<std::pair<int, int>, hipGraphExec_t> graphs;
+    bool use_graphs = true;
 
     // diagnostics: events bracketing launches of one kernel class
     int prof_class = 0;
@@ -150,8 +163,9 @@ void prof_mark(llama_ctx* c, int kc, hipStream_t s) {
 
 namespace {
 
-QkvTarget qkv_target(const llama_ctx* c, int l, int start_pos, int seqlen) {
+QkvTarget qkv_target(const llama_ctx* c, int l, int start_pos, int seqlen, const StepState* st = nullptr) {
     QkvTarget t{};
+    t.st = st;
     t.q = c->at<float>(c->L.q32);
     t.cache_k = c->kcache(l);
     t.cache_v = c->vcache(l);
@@ -166,8 +180,19 @@ QkvTarget qkv_target(const llama_ctx* c, int l, int start_pos, int seqlen) {
 }
 
 // Attention over `rows` query rows (row t = batch t / seqlen, position start_pos + t % seqlen).
+// Key splits of a decode step of `rows` rows at context ctx.
+int decode_splits(const llama_ctx* c, int rows, int ctx) {
+    const int n_rep = c->a.n_heads / c->a.n_kv_heads;
+    const int slots = 4 * (n_rep <= 2 ? 16 : 8);
+    const int pairs = rows * c->a.n_kv_heads;
+    const int want = (512 + pairs - 1) / pairs;
+    const int by_len = (ctx + 4 * slots - 1) / (4 * slots);
+    return std::max(1, std::min(kMaxSplit, std::min(want, by_len)));
+}
+
 llama_status run_attention(const llama_ctx* c, int l, int rows, int seqlen, int start_pos,
-                           void* out, bool out_bf16, bool allow_split, hipStream_t s) {
+                           void* out, bool out_bf16, bool allow_split, hipStream_t s,
+                           const StepState* st = nullptr, int graph_splits = 0) {
     AttnArgs at{};
     at.q = c->at<const float>(c->L.q32);
     at.cache_k = c->kcache(l);
@@ -184,30 +209,30 @@ llama_status run_attention(const llama_ctx* c, int l, int rows, int seqlen, int 
     at.start_pos = start_pos;
     at.seqlen = seqlen;
     at.scale = 1.0f / std::sqrt((float)c->hd);
-    const int ctx = start_pos + seqlen;   // longest visible prefix among the rows
-    int n_split = 1;
-    if (allow_split) {
+    at.st = st;
+    if (st) {
+        // graph replay: split count fixed at capture, keys per split derived in the kernel
+        at.n_split = graph_splits;
+        at.chunk = 0;
+    } else {
         // split the keys only when there are too few (row, kv head) pairs to fill the chip,
         // and never below one round of loads per workgroup (slots x 4 keys)
-        const int n_rep = c->a.n_heads / c->a.n_kv_heads;
-        const int slots = 4 * (n_rep <= 2 ? 16 : 8);
-        const int pairs = rows * c->a.n_kv_heads;
-        const int want = (512 + pairs - 1) / pairs;
-        const int by_len = (ctx + 4 * slots - 1) / (4 * slots);
-        n_split = std::max(1, std::min(kMaxSplit, std::min(want, by_len)));
+        const int ctx = start_pos + seqlen;   // longest visible prefix among the rows
+        int n_split = allow_split ? decode_splits(c, rows, ctx) : 1;
+        int chunk = (ctx + n_split - 1) / n_split;
+        chunk = (chunk + 15) / 16 * 16;
+        n_split = (ctx + chunk - 1) / chunk;
+        at.n_split = n_split;
+        at.chunk = chunk;
     }
-    int chunk = (ctx + n_split - 1) / n_split;
-    chunk = (chunk + 15) / 16 * 16;
-    n_split = (ctx + chunk - 1) / chunk;
-    at.n_split = n_split;
-    at.chunk = chunk;
     LAUNCH(c, seqlen == 1 ? LLAMA_KC_ATTN_DECODE : LLAMA_KC_ATTN_PREFILL, s, launch_attn_rows(c->bf16 ? 1 : 0, at, s));
     return LLAMA_OK;
 }
 
 // One transformer block on the GEMV (VALU) path for M activation rows.
 llama_status block_gemv(const llama_ctx* c, int l, int M, int seqlen, int start_pos,
-                        bool allow_split, hipStream_t s) {
+                        bool allow_split, hipStream_t s, const StepState* st = nullptr,
+                        int graph_splits = 0) {
     const llama_layer_weights& W = c->layers[l];
     const int D = c->a.dim, F = c->a.hidden_dim;
     float* h = c->at<float>(c->L.h32);
@@ -219,11 +244,12 @@ llama_status block_gemv(const llama_ctx* c, int l, int M, int seqlen, int start_
     g.x = h; g.ldx = D; g.M = M; g.K = D; g.N = c->nq + 2 * c->nk;
     g.norm_w = W.attention_norm; g.eps = c->a.norm_eps;
     g.w0 = W.wq; g.w1 = W.wk; g.w2 = W.wv;
-    g.qkv = qkv_target(c, l, start_pos, seqlen);
+    g.qkv = qkv_target(c, l, start_pos, seqlen, st);
     LAUNCH(c, LLAMA_KC_GEMV_QKV, s, launch_gemv(wb, EPI_QKV, g, s));
 
-    llama_status st = run_attention(c, l, M, seqlen, start_pos, o32, false, allow_split, s);
-    if (st != LLAMA_OK) return st;
+    const llama_status ast = run_attention(c, l, M, seqlen, start_pos, o32, false, allow_split, s,
+                                           st, graph_splits);
+    if (ast != LLAMA_OK) return ast;
 
     g = GemvArgs{};
     g.x = o32; g.ldx = c->nq; g.M = M; g.K = c->nq; g.N = D;
@@ -254,6 +280,44 @@ int residual_splits(const llama_ctx* c, int T, int K) {
     return std::max(1, std::min(sp, kMaxSplitK));
 }
 
+// One decode block for a bf16 model at batch > kSkinnyRows: projections on the skinny MFMA
+// kernel from bf16 operands (RMSNorm to bf16 first), attention writing bf16.
+llama_status block_skinny(const llama_ctx* c, int l, int M, int start_pos, hipStream_t s,
+                          const StepState* st, int graph_splits) {
+    const llama_layer_weights& W = c->layers[l];
+    const int D = c->a.dim, F = c->a.hidden_dim;
+    float* h = c->at<float>(c->L.h32);
+    void* act = c->at<void>(c->L.act16);
+    void* g16 = c->at<void>(c->L.g16);
+
+    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, M, D, W.attention_norm, c->a.norm_eps, act, D, s));
+    SkinnyArgs k{};
+    k.x = act; k.ldx = D; k.M = M; k.K = D; k.N = c->nq + 2 * c->nk;
+    k.w0 = W.wq; k.w1 = W.wk; k.w2 = W.wv;
+    k.qkv = qkv_target(c, l, start_pos, 1, st);
+    LAUNCH(c, LLAMA_KC_GEMV_QKV, s, launch_skinny(EPI_QKV, k, s));
+
+    const llama_status ast = run_attention(c, l, M, 1, start_pos, act, true, true, s, st, graph_splits);
+    if (ast != LLAMA_OK) return ast;
+
+    k = SkinnyArgs{};
+    k.x = act; k.ldx = c->nq; k.M = M; k.K = c->nq; k.N = D;
+    k.w0 = W.wo; k.resid = h; k.ldr = D;
+    LAUNCH(c, LLAMA_KC_GEMV_WO, s, launch_skinny(EPI_RESID, k, s));
+
+    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, M, D, W.ffn_norm, c->a.norm_eps, act, D, s));
+    k = SkinnyArgs{};
+    k.x = act; k.ldx = D; k.M = M; k.K = D; k.N = F;
+    k.w0 = W.w1; k.w1 = W.w3; k.out16 = g16; k.ldo = F;
+    LAUNCH(c, LLAMA_KC_GEMV_W13, s, launch_skinny(EPI_SWIGLU, k, s));
+
+    k = SkinnyArgs{};
+    k.x = g16; k.ldx = F; k.M = M; k.K = F; k.N = D;
+    k.w0 = W.w2; k.resid = h; k.ldr = D;
+    LAUNCH(c, LLAMA_KC_GEMV_W2, s, launch_skinny(EPI_RESID, k, s));
+    return LLAMA_OK;
+}
+
 // One transformer block on the bf16 MFMA path for T = bsz*seqlen prefill rows.
 llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_pos, hipStream_t s) {
     const llama_layer_weights& W = c->layers[l];
@@ -267,10 +331,34 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
     g.a = act; g.lda = D; g.M = T; g.K = D; g.N = c->nq + 2 * c->nk;
     g.w0 = W.wq; g.w1 = W.wk; g.w2 = W.wv;
     g.qkv = qkv_target(c, l, start_pos, seqlen);
-    LAUNCH(c, LLAMA_KC_GEMM_QKV, s, launch_gemm(EPI_QKV, g, s));
+    if (T > kPlainQkvRows) {
+        // large tiles with a plain fp32 store, then RoPE + bf16 storage in a light pass
+        g.out = c->at<float>(c->L.qkv32); g.ldo = g.N;
+        LAUNCH(c, LLAMA_KC_GEMM_QKV, s, launch_gemm(EPI_STORE_QKV, g, s));
+        LAUNCH(c, LLAMA_KC_GEMM_QKV, s, launch_rope_scatter(g.out, T, g.qkv, s));
+    } else {
+        LAUNCH(c, LLAMA_KC_GEMM_QKV, s, launch_gemm(EPI_QKV, g, s));
+    }
 
-    llama_status st = run_attention(c, l, T, seqlen, start_pos, act, true, false, s);
-    if (st != LLAMA_OK) return st;
+    if (c->hd == 64 || c->hd == 128) {
+        FlashArgs fa{};
+        fa.q = c->at<const float>(c->L.q32);
+        fa.cache_k = c->kcache(l);
+        fa.cache_v = c->vcache(l);
+        fa.out = act;
+        fa.bsz = T / seqlen;
+        fa.seqlen = seqlen;
+        fa.start_pos = start_pos;
+        fa.n_heads = c->a.n_heads;
+        fa.n_kv_heads = c->a.n_kv_heads;
+        fa.head_dim = c->hd;
+        fa.max_seq = c->a.max_seq_len;
+        fa.scale = 1.0f / std::sqrt((float)c->hd);
+        LAUNCH(c, LLAMA_KC_ATTN_PREFILL, s, launch_flash_prefill(fa, s));
+    } else {
+        llama_status st = run_attention(c, l, T, seqlen, start_pos, act, true, false, s);
+        if (st != LLAMA_OK) return st;
+    }
 
     g = GemmArgs{};
     g.a = act; g.lda = c->nq; g.M = T; g.K = c->nq; g.N = D;
@@ -294,8 +382,9 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
 
 // Final RMSNorm + output projection for `rows` rows of h spaced `ldx` floats apart.
 llama_status final_logits(const llama_ctx* c, const float* x, int64_t ldx, int rows, float* logits,
-                          hipStream_t s) {
+                          hipStream_t s, const StepState* st = nullptr) {
     GemvArgs g{};
+    g.st = st;
     g.x = x; g.ldx = ldx; g.M = rows; g.K = c->a.dim; g.N = c->a.vocab_size;
     g.norm_w = c->w.norm; g.eps = c->a.norm_eps;
     g.w0 = c->w.output; g.out = logits; g.ldo = c->a.vocab_size;
@@ -343,6 +432,10 @@ llama_status llama_init(const llama_args* a, const llama_weights* w, void* d_wor
     c->nq = a->n_heads * c->hd;
     c->nk = a->n_kv_heads * c->hd;
     c->bf16 = a->dtype == LLAMA_BF16;
+    {
+        const char* g = std::getenv("LLAMA_MI355X_GRAPHS");
+        c->use_graphs = !(g && g[0] == '0');
+    }
 
     // RoPE table: entry (t, i) = (cos, sin) of t * theta^(-2i/hd), computed in float64.
     const int half = c->hd / 2;
@@ -377,7 +470,7 @@ llama_status llama_prefill(llama_ctx* c, const int32_t* d_tokens, int64_t ld_tok
     const int T = bsz * seqlen;
     float* h = c->at<float>(c->L.h32);
     HIP_TRY(launch_embed(d_tokens, ld_tokens, bsz, seqlen, c->w.tok_embeddings, c->bf16 ? 1 : 0,
-                         c->a.vocab_size, D, h, s));
+                         c->a.vocab_size, D, h, nullptr, s));
     for (int l = 0; l < c->a.n_layers; ++l) {
         const llama_status st = c->bf16 ? block_mfma(c, l, T, seqlen, start_pos, s)
                                         : block_gemv(c, l, T, seqlen, start_pos, false, s);
@@ -394,6 +487,60 @@ llama_status llama_prefill(llama_ctx* c, const int32_t* d_tokens, int64_t ld_tok
     return LLAMA_OK;
 }
 
+// The launch sequence of one decode step.  With st, per-step values are read from the
+// device step state (graph capture); otherwise they are launch arguments.
+static llama_status decode_plan(llama_ctx* c, const int32_t* d_tokens, int64_t ld_tokens, int32_t bsz,
+                                int32_t start_pos, float* d_logits, hipStream_t s,
+                                const StepState* st, int graph_splits) {
+    const int D = c->a.dim;
+    float* h = c->at<float>(c->L.h32);
+    HIP_TRY(launch_embed(d_tokens, ld_tokens, bsz, 1, c->w.tok_embeddings, c->bf16 ? 1 : 0,
+                         c->a.vocab_size, D, h, st, s));
+    const bool skinny = c->bf16 && bsz > kSkinnyRows;
+    for (int l = 0; l < c->a.n_layers; ++l) {
+        const llama_status r = skinny ? block_skinny(c, l, bsz, start_pos, s, st, graph_splits)
+                                      : block_gemv(c, l, bsz, 1, start_pos, true, s, st, graph_splits);
+        if (r != LLAMA_OK) return r;
+    }
+    if (!skinny) return final_logits(c, h, D, bsz, d_logits, s, st);
+    void* act = c->at<void>(c->L.act16);
+    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, bsz, D, c->w.norm, c->a.norm_eps, act, D, s));
+    SkinnyArgs k{};
+    k.x = act; k.ldx = D; k.M = bsz; k.K = D; k.N = c->a.vocab_size;
+    k.w0 = c->w.output; k.out = d_logits; k.ldo = c->a.vocab_size; k.st = st;
+    LAUNCH(c, LLAMA_KC_GEMV_OUT, s, launch_skinny(EPI_STORE, k, s));
+    return LLAMA_OK;
+}
+
+// Captured graph of a decode step for (bsz, key splits), instantiated on first use.
+static llama_status decode_graph(llama_ctx* c, int bsz, int splits, hipGraphExec_t* out) {
+    const auto key = std::make_pair(bsz, splits);
+    const auto it = c->graphs.find(key);
+    if (it != c->graphs.end()) {
+        *out = it->second;
+        return LLAMA_OK;
+    }
+    if (!c->cap_stream && hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking) != hipSuccess)
+        return LLAMA_ERR_HIP;
+    const StepState* st = c->at<const StepState>(c->L.step);
+    if (hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal) != hipSuccess)
+        return LLAMA_ERR_HIP;
+    const llama_status r = decode_plan(c, nullptr, 0, bsz, 0, nullptr, c->cap_stream, st, splits);
+    hipGraph_t graph = nullptr;
+    const hipError_t e = hipStreamEndCapture(c->cap_stream, &graph);
+    if (r != LLAMA_OK || e != hipSuccess) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return r != LLAMA_OK ? r : LLAMA_ERR_HIP;
+    }
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ie = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ie != hipSuccess) return LLAMA_ERR_HIP;
+    c->graphs[key] = exec;
+    *out = exec;
+    return LLAMA_OK;
+}
+
 llama_status llama_decode_step(llama_ctx* c, const int32_t* d_tokens, int64_t ld_tokens,
                                int32_t bsz, int32_t start_pos, float* d_logits, void* stream) {
     if (!c || !d_tokens || !d_logits) return LLAMA_ERR_INVALID_ARG;
@@ -401,15 +548,16 @@ llama_status llama_decode_step(llama_ctx* c, const int32_t* d_tokens, int64_t ld
         ld_tokens < 1)
         return LLAMA_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int D = c->a.dim;
-    float* h = c->at<float>(c->L.h32);
-    HIP_TRY(launch_embed(d_tokens, ld_tokens, bsz, 1, c->w.tok_embeddings, c->bf16 ? 1 : 0,
-                         c->a.vocab_size, D, h, s));
-    for (int l = 0; l < c->a.n_layers; ++l) {
-        const llama_status st = block_gemv(c, l, bsz, 1, start_pos, true, s);
-        if (st != LLAMA_OK) return st;
-    }
-    return final_logits(c, h, D, bsz, d_logits, s);
+    if (!c->use_graphs || c->prof_class != 0)
+        return decode_plan(c, d_tokens, ld_tokens, bsz, start_pos, d_logits, s, nullptr, 0);
+    // graph replay: per-step values go to the device step state, then one graph launch
+    const int splits = decode_splits(c, bsz, start_pos + 1);
+    hipGraphExec_t exec;
+    const llama_status r = decode_graph(c, bsz, splits, &exec);
+    if (r != LLAMA_OK) return r;
+    HIP_TRY(launch_set_step(c->at<StepState>(c->L.step), start_pos, ld_tokens, d_tokens, d_logits, s));
+    HIP_TRY(hipGraphLaunch(exec, s));
+    return LLAMA_OK;
 }
 
 llama_status llama_argmax(const float* d_logits, int32_t bsz, int32_t vocab, int64_t row_stride,
@@ -459,6 +607,8 @@ llama_status llama_profile_read(llama_ctx* c, int64_t* launches, double* total_m
 void llama_destroy(llama_ctx* c) {
     if (!c) return;
     for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
+    for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
+    if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
     delete c;
 }
 

@@ -9,7 +9,12 @@ namespace {
 // h[b*seqlen + s][:] = E[tokens[b*ld + s]][:] as fp32 (the residual stream is fp32).
 template <typename WT>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* tokens, int64_t ld, int seqlen,
-                                                    const WT* table, int vocab, int dim, float* h) {
+                                                    const WT* table, int vocab, int dim, float* h,
+                                                    const StepState* st) {
+    if (st) {
+        tokens = st->tokens;
+        ld = st->ld;
+    }
     const int t = blockIdx.x;
     const int b = t / seqlen, s = t - b * seqlen;
     int tok = tokens[(size_t)b * ld + s];
@@ -96,23 +101,73 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* logits, int v
     }
 }
 
+__global__ void set_step_kernel(StepState* st, int pos, int64_t ld, const int32_t* tokens,
+                                float* logits) {
+    st->pos = pos;
+    st->pad = 0;
+    st->ld = ld;
+    st->tokens = tokens;
+    st->logits = logits;
+}
+
 __global__ void select_kernel(const int32_t* next, int32_t* tokens, int64_t ld, int cur_pos,
                               const int32_t* prompt_len, int bsz) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b < bsz && cur_pos >= prompt_len[b]) tokens[(size_t)b * ld + cur_pos] = next[b];
 }
 
+// RoPE + bf16 storage of q and the K/V cache append from fp32 projections y [T][nq+2nk]
+// (used when the [wq;wk;wv] GEMM stores plainly).  One thread per (row, pair).
+__global__ void rope_scatter_kernel(const float* y, int T, QkvTarget t) {
+    const int npairs = (t.nq + 2 * t.nk) / 2;
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)T * npairs) return;
+    const int m = (int)(i / npairs);
+    const int n0 = 2 * (int)(i - (size_t)m * npairs);
+    const float2 v = *reinterpret_cast<const float2*>(y + (size_t)m * (t.nq + 2 * t.nk) + n0);
+    float y0 = v.x, y1 = v.y;
+    const int b = m / t.seqlen;
+    const int pos = t.start_pos + (m - b * t.seqlen);
+    if (n0 < t.nq + t.nk) {
+        const float2 cs = t.rope[(size_t)pos * (t.head_dim / 2) + (n0 % t.head_dim) / 2];
+        const float r0 = y0 * cs.x - y1 * cs.y;
+        const float r1 = y0 * cs.y + y1 * cs.x;
+        y0 = r0;
+        y1 = r1;
+    }
+    if (n0 < t.nq) {
+        *reinterpret_cast<float2*>(t.q + (size_t)m * t.nq + n0) = make_float2(round_bf16(y0), round_bf16(y1));
+        return;
+    }
+    const bool is_k = n0 < t.nq + t.nk;
+    const int c = is_k ? n0 - t.nq : n0 - t.nq - t.nk;
+    uint16_t* cache = static_cast<uint16_t*>(is_k ? t.cache_k : t.cache_v);
+    *reinterpret_cast<uint32_t*>(cache + ((size_t)b * t.max_seq + pos) * (size_t)t.nk + c) = pack_bf16x2(y0, y1);
+}
+
 }  // namespace
 
+hipError_t launch_rope_scatter(const float* y, int T, const QkvTarget& t, hipStream_t s) {
+    const size_t n = (size_t)T * ((t.nq + 2 * t.nk) / 2);
+    hipLaunchKernelGGL(rope_scatter_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, T, t);
+    return hipGetLastError();
+}
+
 hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, const void* table,
-                        int wbf16, int vocab, int dim, float* h, hipStream_t s) {
+                        int wbf16, int vocab, int dim, float* h, const StepState* st, hipStream_t s) {
     const dim3 grid(bsz * seqlen), block(256);
     if (wbf16)
         hipLaunchKernelGGL(embed_kernel<bf16>, grid, block, 0, s, tokens, ld, seqlen,
-                           static_cast<const bf16*>(table), vocab, dim, h);
+                           static_cast<const bf16*>(table), vocab, dim, h, st);
     else
         hipLaunchKernelGGL(embed_kernel<float>, grid, block, 0, s, tokens, ld, seqlen,
-                           static_cast<const float*>(table), vocab, dim, h);
+                           static_cast<const float*>(table), vocab, dim, h, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_step(StepState* st, int pos, int64_t ld, const int32_t* tokens, float* logits,
+                           hipStream_t s) {
+    hipLaunchKernelGGL(set_step_kernel, dim3(1), dim3(1), 0, s, st, pos, ld, tokens, logits);
     return hipGetLastError();
 }
 

@@ -71,9 +71,11 @@ def gpu_generate(wl, weights, prompts, keep_logits=True):
     return out
 
 
-def verify_generate(wl, prompts, tokens, call_logits, tf_logits, tol, cos_min=None):
-    """call i of the generate schedule produced logits of position min_len-1+i."""
-    min_len = min(len(p) for p in prompts)
+def verify_generate(wl, prompts, tokens, call_logits, tf_logits, tol, cos_min=None, min_len=None):
+    """call i of the generate schedule produced logits of position min_len-1+i (min_len: the
+    shortest prompt of the whole batch)."""
+    if min_len is None:
+        min_len = min(len(p) for p in prompts)
     worst = 0.0
     worst_cos = 1.0
     checked = 0
@@ -188,6 +190,12 @@ SMALL_BF16 = {
                                                n_kv_heads=4, dim=512, hidden_dim=1536, vocab_size=1000,
                                                batch=4, prompt_len=17, gen_steps=20, weight_seed=13,
                                                prompt_seed=113),
+    # long prompts: 4 x 600 = 2400 prefill rows take the large-M GEMM path (ragged tiles)
+    # and the plain-store QKV projection followed by the RoPE / bf16-storage pass
+    "long": synth.WORKLOADS["tiny_fp32"].with_(name="small_bf16_long", dtype="bf16", n_heads=4,
+                                               n_kv_heads=4, dim=512, hidden_dim=1536, vocab_size=1024,
+                                               batch=4, prompt_len=600, gen_steps=6, weight_seed=14,
+                                               prompt_seed=114, max_seq_len=640),
 }
 
 
@@ -253,6 +261,31 @@ def test_small_bf16_chunked_prefill_all_positions(name):
     say(f"  max|dlogit|={d:.3e} min cos={cos:.6f}")
     assert d <= BF16_TOL and cos >= COS_MIN
     model.close()
+
+
+@pytest.mark.parametrize("name", ["gqa8", "mha"])
+def test_decode_graph_replays_match_eager_launches(name):
+    """Decode steps replay one captured graph per split count; the generate loop puts eager
+    work (argmax, select, step-state writes) between replays.  Every replay's logits must
+    equal the eagerly launched step bit for bit (same kernels, same arithmetic)."""
+    wl = SMALL_BF16[name]
+    say(f"case {wl.name}: graph replays vs eager launches")
+    W = synth.gen_weights(wl, device="cuda")
+    prompts = synth.prompts(wl)
+    old = os.environ.get("LLAMA_MI355X_GRAPHS")
+    try:
+        os.environ["LLAMA_MI355X_GRAPHS"] = "0"
+        t_eager, l_eager, _ = gpu_generate(wl, W, prompts)
+        os.environ["LLAMA_MI355X_GRAPHS"] = "1"
+        t_graph, l_graph, _ = gpu_generate(wl, W, prompts)
+    finally:
+        if old is None:
+            os.environ.pop("LLAMA_MI355X_GRAPHS", None)
+        else:
+            os.environ["LLAMA_MI355X_GRAPHS"] = old
+    assert np.array_equal(t_eager, t_graph)
+    assert np.array_equal(l_eager, l_graph), np.abs(l_eager - l_graph).max()
+    say(f"  {l_graph.shape[0] - 1} graph replays identical to eager launches")
 
 
 def test_generator_bit_identical_on_gpu_and_cpu():
@@ -355,3 +388,89 @@ def test_llama2_7b_b1_generate_matches_oracle():
     plain = oracle.teacher_forced_logits(oracle.args_from_workload(wl), host_weights(wl, W),
                                          tokens[:, :-1], np.float32)
     plain_distance(logits, plain, len(prompts[0]))
+
+
+# ----------------------------------------------------------------------------- other workloads
+#
+# The oracle's cost grows with batch x depth x length, so the larger workloads are checked
+# on sampled rows: the GPU runs the whole batch (the launch configuration of a real
+# generate), the oracle follows selected rows teacher-forced.  Where depth makes even one
+# row too slow, the model is cut to its first layers at full width (same kernels, same
+# shapes) and the full-depth run is checked on a causal prefix.  The spread bar uses a
+# second, equivalent evaluation: permuting the model dimension consistently across all
+# weights leaves the function unchanged but changes every fp32 summation order.
+
+def permuted_provider(base, dim, hidden, seed=7):
+    rng = np.random.default_rng(seed)
+    pd, ph = rng.permutation(dim), rng.permutation(hidden)
+
+    def get(name, layer):
+        w = base(name, layer)
+        if name in ("tok_embeddings", "output", "wq", "wk", "wv"):
+            return np.ascontiguousarray(w[:, pd])
+        if name in ("norm", "attention_norm", "ffn_norm"):
+            return np.ascontiguousarray(w[pd])
+        if name in ("wo",):
+            return np.ascontiguousarray(w[pd, :])
+        if name in ("w1", "w3"):
+            return np.ascontiguousarray(w[ph][:, pd])
+        if name == "w2":
+            return np.ascontiguousarray(w[pd][:, ph])
+        return w
+    return get
+
+
+def cached_provider(W):
+    cache = {}
+
+    def get(name, layer):
+        if (name, layer) not in cache:
+            if layer >= 0:
+                for k in [k for k in cache if k[1] >= 0 and k[1] != layer]:
+                    del cache[k]
+            t = W[name] if layer < 0 else W["layers"][layer][name]
+            cache[(name, layer)] = t.float().cpu().numpy()
+        return cache[(name, layer)]
+    return get
+
+
+def check_rows(wl, W, prompts, tokens, call_logits, rows):
+    """Teacher-forced oracle (bf16 storage) on the selected rows; bar from the permuted
+    evaluation's spread."""
+    a = oracle.args_from_workload(wl)
+    base = cached_provider(W)
+    min_len = min(len(p) for p in prompts)
+    for b in rows:
+        tb = tokens[b:b + 1, :-1]
+        t1 = oracle.teacher_forced_logits(a, base, tb, np.float32, storage="bf16")[0]
+        t2 = oracle.teacher_forced_logits(a, permuted_provider(base, wl.dim, wl.hidden_dim), tb,
+                                          np.float32, storage="bf16")[0]
+        sel = np.arange(min_len - 1, min_len - 1 + call_logits.shape[0])
+        spread = float(np.abs(t1[sel] - t2[sel]).max())
+        tol = max(BF16_TOL, 1.5 * spread)
+        say(f"  row {b}: oracle permuted-evaluation spread {spread:.4f} -> bar {tol:.4f}")
+        verify_generate(wl, [prompts[b]], tokens[b:b + 1], call_logits[:, b:b + 1],
+                        t1[None], tol, COS_MIN, min_len=min_len)
+
+
+@pytest.mark.timeout(900)
+def test_llama2_7b_b32_ragged_generate_rows_match_oracle():
+    wl = synth.WORKLOADS["llama2_7b_b32_ragged"]
+    say(f"case {wl.name}: full batch, ragged prompts, full depth; oracle on row 0")
+    W = synth.gen_weights(wl, device="cuda")
+    prompts = synth.prompts(wl)
+    tokens, logits, _ = gpu_generate(wl, W, prompts)
+    assert np.isfinite(logits).all()
+    check_rows(wl, W, prompts, tokens, logits, rows=[0])
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["llama2_13b_b16", "llama2_70b_b8"])
+def test_full_width_first_layers_generate_rows_match_oracle(name):
+    wl = synth.WORKLOADS[name].with_(n_layers=2)
+    say(f"case {wl.name} cut to 2 layers: full batch {wl.batch} x {wl.prompt_len}, {wl.gen_steps} steps")
+    W = synth.gen_weights(wl, device="cuda")
+    prompts = synth.prompts(wl)
+    tokens, logits, _ = gpu_generate(wl, W, prompts)
+    assert np.isfinite(logits).all()
+    check_rows(wl, W, prompts, tokens, logits, rows=[0])
