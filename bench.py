@@ -11,7 +11,7 @@ prefill tokens/s (batch * prompt_len / prefill time) is reported beside it.  `ro
 the dominant decode kernel (the fused RMSNorm + [w1;w3] + SiLU-gate GEMV, 44.6% of the
 bytes a 7B decode step streams): algorithmic bytes per launch over its average launch
 duration, timed live with HIP events on the launch stream.  `cpu_baseline` is the NumPy
-oracle on this host's cores over a bounded sample (2 of the layers, scaled to all).
+oracle on this host's cores over a bounded sample (the whole model, the first decode calls).
 """
 from __future__ import annotations
 
@@ -56,11 +56,11 @@ def w13_launch_bytes(wl) -> float:
     return 2 * wl.hidden_dim * wl.dim * e + wl.dim * e + wl.batch * wl.dim * 4 + wl.batch * wl.hidden_dim * 4
 
 
-def cpu_baseline(wl, dev_weights, prompts, sample_layers: int = 2, decode_steps: int = 4) -> dict:
-    """The oracle as it stands, on this host, over a bounded sample: the first
-    `sample_layers` layers over the full prompt (prefill) and `decode_steps` incremental
-    steps, plus the head (final norm + vocab projection) timed alone; layer time is scaled
-    to all layers."""
+def cpu_baseline(wl, dev_weights, prompts, decode_steps: int = 48) -> dict:
+    """The oracle as it stands, on this host, over a bounded sample of the same workload:
+    the whole model (every layer and the head) in fp32 NumPy, prefill of the prompt batch
+    and then the first `decode_steps` single-token decode calls.  Nothing is scaled."""
+    import dataclasses
     import numpy as np
     import oracle
     try:
@@ -69,44 +69,32 @@ def cpu_baseline(wl, dev_weights, prompts, sample_layers: int = 2, decode_steps:
     except Exception:
         threads = os.cpu_count()
 
-    def hostw(name, layer):
-        t = dev_weights[name] if layer < 0 else dev_weights["layers"][layer][name]
-        return t.float().cpu().numpy()
     cache = {}
 
     def provider(name, layer):
         k = (name, layer)
         if k not in cache:
-            cache[k] = hostw(name, layer)
+            t = dev_weights[name] if layer < 0 else dev_weights["layers"][layer][name]
+            cache[k] = t.float().cpu().numpy()
         return cache[k]
     tok = np.array([p[:min(len(x) for x in prompts)] for p in prompts])
     B, S = tok.shape
-    base = oracle.args_from_workload(wl)
-    import dataclasses
-
-    def timed(n_layers):
-        a = dataclasses.replace(base, n_layers=n_layers, max_seq_len=S + decode_steps + 1)
-        m = oracle.Oracle(a, provider, B, np.float32)
-        t0 = time.perf_counter()
-        m.forward(tok, 0)
-        t1 = time.perf_counter()
-        nxt = tok[:, -1:]
-        for j in range(decode_steps):
-            m.forward(nxt, S + j)
-        t2 = time.perf_counter()
-        return t1 - t0, (t2 - t1) / decode_steps
-    timed(0)                                # warm the weight cache / BLAS
-    timed(sample_layers)
-    head_p, head_d = timed(0)
-    lay_p, lay_d = timed(sample_layers)
-    scale = wl.n_layers / sample_layers
-    t_prefill = head_p + (lay_p - head_p) * scale
-    t_decode = head_d + (lay_d - head_d) * scale
-    return {"value": B / t_decode, "unit": "tok/s", "cores": threads, "kind": "oracle",
-            "prefill_tok_per_s": B * S / t_prefill,
-            "sample": (f"{wl.name}: oracle fp32 NumPy, {sample_layers} of {wl.n_layers} layers over the "
-                       f"{S}-token prefill and {decode_steps} decode steps, head timed alone, layer time "
-                       f"scaled x{scale:g}; host cpu_count={os.cpu_count()}")}
+    a = dataclasses.replace(oracle.args_from_workload(wl), max_seq_len=S + decode_steps + 1)
+    m = oracle.Oracle(a, provider, B, np.float32)
+    m.forward(tok[:, :1], 0)                # first touch: weights to host fp32, BLAS warm-up
+    t0 = time.perf_counter()
+    logits = m.forward(tok, 0)
+    t1 = time.perf_counter()
+    nxt = oracle.argmax_lowest(logits[:, -1]).reshape(B, 1)
+    for j in range(decode_steps):
+        logits = m.forward(nxt, S + j)
+        nxt = oracle.argmax_lowest(logits[:, -1]).reshape(B, 1)
+    t2 = time.perf_counter()
+    return {"value": B * decode_steps / (t2 - t1), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "prefill_tok_per_s": B * S / (t1 - t0),
+            "sample": (f"{wl.name}: oracle fp32 NumPy, all {wl.n_layers} layers and the head, "
+                       f"{S}-token prefill of {B} row(s) then {decode_steps} greedy decode calls "
+                       f"({t2 - t0:.1f} s timed); host cpu_count={os.cpu_count()}")}
 
 
 def main() -> int:
@@ -117,6 +105,8 @@ def main() -> int:
     ap.add_argument("--workload", default="llama2_7b_b1")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--profile-class", default="gemv_w13")
+    ap.add_argument("--gen-steps", type=int, default=0,
+                    help="cap on generated positions per step (profiler runs only; 0 = the workload's)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -141,7 +131,8 @@ def main() -> int:
     model = runtime.LlamaModel(runtime.make_args(
         wl.dim, wl.n_layers, wl.n_heads, wl.n_kv_heads, wl.vocab_size, wl.hidden_dim,
         wl.norm_eps, wl.rope_theta, wl.batch, wl.max_seq_len, wl.dtype), W)
-    run = runtime.GreedyRun(model, prompts, wl.gen_steps, keep_logits=False)
+    gen_steps = min(wl.gen_steps, args.gen_steps) if args.gen_steps > 0 else wl.gen_steps
+    run = runtime.GreedyRun(model, prompts, gen_steps, keep_logits=False)
     B, S, n_dec = run.bsz, run.min_len, run.n_calls - 1
 
     def one_step(ev=None):

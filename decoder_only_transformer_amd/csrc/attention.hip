@@ -258,10 +258,10 @@ hipError_t launch4(const AttnArgs& args, hipStream_t s) {
         const int n = min(kMaxZ, args.rows - r0);
         const dim3 grid(a.n_split, a.n_kv_heads, n);
         if (a.seqlen == 1)
-            hipLaunchKernelGGL((attn_rows_kernel<KT, HD, NREP, OB, kDecodeWaves<NREP>>), grid,
+            launch_kernel((attn_rows_kernel<KT, HD, NREP, OB, kDecodeWaves<NREP>>), grid,
                                dim3(64 * kDecodeWaves<NREP>), 0, s, a);
         else
-            hipLaunchKernelGGL((attn_rows_kernel<KT, HD, NREP, OB, 4>), grid, dim3(256), 0, s, a);
+            launch_kernel((attn_rows_kernel<KT, HD, NREP, OB, 4>), grid, dim3(256), 0, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

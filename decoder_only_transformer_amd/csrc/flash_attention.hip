@@ -186,9 +186,9 @@ hipError_t launch_flash_prefill(const FlashArgs& a, hipStream_t s) {
     const int n_rep = a.n_heads / a.n_kv_heads;
     const dim3 grid((a.seqlen * n_rep + kRows - 1) / kRows, a.n_kv_heads, a.bsz);
     if (a.head_dim == 128)
-        hipLaunchKernelGGL(flash_prefill_kernel<128>, grid, dim3(256), 0, s, a);
+        launch_kernel(flash_prefill_kernel<128>, grid, dim3(256), 0, s, a);
     else if (a.head_dim == 64)
-        hipLaunchKernelGGL(flash_prefill_kernel<64>, grid, dim3(256), 0, s, a);
+        launch_kernel(flash_prefill_kernel<64>, grid, dim3(256), 0, s, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

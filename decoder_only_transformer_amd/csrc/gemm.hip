@@ -251,11 +251,11 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     const int n_tn = (a.N + ncols - 1) / ncols, n_tm = (a.M + BM - 1) / BM;
     const int per_xcd = (n_tn * n_tm + kXcds - 1) / kXcds;
     const dim3 grid(per_xcd * kXcds, 1, splits);
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WGM, WGN, EPI>), grid, dim3(64 * WGM * WGN), 0, s, a, n_tm, n_tn);
+    launch_kernel((gemm_kernel<BM, BN, WGM, WGN, EPI>), grid, dim3(64 * WGM * WGN), 0, s, a, n_tm, n_tn);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     const size_t n = (size_t)a.M * a.N;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+    launch_kernel(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        a.part, splits, a.M, a.N, a.resid, a.ldr);
     return hipGetLastError();
 }
@@ -423,12 +423,12 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
     const int splits = (EPI == EPI_RESID && a.part) ? std::max(1, a.splits) : 1;
     const int n_tn = (a.N + ncols - 1) / ncols, n_tm = (a.M + kBigBM - 1) / kBigBM;
     const int per_xcd = (n_tn * n_tm + kXcds - 1) / kXcds;
-    hipLaunchKernelGGL((gemm_big_kernel<EPI>), dim3(per_xcd * kXcds, 1, splits), dim3(512), 0, s, a,
+    launch_kernel((gemm_big_kernel<EPI>), dim3(per_xcd * kXcds, 1, splits), dim3(512), 0, s, a,
                        n_tm, n_tn);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     const size_t n = (size_t)a.M * a.N;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+    launch_kernel(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        a.part, splits, a.M, a.N, a.resid, a.ldr);
     return hipGetLastError();
 }

@@ -294,11 +294,11 @@ hipError_t launch_mb(const GemvArgs& a, hipStream_t s) {
     const int n_units = (EPI == EPI_SWIGLU) ? a.N : a.N / 2;
     const dim3 grid((n_units + kWavesPerBlock - 1) / kWavesPerBlock);
     if (a.M == 1) {
-        hipLaunchKernelGGL((gemv_kernel<WT, 1, EPI, NORM>), grid, dim3(kThreads), 0, s, a);
+        launch_kernel((gemv_kernel<WT, 1, EPI, NORM>), grid, dim3(kThreads), 0, s, a);
     } else if (a.M == 2) {
-        hipLaunchKernelGGL((gemv_kernel<WT, 2, EPI, NORM>), grid, dim3(kThreads), 0, s, a);
+        launch_kernel((gemv_kernel<WT, 2, EPI, NORM>), grid, dim3(kThreads), 0, s, a);
     } else {
-        hipLaunchKernelGGL((gemv_kernel<WT, 4, EPI, NORM>), grid, dim3(kThreads), 0, s, a);
+        launch_kernel((gemv_kernel<WT, 4, EPI, NORM>), grid, dim3(kThreads), 0, s, a);
     }
     return hipGetLastError();
 }

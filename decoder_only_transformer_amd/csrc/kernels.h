@@ -1,10 +1,29 @@
 // Launch interface between the host library (llama_api.cpp) and the gfx950 kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace llk {
+
+// Per-kernel timing for diagnostics.  While a timer is installed on the calling thread,
+// every kernel goes out through hipExtLaunchKernel with an event pair of its own, which HIP
+// ties to that dispatch's begin and end timestamps (so queue gaps between launches are not
+// counted).  With no timer installed a launch is a plain hipLaunchKernelGGL.
+struct KernelTimer {
+    virtual bool next_pair(hipEvent_t* start, hipEvent_t* stop) = 0;
+};
+extern thread_local KernelTimer* t_kernel_timer;
+
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, Args... args) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (t_kernel_timer && t_kernel_timer->next_pair(&e0, &e1))
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, e0, e1, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+}
 
 enum Epilogue : int {
     EPI_QKV = 0,     // rows of [wq; wk; wv]: RoPE on q and k, q -> q buffer, k/v -> KV cache

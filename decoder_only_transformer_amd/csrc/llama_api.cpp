@@ -115,13 +115,30 @@ struct llama_ctx {
     // decode graphs: one per (bsz, key splits), captured on a private stream
     hipStream_t cap_stream = nullptr;
     std::map<std::pair<int, int>, hipGraphExec_t> graphs;
-    bool use_graphs = true;
+    bool use_graphs = false;
 
-    // diagnostics: events bracketing launches of one kernel class
+    // diagnostics: per-kernel begin/end events of the launches of one kernel class
+    struct Timer : llk::KernelTimer {
+        std::vector<hipEvent_t> ev;     // pairs (start, stop)
+        size_t used = 0;
+        bool failed = false;
+        bool next_pair(hipEvent_t* start, hipEvent_t* stop) override {
+            while (used + 2 > ev.size()) {
+                hipEvent_t e;
+                if (hipEventCreate(&e) != hipSuccess) {
+                    failed = true;
+                    return false;
+                }
+                ev.push_back(e);
+            }
+            *start = ev[used];
+            *stop = ev[used + 1];
+            used += 2;
+            return true;
+        }
+    };
     int prof_class = 0;
-    std::vector<hipEvent_t> ev;     // pairs (start, stop)
-    size_t ev_used = 0;
-    bool ev_failed = false;
+    Timer timer;
 
     template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
     size_t esz() const { return bf16 ? 2 : 4; }
@@ -134,30 +151,37 @@ struct llama_ctx {
         if ((expr) != hipSuccess) return LLAMA_ERR_HIP; \
     } while (0)
 
+namespace llk {
+thread_local KernelTimer* t_kernel_timer = nullptr;
+}
+
 namespace {
 
-// Records a diagnostics event if launches of class `kc` are being bracketed.
-void prof_mark(llama_ctx* c, int kc, hipStream_t s) {
-    if (c->prof_class != kc || kc == 0) return;
-    if (c->ev_used == c->ev.size()) {
-        hipEvent_t e;
-        if (hipEventCreate(&e) != hipSuccess) {
-            c->ev_failed = true;
-            return;
+// Installs the context's kernel timer on this thread for the launches of class kc, if that
+// class is the one being profiled; removes it again at the end of the scope.
+struct TimerScope {
+    TimerScope(const llama_ctx* c, int kc) {
+        if (kc != 0 && c->prof_class == kc) {
+            llk::t_kernel_timer = &const_cast<llama_ctx*>(c)->timer;
+            on = true;
         }
-        c->ev.push_back(e);
     }
-    if (hipEventRecord(c->ev[c->ev_used++], s) != hipSuccess) c->ev_failed = true;
-}
+    ~TimerScope() {
+        if (on) llk::t_kernel_timer = nullptr;
+    }
+    bool on = false;
+};
 
 }  // namespace
 
-// Launch `expr` (a hipError_t expression) bracketed for kernel class kc.
+// Launch `expr` (a hipError_t expression); its kernels are timed if class kc is profiled.
 #define LAUNCH(c, kc, s, expr)                                 \
     do {                                                       \
-        prof_mark(const_cast<llama_ctx*>(c), (kc), (s));      \
-        const hipError_t e_ = (expr);                          \
-        prof_mark(const_cast<llama_ctx*>(c), (kc), (s));      \
+        hipError_t e_;                                         \
+        {                                                      \
+            TimerScope ts_((c), (kc));                         \
+            e_ = (expr);                                       \
+        }                                                      \
         if (e_ != hipSuccess) return LLAMA_ERR_HIP;            \
     } while (0)
 
@@ -433,8 +457,10 @@ llama_status llama_init(const llama_args* a, const llama_weights* w, void* d_wor
     c->nk = a->n_kv_heads * c->hd;
     c->bf16 = a->dtype == LLAMA_BF16;
     {
+        // Graph replay of decode steps is opt-in: measured on this stack, replaying the
+        // captured step is no faster than launching its kernels back to back.
         const char* g = std::getenv("LLAMA_MI355X_GRAPHS");
-        c->use_graphs = !(g && g[0] == '0');
+        c->use_graphs = g && g[0] == '1';
     }
 
     // RoPE table: entry (t, i) = (cos, sin) of t * theta^(-2i/hd), computed in float64.
@@ -585,20 +611,21 @@ llama_status llama_profile_select(llama_ctx* c, int32_t kernel_class) {
 
 llama_status llama_profile_read(llama_ctx* c, int64_t* launches, double* total_ms) {
     if (!c || !launches || !total_ms) return LLAMA_ERR_INVALID_ARG;
+    auto& T = c->timer;
     double ms = 0.0;
-    const size_t pairs = c->ev_used / 2;
+    const size_t pairs = T.used / 2;
     for (size_t i = 0; i < pairs; ++i) {
         float t = 0.f;
-        if (hipEventSynchronize(c->ev[2 * i + 1]) != hipSuccess ||
-            hipEventElapsedTime(&t, c->ev[2 * i], c->ev[2 * i + 1]) != hipSuccess)
+        if (hipEventSynchronize(T.ev[2 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&t, T.ev[2 * i], T.ev[2 * i + 1]) != hipSuccess)
             return LLAMA_ERR_HIP;
         ms += t;
     }
     *launches = (int64_t)pairs;
     *total_ms = ms;
-    c->ev_used = 0;
-    if (c->ev_failed) {
-        c->ev_failed = false;
+    T.used = 0;
+    if (T.failed) {
+        T.failed = false;
         return LLAMA_ERR_HIP;
     }
     return LLAMA_OK;
@@ -606,7 +633,7 @@ llama_status llama_profile_read(llama_ctx* c, int64_t* launches, double* total_m
 
 void llama_destroy(llama_ctx* c) {
     if (!c) return;
-    for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
+    for (hipEvent_t e : c->timer.ev) (void)hipEventDestroy(e);
     for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
     if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
     delete c;

@@ -149,7 +149,7 @@ __global__ void rope_scatter_kernel(const float* y, int T, QkvTarget t) {
 
 hipError_t launch_rope_scatter(const float* y, int T, const QkvTarget& t, hipStream_t s) {
     const size_t n = (size_t)T * ((t.nq + 2 * t.nk) / 2);
-    hipLaunchKernelGGL(rope_scatter_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, T, t);
+    launch_kernel(rope_scatter_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, T, t);
     return hipGetLastError();
 }
 
@@ -157,36 +157,36 @@ hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, 
                         int wbf16, int vocab, int dim, float* h, const StepState* st, hipStream_t s) {
     const dim3 grid(bsz * seqlen), block(256);
     if (wbf16)
-        hipLaunchKernelGGL(embed_kernel<bf16>, grid, block, 0, s, tokens, ld, seqlen,
+        launch_kernel(embed_kernel<bf16>, grid, block, 0, s, tokens, ld, seqlen,
                            static_cast<const bf16*>(table), vocab, dim, h, st);
     else
-        hipLaunchKernelGGL(embed_kernel<float>, grid, block, 0, s, tokens, ld, seqlen,
+        launch_kernel(embed_kernel<float>, grid, block, 0, s, tokens, ld, seqlen,
                            static_cast<const float*>(table), vocab, dim, h, st);
     return hipGetLastError();
 }
 
 hipError_t launch_set_step(StepState* st, int pos, int64_t ld, const int32_t* tokens, float* logits,
                            hipStream_t s) {
-    hipLaunchKernelGGL(set_step_kernel, dim3(1), dim3(1), 0, s, st, pos, ld, tokens, logits);
+    launch_kernel(set_step_kernel, dim3(1), dim3(1), 0, s, st, pos, ld, tokens, logits);
     return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm_bf16(const float* h, int64_t ldh, int rows, int dim, const void* w,
                                float eps, void* out, int64_t ldo, hipStream_t s) {
-    hipLaunchKernelGGL(rmsnorm_bf16_kernel<bf16>, dim3(rows), dim3(256), 0, s, h, ldh, dim,
+    launch_kernel(rmsnorm_bf16_kernel<bf16>, dim3(rows), dim3(256), 0, s, h, ldh, dim,
                        static_cast<const bf16*>(w), eps, static_cast<uint16_t*>(out), ldo);
     return hipGetLastError();
 }
 
 hipError_t launch_argmax(const float* logits, int bsz, int vocab, int64_t stride, int32_t* out,
                          hipStream_t s) {
-    hipLaunchKernelGGL(argmax_kernel, dim3(bsz), dim3(1024), 0, s, logits, vocab, stride, out);
+    launch_kernel(argmax_kernel, dim3(bsz), dim3(1024), 0, s, logits, vocab, stride, out);
     return hipGetLastError();
 }
 
 hipError_t launch_select(const int32_t* next, int32_t* tokens, int64_t ld, int cur_pos,
                          const int32_t* prompt_len, int bsz, hipStream_t s) {
-    hipLaunchKernelGGL(select_kernel, dim3((bsz + 63) / 64), dim3(64), 0, s, next, tokens, ld,
+    launch_kernel(select_kernel, dim3((bsz + 63) / 64), dim3(64), 0, s, next, tokens, ld,
                        cur_pos, prompt_len, bsz);
     return hipGetLastError();
 }

@@ -164,9 +164,9 @@ template <int EPI>
 hipError_t launch_epi(const SkinnyArgs& a, hipStream_t s) {
     const dim3 grid((a.N + 15) / 16);
     if (a.M <= 16)
-        hipLaunchKernelGGL((skinny_kernel<1, EPI>), grid, dim3(256), 0, s, a);
+        launch_kernel((skinny_kernel<1, EPI>), grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((skinny_kernel<2, EPI>), grid, dim3(256), 0, s, a);
+        launch_kernel((skinny_kernel<2, EPI>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -164,11 +164,12 @@ llama_status llama_select_next(const int32_t *d_next, int32_t *d_tokens, int64_t
 
 /*
  * Diagnostics: device time of one class of kernel launches.  llama_profile_select(c, k)
- * makes the ctx bracket every later launch of kernel class k (LLAMA_KC_*, 0 = none) with
- * a pair of HIP events recorded on the launch stream; llama_profile_read waits for those
- * events, returns the number of bracketed launches and their summed duration in
- * milliseconds, and forgets them.  Meant for measurement runs only: the events add a few
- * microseconds around each bracketed launch.
+ * makes the ctx time every kernel it later launches for class k (LLAMA_KC_*, 0 = none):
+ * each such kernel is dispatched with hipExtLaunchKernel and an event pair that HIP binds
+ * to that dispatch's own begin and end.  llama_profile_read waits for those events, returns
+ * the number of timed kernels and their summed duration in milliseconds, and forgets them.
+ * The calling thread is the one whose launches are timed.  Meant for measurement runs: the
+ * timed dispatches carry profiling timestamps.
  * Errors: INVALID_ARG for a NULL ctx/pointer or an unknown class; HIP on event failure.
  */
 enum llama_kernel_class {
