@@ -8,9 +8,11 @@ token select), with weights, prompts and KV cache already resident in HBM.
 
 Prints one JSON line.  `value` is decode tokens/s (batch * decode calls / decode time);
 prefill tokens/s (batch * prompt_len / prefill time) is reported beside it.  `roofline` is
-the dominant decode kernel (the fused RMSNorm + [w1;w3] + SiLU-gate GEMV, 44.6% of the
+the dominant decode kernel (the fused RMSNorm + [w1;w3] + SiLU-gate GEMV, about 43% of the
 bytes a 7B decode step streams): algorithmic bytes per launch over its average launch
-duration, timed live with HIP events on the launch stream.  `cpu_baseline` is the NumPy
+duration, timed live with HIP events bound to each of its dispatches; `traffic` is the HBM
+bytes per launch that rocprofv3 counters measured for the same kernel and workload (kept
+under profiles/, reported only while the kernel's sources are unchanged).  `cpu_baseline` is the NumPy
 oracle on this host's cores over a bounded sample (the whole model, the first decode calls).
 """
 from __future__ import annotations
@@ -54,6 +56,30 @@ def w13_launch_bytes(wl) -> float:
     residual rows read and the gated rows written."""
     e = 2 if wl.dtype == "bf16" else 4
     return 2 * wl.hidden_dim * wl.dim * e + wl.dim * e + wl.batch * wl.dim * 4 + wl.batch * wl.hidden_dim * 4
+
+
+def measured_traffic(kernel_class: str, workload: str):
+    """HBM bytes per launch of `kernel_class` on `workload` from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads for a
+    device copy of known size), or None if there is none or the kernel's sources have
+    changed since the counters were taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", f"{kernel_class}_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        k, sep, v = line.partition(":")
+        if sep and k.strip() in ("traffic_bytes_per_launch", "kernel_source_sha256"):
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for name in ("gemv.hip", "common.h", "kernels.h"):
+        with open(os.path.join(here, "decoder_only_transformer_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if fields.get("kernel_source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(wl, dev_weights, prompts, decode_steps: int = 48) -> dict:
@@ -227,7 +253,8 @@ def main() -> int:
         "prefill_tflops": round(prefill_tflops, 2),
         "prefill_mfma_frac": round(prefill_tflops / BF16_PEAK_TFLOPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.profile_class, wl.name),
                      "kernel": args.profile_class, "launches": n_launch, "avg_us": round(avg_us, 3),
                      "bytes_per_launch": per_launch},
         "copy_kernel_gbs": round(copy_gbs, 1),
