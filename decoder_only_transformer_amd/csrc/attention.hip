@@ -184,7 +184,8 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(AttnArgs a) {
         if (a.n_split == 1) {
             const float o = A / L;
             if (OUT_BF16)
-                static_cast<uint16_t*>(a.out)[(size_t)t * qstride + h * HD + d] = f32_to_bf16(o);
+                static_cast<uint16_t*>(a.out)[a.out_frag_mt ? frag_index(t, h * HD + d, a.out_frag_mt)
+                                                            : (size_t)t * qstride + h * HD + d] = f32_to_bf16(o);
             else
                 static_cast<float*>(a.out)[(size_t)t * qstride + h * HD + d] = o;
         } else {
@@ -237,7 +238,8 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(AttnArgs a) {
         }
         const float o = A / L;
         if (OUT_BF16)
-            static_cast<uint16_t*>(a.out)[(size_t)t * qstride + h * HD + d] = f32_to_bf16(o);
+            static_cast<uint16_t*>(a.out)[a.out_frag_mt ? frag_index(t, h * HD + d, a.out_frag_mt)
+                                                        : (size_t)t * qstride + h * HD + d] = f32_to_bf16(o);
         else
             static_cast<float*>(a.out)[(size_t)t * qstride + h * HD + d] = o;
     }

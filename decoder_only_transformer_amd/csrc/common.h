@@ -88,4 +88,12 @@ __device__ __forceinline__ float group_sum(float v) {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
+// Fragment-major position of element (m, k) of a bf16 activation matrix kept as mt tiles of
+// 16 rows: the 16 x 32 block (row tile m / 16, k-step k / 32) is 1 KB laid out in the lane
+// order of an MFMA 16x16x32 B operand, lane (m % 16) + 16 * ((k % 32) / 8) holding 8
+// consecutive k.  Rows past the matrix inside the last tile are padding.
+__device__ __forceinline__ size_t frag_index(int m, int k, int mt) {
+    return ((size_t)(k >> 5) * mt + (m >> 4)) * 512 + ((k >> 3) & 3) * 128 + (m & 15) * 8 + (k & 7);
+}
+
 }  // namespace llk

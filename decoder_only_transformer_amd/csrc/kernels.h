@@ -84,12 +84,14 @@ struct GemmArgs {
     float* part;
 };
 
-// y = x W^T for M <= 32 rows on bf16 MFMA (decode with batch > 4); x bf16 [M][ldx].
+// y = x W^T for M <= 32 rows on bf16 MFMA (decode with batch > 4).  x is bf16 in
+// fragment-major order for MT = ceil(M / 16) row tiles (frag_index).
 struct SkinnyArgs {
-    const void* x; int64_t ldx;
+    const void* x;
     int M, K, N;           // N = output rows (SWIGLU: hidden units)
     const void* w0; const void* w1; const void* w2;
     float* out; void* out16; int64_t ldo;   // STORE (fp32) / SWIGLU (bf16)
+    int out_frag_mt;       // SWIGLU: > 0 writes out16 fragment-major for that many row tiles
     float* resid; int64_t ldr;
     QkvTarget qkv;
     const StepState* st;   // if set, the STORE epilogue writes st->logits
@@ -103,6 +105,7 @@ struct AttnArgs {
     const void* cache_v;
     void* out;             // [rows][n_heads*hd], fp32 or bf16 (out_bf16)
     int out_bf16;
+    int out_frag_mt;       // bf16 out: > 0 writes it fragment-major for that many row tiles
     float* part;           // [rows][n_heads][n_split][hd + 2] partials when n_split > 1
     int* counters;         // [rows][n_kv_heads] arrival counters (zero between launches)
     int rows, n_heads, n_kv_heads, head_dim, max_seq;
@@ -130,8 +133,9 @@ hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, 
                         int wbf16, int vocab, int dim, float* h, const StepState* st, hipStream_t s);
 hipError_t launch_set_step(StepState* st, int pos, int64_t ld, const int32_t* tokens, float* logits,
                            hipStream_t s);
+// RMSNorm of fp32 rows to bf16; frag_mt > 0 writes the rows fragment-major (frag_index).
 hipError_t launch_rmsnorm_bf16(const float* h, int64_t ldh, int rows, int dim, const void* w,
-                               float eps, void* out, int64_t ldo, hipStream_t s);
+                               float eps, void* out, int64_t ldo, int frag_mt, hipStream_t s);
 hipError_t launch_gemv(int wbf16, int epi, const GemvArgs& a, hipStream_t s);
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
 hipError_t launch_skinny(int epi, const SkinnyArgs& a, hipStream_t s);

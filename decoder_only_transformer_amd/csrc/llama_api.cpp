@@ -88,8 +88,11 @@ Layout layout_of(const llama_args& a) {
     L.q32 = take(maxT * nq * sizeof(float));
     L.o32 = take(rows32 * nq * sizeof(float));
     L.g32 = take(rows32 * (size_t)a.hidden_dim * sizeof(float));
-    L.act16 = fp32 ? off : take(maxT * (size_t)(a.dim > (int)nq ? a.dim : (int)nq) * 2);
-    L.g16 = fp32 ? off : take(maxT * (size_t)a.hidden_dim * 2);
+    // bf16 activations: row-major prefill rows, or fragment-major decode rows (up to 32,
+    // padding included)
+    const size_t rows16 = std::max(maxT, (size_t)32);
+    L.act16 = fp32 ? off : take(rows16 * (size_t)(a.dim > (int)nq ? a.dim : (int)nq) * 2);
+    L.g16 = fp32 ? off : take(rows16 * (size_t)a.hidden_dim * 2);
     L.part = take(maxB * (size_t)a.n_heads * kMaxSplit * (hd + 2) * sizeof(float));
     L.counters = take(maxB * (size_t)a.n_kv_heads * sizeof(int));
     // split-K partials of the residual GEMMs, used while a prefill has at most kSplitKRows rows
@@ -216,13 +219,14 @@ int decode_splits(const llama_ctx* c, int rows, int ctx) {
 
 llama_status run_attention(const llama_ctx* c, int l, int rows, int seqlen, int start_pos,
                            void* out, bool out_bf16, bool allow_split, hipStream_t s,
-                           const StepState* st = nullptr, int graph_splits = 0) {
+                           const StepState* st = nullptr, int graph_splits = 0, int out_frag_mt = 0) {
     AttnArgs at{};
     at.q = c->at<const float>(c->L.q32);
     at.cache_k = c->kcache(l);
     at.cache_v = c->vcache(l);
     at.out = out;
     at.out_bf16 = out_bf16 ? 1 : 0;
+    at.out_frag_mt = out_frag_mt;
     at.part = c->at<float>(c->L.part);
     at.counters = c->at<int>(c->L.counters);
     at.rows = rows;
@@ -305,38 +309,40 @@ int residual_splits(const llama_ctx* c, int T, int K) {
 }
 
 // One decode block for a bf16 model at batch > kSkinnyRows: projections on the skinny MFMA
-// kernel from bf16 operands (RMSNorm to bf16 first), attention writing bf16.
+// kernel, whose activation operands (RMSNorm output, attention output, SiLU gate) are written
+// bf16 in fragment-major order for MT = ceil(M / 16) row tiles.
 llama_status block_skinny(const llama_ctx* c, int l, int M, int start_pos, hipStream_t s,
                           const StepState* st, int graph_splits) {
     const llama_layer_weights& W = c->layers[l];
     const int D = c->a.dim, F = c->a.hidden_dim;
+    const int mt = (M + 15) / 16;
     float* h = c->at<float>(c->L.h32);
     void* act = c->at<void>(c->L.act16);
     void* g16 = c->at<void>(c->L.g16);
 
-    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, M, D, W.attention_norm, c->a.norm_eps, act, D, s));
+    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, M, D, W.attention_norm, c->a.norm_eps, act, 0, mt, s));
     SkinnyArgs k{};
-    k.x = act; k.ldx = D; k.M = M; k.K = D; k.N = c->nq + 2 * c->nk;
+    k.x = act; k.M = M; k.K = D; k.N = c->nq + 2 * c->nk;
     k.w0 = W.wq; k.w1 = W.wk; k.w2 = W.wv;
     k.qkv = qkv_target(c, l, start_pos, 1, st);
     LAUNCH(c, LLAMA_KC_GEMV_QKV, s, launch_skinny(EPI_QKV, k, s));
 
-    const llama_status ast = run_attention(c, l, M, 1, start_pos, act, true, true, s, st, graph_splits);
+    const llama_status ast = run_attention(c, l, M, 1, start_pos, act, true, true, s, st, graph_splits, mt);
     if (ast != LLAMA_OK) return ast;
 
     k = SkinnyArgs{};
-    k.x = act; k.ldx = c->nq; k.M = M; k.K = c->nq; k.N = D;
+    k.x = act; k.M = M; k.K = c->nq; k.N = D;
     k.w0 = W.wo; k.resid = h; k.ldr = D;
     LAUNCH(c, LLAMA_KC_GEMV_WO, s, launch_skinny(EPI_RESID, k, s));
 
-    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, M, D, W.ffn_norm, c->a.norm_eps, act, D, s));
+    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, M, D, W.ffn_norm, c->a.norm_eps, act, 0, mt, s));
     k = SkinnyArgs{};
-    k.x = act; k.ldx = D; k.M = M; k.K = D; k.N = F;
-    k.w0 = W.w1; k.w1 = W.w3; k.out16 = g16; k.ldo = F;
+    k.x = act; k.M = M; k.K = D; k.N = F;
+    k.w0 = W.w1; k.w1 = W.w3; k.out16 = g16; k.out_frag_mt = mt;
     LAUNCH(c, LLAMA_KC_GEMV_W13, s, launch_skinny(EPI_SWIGLU, k, s));
 
     k = SkinnyArgs{};
-    k.x = g16; k.ldx = F; k.M = M; k.K = F; k.N = D;
+    k.x = g16; k.M = M; k.K = F; k.N = D;
     k.w0 = W.w2; k.resid = h; k.ldr = D;
     LAUNCH(c, LLAMA_KC_GEMV_W2, s, launch_skinny(EPI_RESID, k, s));
     return LLAMA_OK;
@@ -350,7 +356,7 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
     void* act = c->at<void>(c->L.act16);
     void* g16 = c->at<void>(c->L.g16);
 
-    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.attention_norm, c->a.norm_eps, act, D, s));
+    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.attention_norm, c->a.norm_eps, act, D, 0, s));
     GemmArgs g{};
     g.a = act; g.lda = D; g.M = T; g.K = D; g.N = c->nq + 2 * c->nk;
     g.w0 = W.wq; g.w1 = W.wk; g.w2 = W.wv;
@@ -390,7 +396,7 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
     g.splits = residual_splits(c, T, c->nq); g.part = c->at<float>(c->L.splitk);
     LAUNCH(c, LLAMA_KC_GEMM_WO, s, launch_gemm(EPI_RESID, g, s));
 
-    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.ffn_norm, c->a.norm_eps, act, D, s));
+    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.ffn_norm, c->a.norm_eps, act, D, 0, s));
     g = GemmArgs{};
     g.a = act; g.lda = D; g.M = T; g.K = D; g.N = F;
     g.w0 = W.w1; g.w1 = W.w3; g.out16 = g16; g.ldo16 = F;
@@ -505,7 +511,7 @@ llama_status llama_prefill(llama_ctx* c, const int32_t* d_tokens, int64_t ld_tok
     if (!all_positions) return final_logits(c, h + (size_t)(seqlen - 1) * D, (int64_t)seqlen * D, bsz, d_logits, s);
     if (!c->bf16) return final_logits(c, h, D, T, d_logits, s);
     void* act = c->at<void>(c->L.act16);
-    HIP_TRY(launch_rmsnorm_bf16(h, D, T, D, c->w.norm, c->a.norm_eps, act, D, s));
+    HIP_TRY(launch_rmsnorm_bf16(h, D, T, D, c->w.norm, c->a.norm_eps, act, D, 0, s));
     GemmArgs g{};
     g.a = act; g.lda = D; g.M = T; g.K = D; g.N = c->a.vocab_size;
     g.w0 = c->w.output; g.out = d_logits; g.ldo = c->a.vocab_size;
@@ -530,9 +536,9 @@ static llama_status decode_plan(llama_ctx* c, const int32_t* d_tokens, int64_t l
     }
     if (!skinny) return final_logits(c, h, D, bsz, d_logits, s, st);
     void* act = c->at<void>(c->L.act16);
-    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, bsz, D, c->w.norm, c->a.norm_eps, act, D, s));
+    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, bsz, D, c->w.norm, c->a.norm_eps, act, 0, (bsz + 15) / 16, s));
     SkinnyArgs k{};
-    k.x = act; k.ldx = D; k.M = bsz; k.K = D; k.N = c->a.vocab_size;
+    k.x = act; k.M = bsz; k.K = D; k.N = c->a.vocab_size;
     k.w0 = c->w.output; k.out = d_logits; k.ldo = c->a.vocab_size; k.st = st;
     LAUNCH(c, LLAMA_KC_GEMV_OUT, s, launch_skinny(EPI_STORE, k, s));
     return LLAMA_OK;

@@ -28,7 +28,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* tokens, int64
 template <typename WT>
 __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const float* h, int64_t ldh, int dim,
                                                            const WT* w, float eps, uint16_t* out,
-                                                           int64_t ldo) {
+                                                           int64_t ldo, int frag_mt) {
     __shared__ float red[4];
     const float* x = h + (size_t)blockIdx.x * ldh;
     float ss = 0.f;
@@ -40,13 +40,14 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const float* h, int64
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
     const float r = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)dim + eps);
-    uint16_t* o = out + (size_t)blockIdx.x * ldo;
+    // row-major [rows][ldo], or fragment-major (4 consecutive k stay adjacent in both)
     for (int k = threadIdx.x * 4; k < dim; k += 256 * 4) {
         const float4 v = *reinterpret_cast<const float4*>(x + k);
         uint2 p;
         p.x = pack_bf16x2(v.x * r * Elem<WT>::load(w, k), v.y * r * Elem<WT>::load(w, k + 1));
         p.y = pack_bf16x2(v.z * r * Elem<WT>::load(w, k + 2), v.w * r * Elem<WT>::load(w, k + 3));
-        *reinterpret_cast<uint2*>(o + k) = p;
+        const size_t o = frag_mt ? frag_index(blockIdx.x, k, frag_mt) : (size_t)blockIdx.x * ldo + k;
+        *reinterpret_cast<uint2*>(out + o) = p;
     }
 }
 
@@ -172,9 +173,9 @@ hipError_t launch_set_step(StepState* st, int pos, int64_t ld, const int32_t* to
 }
 
 hipError_t launch_rmsnorm_bf16(const float* h, int64_t ldh, int rows, int dim, const void* w,
-                               float eps, void* out, int64_t ldo, hipStream_t s) {
+                               float eps, void* out, int64_t ldo, int frag_mt, hipStream_t s) {
     launch_kernel(rmsnorm_bf16_kernel<bf16>, dim3(rows), dim3(256), 0, s, h, ldh, dim,
-                       static_cast<const bf16*>(w), eps, static_cast<uint16_t*>(out), ldo);
+                  static_cast<const bf16*>(w), eps, static_cast<uint16_t*>(out), ldo, frag_mt);
     return hipGetLastError();
 }
 

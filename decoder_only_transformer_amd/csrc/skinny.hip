@@ -1,14 +1,22 @@
 // Weight-streaming products for a few activation rows on bf16 MFMA (decode with batch > 4).
 //
 // y[m][n] = sum_k x[m][k] * W[n][k] for M <= 32 rows.  The vector-ALU GEMV would spend M FMAs
-// per weight element; here the weights are the MFMA A operand instead: a workgroup owns 16
-// output rows (16 hidden units for the SiLU gate, from w1 and w3), its four waves take
-// interleaved 32-wide k-steps, each lane streams 16 bytes of one weight row per k-step with
-// eight k-steps of loads in flight, and the activations -- bf16 [M][K], L2 resident -- are
-// read directly as B fragments (rows of the batch as MFMA columns).  The waves' partial
-// sums meet in LDS; the result tile D[n][m] puts the RoPE pair (n, n+1) in one lane.
-// Epilogues match the GEMV ones: RoPE + bf16 q / KV append, residual add, SiLU gate (bf16
-// out), fp32 logits.
+// per weight element; here the weights are the MFMA A operand (16 output rows) and the
+// activations the B operand (batch rows as MFMA columns).
+//
+// Memory access is what matters.  A 16-row A fragment loaded straight from a row-major
+// matrix touches 16 rows per quarter-wave and ran at half of HBM bandwidth, so:
+//  - weights go global -> LDS with global_load_lds_dwordx4, 8 rows x 128 bytes per wave
+//    instruction (lanes 8r..8r+7 read the chunks of row r: whole cache lines); lane 8r + s
+//    fetches chunk s ^ r, so that a fragment read (16 rows, one chunk each) hits distinct
+//    LDS banks;
+//  - activations arrive in fragment-major order (their producer wrote them that way; see
+//    frag_index), so a wave's B fragment is one contiguous 1 KB load.
+// A workgroup owns 16 output rows; its waves take interleaved stages of 64 k (128 bytes of
+// each row), each wave through a ring of its own (D slots, D - 1 stages in flight), with no
+// barrier inside the loop.  At the end the waves' partial sums meet in LDS.
+// Epilogues: RoPE + bf16 q / KV append, residual add, SiLU gate (bf16 out, optionally in
+// fragment-major order for the next product), fp32 logits.
 #include "common.h"
 #include "kernels.h"
 
@@ -17,47 +25,143 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-constexpr int kWaves = 4;
-constexpr int kPF = 8;        // k-steps of weight loads in flight per wave
+constexpr int kSkBK = 64;          // k per stage: 128 bytes of every row
+constexpr int kSkWBytes = 2048;    // one matrix's stage for one wave: 16 rows x 128 bytes
 
 __device__ __forceinline__ bf16x8_t frag(const uint4& v) {
     return __builtin_bit_cast(bf16x8_t, u32x4_t{v.x, v.y, v.z, v.w});
 }
+__device__ __forceinline__ bf16x8_t frag(const u32x4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-template <int MT, int EPI>
-__global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
-    constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;    // weight matrices per output unit
-    __shared__ f32x4 red[kWaves][NW][MT][64];
+// Byte offset, inside a block of 8 rows x 128 bytes, of 16-byte chunk c of row r.
+__device__ __forceinline__ int sk_slot(int r, int c) { return (8 * r + (c ^ r)) * 16; }
+
+// Two LDS fragment reads that wait for their own results (the compiler then has no LDS read
+// to order after the ring's DMA writes, which it cannot tell apart from this stage's).
+__device__ __forceinline__ void lds_read2(u32x4_t& r0, u32x4_t& r1, uint32_t a0, uint32_t a1) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1)
+        : "v"(a0), "v"(a1)
+        : "memory");
+}
+
+// Pointer to row n of the weight matrix `w` of the product (QKV: the row of wq, wk or wv).
+template <int EPI>
+__device__ __forceinline__ const uint16_t* sk_row(const SkinnyArgs& a, int w, int n) {
+    if (EPI == EPI_QKV) {
+        const int nq = a.qkv.nq, nk = a.qkv.nk;
+        const void* m = n < nq ? a.w0 : (n < nq + nk ? a.w1 : a.w2);
+        const int r = n < nq ? n : (n < nq + nk ? n - nq : n - nq - nk);
+        return static_cast<const uint16_t*>(m) + (size_t)r * a.K;
+    }
+    return static_cast<const uint16_t*>(w == 0 ? a.w0 : a.w1) + (size_t)n * a.K;
+}
+
+// Epilogue of one 16 x 16 result tile: acc[w][e] = y[m][n = nb + 4g + e] of matrix w.
+template <int NW, int EPI>
+__device__ __forceinline__ void sk_epilogue(const SkinnyArgs& a, const f32x4 (&acc)[NW], int m, int nb, int g) {
+    if (m >= a.M) return;
+    if (EPI == EPI_QKV) {
+        const QkvTarget& q = a.qkv;
+        const int b = m / q.seqlen;
+        const int pos = (q.st ? q.st->pos : q.start_pos) + (m - b * q.seqlen);
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+            const int n = nb + 4 * g + e;
+            if (n >= a.N) continue;
+            float y0 = acc[0][e], y1 = acc[0][e + 1];
+            if (n < q.nq + q.nk) {
+                const float2 cs = q.rope[(size_t)pos * (q.head_dim / 2) + (n % q.head_dim) / 2];
+                const float r0 = y0 * cs.x - y1 * cs.y;
+                const float r1 = y0 * cs.y + y1 * cs.x;
+                y0 = r0;
+                y1 = r1;
+            }
+            if (n < q.nq) {
+                q.q[(size_t)m * q.nq + n] = round_bf16(y0);
+                q.q[(size_t)m * q.nq + n + 1] = round_bf16(y1);
+            } else {
+                const bool is_k = n < q.nq + q.nk;
+                const int c = is_k ? n - q.nq : n - q.nq - q.nk;
+                uint16_t* cache = static_cast<uint16_t*>(is_k ? q.cache_k : q.cache_v);
+                *reinterpret_cast<uint32_t*>(cache + ((size_t)b * q.max_seq + pos) * (size_t)q.nk + c) =
+                    pack_bf16x2(y0, y1);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int n = nb + 4 * g + e;
+            if (n >= a.N) continue;
+            if (EPI == EPI_RESID) {
+                a.resid[(size_t)m * a.ldr + n] += acc[0][e];
+            } else if (EPI == EPI_SWIGLU) {
+                const size_t o = a.out_frag_mt ? frag_index(m, n, a.out_frag_mt) : (size_t)m * a.ldo + n;
+                static_cast<uint16_t*>(a.out16)[o] = f32_to_bf16(silu(acc[0][e]) * acc[NW - 1][e]);
+            } else {
+                (a.st ? a.st->logits : a.out)[(size_t)m * a.ldo + n] = acc[0][e];
+            }
+        }
+    }
+}
+
+template <int NW, int MT, int EPI, int D, int NWV>
+__global__ __launch_bounds__(64 * NWV) void skinny_kernel(SkinnyArgs a) {
+    constexpr int kStage = NW * kSkWBytes;        // one wave's ring slot
+    constexpr int kOps = 2 * NW + 2 * MT;         // loads per wave per stage (DMA + fragments)
+    constexpr int kWait = (D - 2) * kOps;         // loads of later stages left in flight
+    static_assert(kWait < 64, "vmcnt holds at most 63");
+    static_assert(NWV * D * kStage >= NWV * NW * MT * 64 * 16, "the reduction reuses the ring");
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NWV * D * kStage];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int fr = lane & 15, g = lane >> 4;
     const int n0 = blockIdx.x * 16;
-    const int K = a.K;
-    const int nsteps = K / 32;
+    const int nst = a.K / kSkBK;
+    const int n_my = (nst - wid + NWV - 1) / NWV;     // stages wid, wid + NWV, ... of this wave
 
-    // weight rows of this lane (row n0 + fr of each matrix; clamped past N)
-    const uint16_t* wrow[NW];
-    {
-        const int n = min(n0 + fr, a.N - 1);
-        if (EPI == EPI_SWIGLU) {
-            wrow[0] = static_cast<const uint16_t*>(a.w0) + (size_t)n * K;
-            wrow[1] = static_cast<const uint16_t*>(a.w1) + (size_t)n * K;
-        } else if (EPI == EPI_QKV) {
-            const int nq = a.qkv.nq, nk = a.qkv.nk;
-            const uint16_t* m = static_cast<const uint16_t*>(n < nq ? a.w0 : (n < nq + nk ? a.w1 : a.w2));
-            const int r = n < nq ? n : (n < nq + nk ? n - nq : n - nq - nk);
-            wrow[0] = m + (size_t)r * K;
-        } else {
-            wrow[0] = static_cast<const uint16_t*>(a.w0) + (size_t)n * K;
-        }
-    }
-    // activation rows of this lane (batch rows fr and 16 + fr; clamped past M, masked later)
-    const uint16_t* xrow[MT];
+    // DMA sources of this lane: rows n0 + 8h + r8 (clamped past N), chunk c8
+    const int r8 = lane >> 3, c8 = (lane & 7) ^ r8;
+    const uint16_t* wsrc[NW][2];
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-        xrow[t] = static_cast<const uint16_t*>(a.x) + (size_t)min(16 * t + fr, a.M - 1) * a.ldx;
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) wsrc[w][h] = sk_row<EPI>(a, w, min(n0 + 8 * h + r8, a.N - 1)) + c8 * 8;
+    // fragment-major activations: tile t of k-step s is the 1 KB at element (s * MT + t) * 512
+    const uint16_t* xsrc = static_cast<const uint16_t*>(a.x) + lane * 8;
+
+    uint8_t* wring = ring + wid * D * kStage;
+    const uint32_t wring_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)wring));
+    uint4 xr[D][2][MT];     // activation fragments of the stages in flight
+
+    // Workgroups start at rotated points of K: with every workgroup at the same k, the rows'
+    // chunks (a fixed stride apart) crowd onto the same HBM channels.
+    const int rot = (int)((blockIdx.x * 37u) % (unsigned)nst);
+    auto issue = [&](int i, int u) {
+        int kt = min(wid + NWV * i, nst - 1) + rot;     // repeats of the last stage past the end
+        kt = kt >= nst ? kt - nst : kt;
+        const int k = kt * kSkBK;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                __builtin_amdgcn_global_load_lds((gbl_void_t*)(wsrc[w][h] + k),
+                                                 (lds_void_t*)(wring + u * kStage + w * kSkWBytes + h * 1024), 16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) xr[u][j][t] = ld16(xsrc + (size_t)((2 * kt + j) * MT + t) * 512);
+    };
+
+    // A fragment offsets in a slot for the two k-steps of a stage (chunks 4j + g)
+    const uint32_t aoff0 = (fr >> 3) * 1024 + sk_slot(fr & 7, g);
+    const uint32_t aoff1 = (fr >> 3) * 1024 + sk_slot(fr & 7, 4 + g);
 
     f32x4 acc[NW][MT];
 #pragma unroll
@@ -65,115 +169,88 @@ __global__ __launch_bounds__(256) void skinny_kernel(SkinnyArgs a) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[w][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // this wave's k-steps: wid, wid + 4, ...; weight loads kPF steps ahead
-    for (int s0 = wid; s0 < nsteps; s0 += kWaves * kPF) {
-        uint4 wv[kPF][NW];
-        uint4 xv[kPF][MT];
+    // live = 0 (a step past this wave's last stage): the weight fragments are masked to zero,
+    // so the product adds nothing; no branch, so the loop body stays straight-line
+    auto compute = [&](int u, uint32_t live) {
+        const uint32_t sb = wring_addr + u * kStage;
+        u32x4_t ra[NW][2];
 #pragma unroll
-        for (int u = 0; u < kPF; ++u) {
-            const int st = min(s0 + u * kWaves, nsteps - 1);
-            const int k = st * 32 + g * 8;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) wv[u][w] = ld16_stream(wrow[w] + k);
-#pragma unroll
-            for (int t = 0; t < MT; ++t) xv[u][t] = ld16(xrow[t] + k);
+        for (int w = 0; w < NW; ++w) {
+            lds_read2(ra[w][0], ra[w][1], sb + w * kSkWBytes + aoff0, sb + w * kSkWBytes + aoff1);
+            ra[w][0] &= live;
+            ra[w][1] &= live;
         }
-        asm volatile("" ::: "memory");   // keep all kPF steps of loads issued before any use
 #pragma unroll
-        for (int u = 0; u < kPF; ++u) {
-            // steps past the end were loaded clamped; a zero weight fragment cancels them
-            const bool live = s0 + u * kWaves < nsteps;
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const uint4 wz = live ? wv[u][w] : make_uint4(0, 0, 0, 0);
+            for (int w = 0; w < NW; ++w)
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
-                    acc[w][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag(wz), frag(xv[u][t]), acc[w][t], 0, 0, 0);
-            }
+                    acc[w][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag(ra[w][j]), frag(xr[u][j][t]), acc[w][t], 0, 0, 0);
+    };
+
+#pragma unroll
+    for (int u = 0; u < D - 1; ++u) issue(u, u);
+    // Whole ring revolutions with a straight-line body: steps past this wave's last stage
+    // still wait and issue (repeats) and add zero, so the loop has one path and the
+    // compiler's own wait counts stay exact across its back edge.
+    for (int i0 = 0; i0 < n_my; i0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            // this wave's loads of step i0 + u have landed once only those of the D - 2 later
+            // steps are outstanding; its reads of the previous slot finished in compute
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWait) : "memory");
+            issue(i0 + u + D - 1, (u + D - 1) % D);
+            compute(u, i0 + u < n_my ? 0xffffffffu : 0u);
         }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the repeated tail loads
 
-    // sum the four waves' partials
-#pragma unroll
-    for (int w = 0; w < NW; ++w)
-#pragma unroll
-        for (int t = 0; t < MT; ++t) red[wid][w][t][lane] = acc[w][t];
+    // sum the waves' partials: red[wave][w][t][lane] in the ring's memory
     __syncthreads();
-    if (wid != 0) return;
+    f32x4* red = reinterpret_cast<f32x4*>(ring);
 #pragma unroll
     for (int w = 0; w < NW; ++w)
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            f32x4 v = red[0][w][t][lane];
+        for (int t = 0; t < MT; ++t) red[((wid * NW + w) * MT + t) * 64 + lane] = acc[w][t];
+    __syncthreads();
+    // wave t finishes result tile t (batch rows 16t .. 16t + 15)
+    if (wid >= MT) return;
+    f32x4 sum[NW];
 #pragma unroll
-            for (int q = 1; q < kWaves; ++q) v += red[q][w][t][lane];
-            acc[w][t] = v;
-        }
-
-    // lane holds D[n = n0 + 4g + e][m = 16t + fr]
+    for (int w = 0; w < NW; ++w) {
+        sum[w] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        const int m = 16 * t + fr;
-        if (m >= a.M) continue;
-        if (EPI == EPI_QKV) {
-            const QkvTarget& q = a.qkv;
-            const int b = m / q.seqlen;
-            const int pos = (q.st ? q.st->pos : q.start_pos) + (m - b * q.seqlen);
-#pragma unroll
-            for (int e = 0; e < 4; e += 2) {
-                const int n = n0 + 4 * g + e;
-                if (n >= a.N) continue;
-                float y0 = acc[0][t][e], y1 = acc[0][t][e + 1];
-                if (n < q.nq + q.nk) {
-                    const float2 cs = q.rope[(size_t)pos * (q.head_dim / 2) + (n % q.head_dim) / 2];
-                    const float r0 = y0 * cs.x - y1 * cs.y;
-                    const float r1 = y0 * cs.y + y1 * cs.x;
-                    y0 = r0;
-                    y1 = r1;
-                }
-                if (n < q.nq) {
-                    q.q[(size_t)m * q.nq + n] = round_bf16(y0);
-                    q.q[(size_t)m * q.nq + n + 1] = round_bf16(y1);
-                } else {
-                    const bool is_k = n < q.nq + q.nk;
-                    const int c = is_k ? n - q.nq : n - q.nq - q.nk;
-                    uint16_t* cache = static_cast<uint16_t*>(is_k ? q.cache_k : q.cache_v);
-                    *reinterpret_cast<uint32_t*>(cache + ((size_t)b * q.max_seq + pos) * (size_t)q.nk + c) =
-                        pack_bf16x2(y0, y1);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int n = n0 + 4 * g + e;
-                if (n >= a.N) continue;
-                if (EPI == EPI_RESID) {
-                    a.resid[(size_t)m * a.ldr + n] += acc[0][t][e];
-                } else if (EPI == EPI_SWIGLU) {
-                    static_cast<uint16_t*>(a.out16)[(size_t)m * a.ldo + n] =
-                        f32_to_bf16(silu(acc[0][t][e]) * acc[NW - 1][t][e]);
-                } else {
-                    (a.st ? a.st->logits : a.out)[(size_t)m * a.ldo + n] = acc[0][t][e];
-                }
-            }
-        }
+        for (int q = 0; q < NWV; ++q) sum[w] += red[((q * NW + w) * MT + wid) * 64 + lane];
     }
+    sk_epilogue<NW, EPI>(a, sum, 16 * wid + fr, n0, g);
 }
 
-template <int EPI>
-hipError_t launch_epi(const SkinnyArgs& a, hipStream_t s) {
+template <int NW, int EPI, int D, int NWV>
+hipError_t launch_waves(const SkinnyArgs& a, hipStream_t s) {
     const dim3 grid((a.N + 15) / 16);
     if (a.M <= 16)
-        launch_kernel((skinny_kernel<1, EPI>), grid, dim3(256), 0, s, a);
+        launch_kernel((skinny_kernel<NW, 1, EPI, D, NWV>), grid, dim3(64 * NWV), 0, s, a);
     else
-        launch_kernel((skinny_kernel<2, EPI>), grid, dim3(256), 0, s, a);
+        launch_kernel((skinny_kernel<NW, 2, EPI, D, NWV>), grid, dim3(64 * NWV), 0, s, a);
     return hipGetLastError();
+}
+
+// Ring depth per wave and waves per workgroup: 8 waves when there are too few 16-row tiles
+// for two 4-wave workgroups per CU; the LDS of a workgroup stays at or under 128 KB.
+template <int EPI>
+hipError_t launch_epi(const SkinnyArgs& a, hipStream_t s) {
+    constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;
+    constexpr int D = NW == 1 ? 8 : 4;
+    const int tiles = (a.N + 15) / 16;
+    if (tiles >= 512) return launch_waves<NW, EPI, D, 4>(a, s);
+    return launch_waves<NW, EPI, D, 8>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_skinny(int epi, const SkinnyArgs& a, hipStream_t s) {
-    if (a.M > 32 || a.K % 32 != 0) return hipErrorInvalidValue;
+    if (a.M < 1 || a.M > 32 || a.K % kSkBK != 0 || a.K < kSkBK) return hipErrorInvalidValue;
     switch (epi) {
         case EPI_QKV: return launch_epi<EPI_QKV>(a, s);
         case EPI_RESID: return launch_epi<EPI_RESID>(a, s);

@@ -190,6 +190,16 @@ SMALL_BF16 = {
                                                n_kv_heads=4, dim=512, hidden_dim=1536, vocab_size=1000,
                                                batch=4, prompt_len=17, gen_steps=20, weight_seed=13,
                                                prompt_seed=113),
+    # decode batches above 4 take the skinny MFMA products (split over K at these widths):
+    # 6 rows (one 16-column tile, rows past the batch clamped) and 32 (two full tiles)
+    "b6": synth.WORKLOADS["tiny_fp32"].with_(name="small_bf16_b6", dtype="bf16", n_heads=16,
+                                             n_kv_heads=2, dim=1024, hidden_dim=2816, vocab_size=2048,
+                                             batch=6, prompt_len=0, prompt_len_range=(20, 60),
+                                             gen_steps=16, weight_seed=15, prompt_seed=115, max_seq_len=128),
+    "b32": synth.WORKLOADS["tiny_fp32"].with_(name="small_bf16_b32", dtype="bf16", n_heads=8,
+                                              n_kv_heads=8, dim=1024, hidden_dim=2816, vocab_size=1000,
+                                              batch=32, prompt_len=0, prompt_len_range=(12, 40),
+                                              gen_steps=12, weight_seed=16, prompt_seed=116, max_seq_len=96),
     # long prompts: 4 x 600 = 2400 prefill rows take the large-M GEMM path (ragged tiles)
     # and the plain-store QKV projection followed by the RoPE / bf16-storage pass
     "long": synth.WORKLOADS["tiny_fp32"].with_(name="small_bf16_long", dtype="bf16", n_heads=4,
@@ -263,7 +273,7 @@ def test_small_bf16_chunked_prefill_all_positions(name):
     model.close()
 
 
-@pytest.mark.parametrize("name", ["gqa8", "mha"])
+@pytest.mark.parametrize("name", ["gqa8", "mha", "b6"])
 def test_decode_graph_replays_match_eager_launches(name):
     """Decode steps replay one captured graph per split count; the generate loop puts eager
     work (argmax, select, step-state writes) between replays.  Every replay's logits must
