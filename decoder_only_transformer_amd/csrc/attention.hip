@@ -5,8 +5,9 @@
 // 16-lane group loads four keys' K and V rows before using any of them and keeps a running
 // (max, sum, acc) online softmax per head in fp32.  The sixteen groups are merged through
 // LDS.  With more than one split per row, every workgroup stores its partial (m, l, acc)
-// and the last one to arrive (per-row counter) merges all splits in split order and
-// resets the counter, so no second launch is needed and the result is deterministic.
+// with device-coherent stores and the last one to arrive (per-row counter) merges all
+// splits in split order and resets the counter, so no second launch is needed and the
+// result is deterministic.
 #include "common.h"
 #include "kernels.h"
 
@@ -190,28 +191,20 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(AttnArgs a) {
                 static_cast<float*>(a.out)[(size_t)t * qstride + h * HD + d] = o;
         } else {
             float* pp = a.part + (((size_t)t * a.n_heads + h) * a.n_split + split) * (HD + 2);
-            pp[d] = A;
+            st_agent(pp + d, A);
             if (d == 0) {
-                pp[HD] = M;
-                pp[HD + 1] = L;
+                st_agent(pp + HD, M);
+                st_agent(pp + HD + 1, L);
             }
         }
     }
     if (a.n_split == 1) return;
 
-    // Last workgroup of this (row, kv head) to arrive merges the splits.
+    // Last workgroup of this (row, kv head) to arrive merges the splits; the partials went
+    // out as device-coherent stores and are read back the same way.
     __shared__ int s_last;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const int old = atomicAdd(&a.counters[(size_t)t * a.n_kv_heads + kvh], 1);
-        s_last = (old == a.n_split - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    // acquire: the other splits' partials (released by their fence before the counter
-    // increment) are visible to ordinary loads from here on
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    int* counter = &a.counters[(size_t)t * a.n_kv_heads + kvh];
+    if (!arrive_last(counter, a.n_split, &s_last)) return;
     for (int idx = tid; idx < NREP * HD; idx += blockDim.x) {
         const int r = idx / HD, d = idx - r * HD;
         const int h = kvh * NREP + r;
@@ -221,9 +214,9 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(AttnArgs a) {
 #pragma unroll
         for (int sp = 0; sp < kMaxSplitMerge; ++sp) {
             if (sp < a.n_split) {
-                ms[sp] = pp[sp * (HD + 2) + HD];
-                ls[sp] = pp[sp * (HD + 2) + HD + 1];
-                as[sp] = pp[sp * (HD + 2) + d];
+                ms[sp] = ld_agent(pp + sp * (HD + 2) + HD);
+                ls[sp] = ld_agent(pp + sp * (HD + 2) + HD + 1);
+                as[sp] = ld_agent(pp + sp * (HD + 2) + d);
                 M = fmaxf(M, ms[sp]);
             }
         }
@@ -243,7 +236,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(AttnArgs a) {
         else
             static_cast<float*>(a.out)[(size_t)t * qstride + h * HD + d] = o;
     }
-    if (tid == 0) a.counters[(size_t)t * a.n_kv_heads + kvh] = 0;
+    if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Waves per workgroup: many for single-token rows (decode: one workgroup covers a short
