@@ -73,6 +73,45 @@ __device__ __forceinline__ void merge_with_lane(float (&m)[NREP], float (&l)[NRE
     }
 }
 
+// Final output of (row t, kv head kvh) from the n_split partials (m, l, acc) of its splits,
+// merged in split order; partials are read device-coherently (they were stored that way by
+// other workgroups of this launch).
+template <int HD, int NREP, bool OUT_BF16>
+__device__ __forceinline__ void merge_splits(const AttnArgs& a, int t, int kvh, int tid, int nthreads) {
+    const int qstride = a.n_heads * HD;
+    for (int idx = tid; idx < NREP * HD; idx += nthreads) {
+        const int r = idx / HD, d = idx - r * HD;
+        const int h = kvh * NREP + r;
+        const float* pp = a.part + ((size_t)t * a.n_heads + h) * a.n_split * (HD + 2);
+        float ms[kMaxSplitMerge], ls[kMaxSplitMerge], as[kMaxSplitMerge];
+        float M = -INFINITY;
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplitMerge; ++sp) {
+            if (sp < a.n_split) {
+                ms[sp] = ld_agent(pp + sp * (HD + 2) + HD);
+                ls[sp] = ld_agent(pp + sp * (HD + 2) + HD + 1);
+                as[sp] = ld_agent(pp + sp * (HD + 2) + d);
+                M = fmaxf(M, ms[sp]);
+            }
+        }
+        float L = 0.f, A = 0.f;
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplitMerge; ++sp) {
+            if (sp < a.n_split && ms[sp] != -INFINITY) {
+                const float w = __expf(ms[sp] - M);
+                L += ls[sp] * w;
+                A += as[sp] * w;
+            }
+        }
+        const float o = A / L;
+        if (OUT_BF16)
+            static_cast<uint16_t*>(a.out)[a.out_frag_mt ? frag_index(t, h * HD + d, a.out_frag_mt)
+                                                        : (size_t)t * qstride + h * HD + d] = f32_to_bf16(o);
+        else
+            static_cast<float*>(a.out)[(size_t)t * qstride + h * HD + d] = o;
+    }
+}
+
 template <typename KT, int HD, int NREP, bool OUT_BF16, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(AttnArgs a) {
     constexpr int EPL = HD / 16;
@@ -205,37 +244,203 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(AttnArgs a) {
     __shared__ int s_last;
     int* counter = &a.counters[(size_t)t * a.n_kv_heads + kvh];
     if (!arrive_last(counter, a.n_split, &s_last)) return;
-    for (int idx = tid; idx < NREP * HD; idx += blockDim.x) {
+    merge_splits<HD, NREP, OUT_BF16>(a, t, kvh, tid, blockDim.x);
+    if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------------------
+// Decode rows with several query heads per kv head (GQA, n_rep >= 4) on MFMA.  The n_rep
+// query heads of one position share every K/V row, so per workgroup (row, kv head, key
+// split) the scores are a small matrix product: S^T = K Q^T (16x16x32 MFMA, keys as rows,
+// the n_rep heads as columns padded to 16) and O^T += V^T P^T (16x16x16 MFMA).  A lane of
+// S^T holds 4 consecutive keys of one head, which is exactly the B fragment P^T needs, so
+// the probabilities never move between lanes; P is split into a bf16 high part and a bf16
+// remainder (two MFMAs) to keep fp32-softmax accuracy.  K (row-major) and V^T tiles of 64
+// keys are staged in LDS, double-buffered, with one barrier per tile; each of the four waves
+// takes 16 keys of a tile and keeps its own online-softmax state, merged at the end through
+// LDS.  Splits merge as in the kernel above.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8v __attribute__((ext_vector_type(8)));
+
+template <int HD, int NREP, bool OUT_BF16>
+__global__ __launch_bounds__(256) void attn_gqa_decode_kernel(AttnArgs a) {
+    constexpr int KT = 64;             // keys per tile, 16 per wave
+    constexpr int KS = HD / 32;        // k-steps of S^T over head_dim
+    constexpr int DT = HD / 16;        // 16-row tiles of O^T
+    constexpr int KLD = HD + 8;        // padded K row (elements)
+    constexpr int VLD = KT + 8;        // padded V^T row (elements)
+    constexpr int CH = KT * HD / 8;    // 16-byte chunks of a K (or V) tile
+    constexpr int CPT = CH / 256;      // chunks per thread
+    static_assert(NREP <= 16 && CPT >= 1, "shape");
+    // staging buffers; after the last tile the same memory holds the waves' O^T for the merge
+    constexpr int kStageBytes = 2 * KT * KLD * 2 + 2 * HD * VLD * 2;
+    constexpr int kMergeBytes = 4 * HD * 17 * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes];
+    auto Ks = reinterpret_cast<uint16_t(*)[KT][KLD]>(lds);
+    auto Vt = reinterpret_cast<uint16_t(*)[HD][VLD]>(lds + 2 * KT * KLD * 2);
+    auto s_o = reinterpret_cast<float(*)[HD][17]>(lds);
+    __shared__ float s_m[4][16], s_l[4][16];
+
+    const int split = blockIdx.x, kvh = blockIdx.y, t = a.row0 + blockIdx.z;
+    const int b = t / a.seqlen;
+    const int start_pos = a.st ? a.st->pos : a.start_pos;
+    const int pos = start_pos + (t - b * a.seqlen);
+    const int ctx = pos + 1;
+    const int chunk = a.chunk ? a.chunk : ((start_pos + a.seqlen + a.n_split - 1) / a.n_split + 15) / 16 * 16;
+    const int j0 = split * chunk;
+    const int j1 = min(ctx, j0 + chunk);
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int fr = lane & 15, g = lane >> 4;
+    const int qstride = a.n_heads * HD;
+    const int64_t kv_row = (int64_t)a.n_kv_heads * HD;
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.cache_k) + (size_t)b * a.max_seq * kv_row + (size_t)kvh * HD;
+    const uint16_t* vbase = static_cast<const uint16_t*>(a.cache_v) + (size_t)b * a.max_seq * kv_row + (size_t)kvh * HD;
+
+    // Q^T fragments: column fr = head kvh * NREP + fr (zero past NREP), k = 32 ks + 8 g + e
+    bf16x8v qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u16x8v v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            v[e] = fr < NREP ? f32_to_bf16(a.q[(size_t)t * qstride + (kvh * NREP + fr) * HD + ks * 32 + g * 8 + e]) : 0;
+        qf[ks] = __builtin_bit_cast(bf16x8v, v);
+    }
+
+    // staging: chunk c of a tile is key c % KT, dims (c / KT) * 8 .. + 7 (key-fastest, so the
+    // V^T stores of a wave spread over banks)
+    uint4 kreg[CPT], vreg[CPT];
+    auto load_tile = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + 256 * i;
+            const int key = c % KT, d8 = (c / KT) * 8;
+            const int kk = min(k0 + key, j1 - 1);          // clamped: masked below
+            kreg[i] = ld16(kbase + (size_t)kk * kv_row + d8);
+            vreg[i] = ld16(vbase + (size_t)kk * kv_row + d8);
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + 256 * i;
+            const int key = c % KT, d8 = (c / KT) * 8;
+            *reinterpret_cast<uint4*>(&Ks[buf][key][d8]) = kreg[i];
+            const uint32_t w[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                Vt[buf][d8 + 2 * q][key] = static_cast<uint16_t>(w[q] & 0xffffu);
+                Vt[buf][d8 + 2 * q + 1][key] = static_cast<uint16_t>(w[q] >> 16);
+            }
+        }
+    };
+
+    float m = -INFINITY, l = 0.f;       // online softmax of head fr over this wave's keys
+    f32x4v o[DT];
+#pragma unroll
+    for (int d = 0; d < DT; ++d) o[d] = f32x4v{0.f, 0.f, 0.f, 0.f};
+
+    const int n_tiles = (j1 - j0 + KT - 1) / KT;
+    if (n_tiles > 0) load_tile(j0);
+    for (int it = 0; it < n_tiles; ++it) {
+        const int buf = it & 1;
+        const int k0 = j0 + it * KT;
+        store_tile(buf);
+        __syncthreads();
+        if (it + 1 < n_tiles) load_tile(k0 + KT);     // in flight under this tile's products
+
+        // S^T for keys k0 + 16 wid + (4g + e), head fr
+        f32x4v st = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8v kf = *reinterpret_cast<const bf16x8v*>(&Ks[buf][16 * wid + fr][ks * 32 + g * 8]);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], st, 0, 0, 0);
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int key = k0 + 16 * wid + 4 * g + e;
+            st[e] = key < j1 ? st[e] * a.scale : -INFINITY;
+            tmax = fmaxf(tmax, st[e]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+        const float mn = fmaxf(m, tmax);
+        const float alpha = (mn == -INFINITY) ? 1.f : __expf(m - mn);
+        float psum = 0.f;
+        s16x4 phi, plo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float p = (mn == -INFINITY) ? 0.f : __expf(st[e] - mn);
+            psum += p;
+            const uint16_t hi = f32_to_bf16(p);
+            phi[e] = static_cast<short>(hi);
+            plo[e] = static_cast<short>(f32_to_bf16(p - bf16_to_f32(hi)));
+        }
+        psum += __shfl_xor(psum, 16, kWave);
+        psum += __shfl_xor(psum, 32, kWave);
+        l = l * alpha + psum;
+        m = mn;
+        // O^T[dims 16 d + 4 g + e][head fr] += V^T[dim][keys 16 wid + 4 g' + j] P^T
+#pragma unroll
+        for (int d = 0; d < DT; ++d) {
+            o[d] *= alpha;
+            const s16x4 vf = *reinterpret_cast<const s16x4*>(&Vt[buf][16 * d + fr][16 * wid + 4 * g]);
+            o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, phi, o[d], 0, 0, 0);
+            o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, plo, o[d], 0, 0, 0);
+        }
+    }
+
+    // merge the four waves: lane (fr, g) holds O^T[16 d + 4 g + e][fr]
+    __syncthreads();                                  // every wave is done with the last tile
+    if (g == 0) {
+        s_m[wid][fr] = m;
+        s_l[wid][fr] = l;
+    }
+#pragma unroll
+    for (int d = 0; d < DT; ++d)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_o[wid][16 * d + 4 * g + e][fr] = o[d][e];
+    __syncthreads();
+
+    for (int idx = tid; idx < NREP * HD; idx += 256) {
         const int r = idx / HD, d = idx - r * HD;
-        const int h = kvh * NREP + r;
-        const float* pp = a.part + ((size_t)t * a.n_heads + h) * a.n_split * (HD + 2);
-        float ms[kMaxSplitMerge], ls[kMaxSplitMerge], as[kMaxSplitMerge];
         float M = -INFINITY;
 #pragma unroll
-        for (int sp = 0; sp < kMaxSplitMerge; ++sp) {
-            if (sp < a.n_split) {
-                ms[sp] = ld_agent(pp + sp * (HD + 2) + HD);
-                ls[sp] = ld_agent(pp + sp * (HD + 2) + HD + 1);
-                as[sp] = ld_agent(pp + sp * (HD + 2) + d);
-                M = fmaxf(M, ms[sp]);
-            }
-        }
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][r]);
         float L = 0.f, A = 0.f;
+        if (M != -INFINITY) {
 #pragma unroll
-        for (int sp = 0; sp < kMaxSplitMerge; ++sp) {
-            if (sp < a.n_split && ms[sp] != -INFINITY) {
-                const float w = __expf(ms[sp] - M);
-                L += ls[sp] * w;
-                A += as[sp] * w;
+            for (int w = 0; w < 4; ++w) {
+                const float wt = __expf(s_m[w][r] - M);
+                L += s_l[w][r] * wt;
+                A += s_o[w][d][r] * wt;
             }
         }
-        const float o = A / L;
-        if (OUT_BF16)
-            static_cast<uint16_t*>(a.out)[a.out_frag_mt ? frag_index(t, h * HD + d, a.out_frag_mt)
-                                                        : (size_t)t * qstride + h * HD + d] = f32_to_bf16(o);
-        else
-            static_cast<float*>(a.out)[(size_t)t * qstride + h * HD + d] = o;
+        const int h = kvh * NREP + r;
+        if (a.n_split == 1) {
+            const float ov = A / L;
+            if (OUT_BF16)
+                static_cast<uint16_t*>(a.out)[a.out_frag_mt ? frag_index(t, h * HD + d, a.out_frag_mt)
+                                                            : (size_t)t * qstride + h * HD + d] = f32_to_bf16(ov);
+            else
+                static_cast<float*>(a.out)[(size_t)t * qstride + h * HD + d] = ov;
+        } else {
+            float* pp = a.part + (((size_t)t * a.n_heads + h) * a.n_split + split) * (HD + 2);
+            st_agent(pp + d, A);
+            if (d == 0) {
+                st_agent(pp + HD, M);
+                st_agent(pp + HD + 1, L);
+            }
+        }
     }
+    if (a.n_split == 1) return;
+    __shared__ int s_last;
+    int* counter = &a.counters[(size_t)t * a.n_kv_heads + kvh];
+    if (!arrive_last(counter, a.n_split, &s_last)) return;
+    merge_splits<HD, NREP, OUT_BF16>(a, t, kvh, tid, 256);
     if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -252,7 +457,15 @@ hipError_t launch4(const AttnArgs& args, hipStream_t s) {
         a.row0 = r0;
         const int n = min(kMaxZ, args.rows - r0);
         const dim3 grid(a.n_split, a.n_kv_heads, n);
-        if (a.seqlen == 1)
+        bool done = false;
+        if constexpr (NREP >= 4 && sizeof(KT) == 2) {
+            if (a.seqlen == 1) {
+                launch_kernel((attn_gqa_decode_kernel<HD, NREP, OB>), grid, dim3(256), 0, s, a);
+                done = true;
+            }
+        }
+        if (done) {
+        } else if (a.seqlen == 1)
             launch_kernel((attn_rows_kernel<KT, HD, NREP, OB, kDecodeWaves<NREP>>), grid,
                                dim3(64 * kDecodeWaves<NREP>), 0, s, a);
         else

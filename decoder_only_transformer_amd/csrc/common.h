@@ -86,6 +86,23 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// v from another lane of the same DPP row (16 lanes) as selected by a DPP control word.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over each DPP row of 16 lanes, in every lane of the row, on DPP moves (VALU) rather
+// than LDS permutes: pair swap, quad half swap, mirror within 8 lanes, mirror within 16.
+template <>
+__device__ __forceinline__ float group_sum<16>(float v) {
+    v += dpp_f32<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+    v += dpp_f32<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    v += dpp_f32<0x141>(v);   // row_half_mirror
+    v += dpp_f32<0x140>(v);   // row_mirror
+    return v;
+}
+
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
 // Device-coherent fp32 store / load: relaxed atomics at agent scope, which bypass the

@@ -210,7 +210,9 @@ QkvTarget qkv_target(const llama_ctx* c, int l, int start_pos, int seqlen, const
 // Key splits of a decode step of `rows` rows at context ctx.
 int decode_splits(const llama_ctx* c, int rows, int ctx) {
     const int n_rep = c->a.n_heads / c->a.n_kv_heads;
-    const int slots = 4 * (n_rep <= 2 ? 16 : 8);
+    // keys one workgroup takes in one round: 16-lane slots x 4 keys (vector kernel), or two
+    // 64-key tiles (MFMA kernel for bf16 GQA with n_rep >= 4)
+    const int slots = (c->bf16 && n_rep >= 4) ? 32 : 4 * (n_rep <= 2 ? 16 : 8);
     const int pairs = rows * c->a.n_kv_heads;
     const int want = (512 + pairs - 1) / pairs;
     const int by_len = (ctx + 4 * slots - 1) / (4 * slots);
