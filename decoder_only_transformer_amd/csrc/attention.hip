@@ -5,16 +5,14 @@
 // 16-lane group loads four keys' K and V rows before using any of them and keeps a running
 // (max, sum, acc) online softmax per head in fp32.  The sixteen groups are merged through
 // LDS.  With more than one split per row, every workgroup stores its partial (m, l, acc)
-// with device-coherent stores and the last one to arrive (per-row counter) merges all
-// splits in split order and resets the counter, so no second launch is needed and the
-// result is deterministic.
+// and a second, small launch combines the splits in split order (deterministic; the kernel
+// boundary makes the partials visible without any cross-workgroup synchronisation).
 #include "common.h"
 #include "kernels.h"
 
 namespace llk {
 namespace {
 
-constexpr int kMaxSplitMerge = 32;   // largest split count the in-kernel merge handles
 
 // N elements of a K or V row as raw bits (4, 8, 16 or 32 bytes), unpacked later so the
 // loads of several keys are in flight together.
@@ -73,43 +71,34 @@ __device__ __forceinline__ void merge_with_lane(float (&m)[NREP], float (&l)[NRE
     }
 }
 
-// Final output of (row t, kv head kvh) from the n_split partials (m, l, acc) of its splits,
-// merged in split order; partials are read device-coherently (they were stored that way by
-// other workgroups of this launch).
-template <int HD, int NREP, bool OUT_BF16>
-__device__ __forceinline__ void merge_splits(const AttnArgs& a, int t, int kvh, int tid, int nthreads) {
-    const int qstride = a.n_heads * HD;
-    for (int idx = tid; idx < NREP * HD; idx += nthreads) {
-        const int r = idx / HD, d = idx - r * HD;
-        const int h = kvh * NREP + r;
-        const float* pp = a.part + ((size_t)t * a.n_heads + h) * a.n_split * (HD + 2);
-        float ms[kMaxSplitMerge], ls[kMaxSplitMerge], as[kMaxSplitMerge];
-        float M = -INFINITY;
-#pragma unroll
-        for (int sp = 0; sp < kMaxSplitMerge; ++sp) {
-            if (sp < a.n_split) {
-                ms[sp] = ld_agent(pp + sp * (HD + 2) + HD);
-                ls[sp] = ld_agent(pp + sp * (HD + 2) + HD + 1);
-                as[sp] = ld_agent(pp + sp * (HD + 2) + d);
-                M = fmaxf(M, ms[sp]);
-            }
+// Second pass of a split launch: output (row t, head h, dim d) from the n_split partials
+// (m, l, acc) of its splits, combined in split order.  One workgroup per (row, head), one
+// thread per dim; the partials were written by the first pass with plain stores.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
+    const int t = a.row0 + blockIdx.y, h = blockIdx.x, d = threadIdx.x;
+    const int HD = a.head_dim;
+    if (d >= HD) return;
+    const float* pp = a.part + ((size_t)t * a.n_heads + h) * a.n_split * (HD + 2);
+    float M = -INFINITY;
+    for (int sp = 0; sp < a.n_split; ++sp) M = fmaxf(M, pp[sp * (HD + 2) + HD]);
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+        for (int sp = 0; sp < a.n_split; ++sp) {
+            const float m = pp[sp * (HD + 2) + HD];
+            if (m == -INFINITY) continue;
+            const float w = __expf(m - M);
+            L += pp[sp * (HD + 2) + HD + 1] * w;
+            A += pp[sp * (HD + 2) + d] * w;
         }
-        float L = 0.f, A = 0.f;
-#pragma unroll
-        for (int sp = 0; sp < kMaxSplitMerge; ++sp) {
-            if (sp < a.n_split && ms[sp] != -INFINITY) {
-                const float w = __expf(ms[sp] - M);
-                L += ls[sp] * w;
-                A += as[sp] * w;
-            }
-        }
-        const float o = A / L;
-        if (OUT_BF16)
-            static_cast<uint16_t*>(a.out)[a.out_frag_mt ? frag_index(t, h * HD + d, a.out_frag_mt)
-                                                        : (size_t)t * qstride + h * HD + d] = f32_to_bf16(o);
-        else
-            static_cast<float*>(a.out)[(size_t)t * qstride + h * HD + d] = o;
     }
+    const float o = A / L;
+    const size_t qstride = (size_t)a.n_heads * HD;
+    if (OUT_BF16)
+        static_cast<uint16_t*>(a.out)[a.out_frag_mt ? frag_index(t, h * HD + d, a.out_frag_mt)
+                                                    : (size_t)t * qstride + h * HD + d] = f32_to_bf16(o);
+    else
+        static_cast<float*>(a.out)[(size_t)t * qstride + h * HD + d] = o;
 }
 
 template <typename KT, int HD, int NREP, bool OUT_BF16, int WAVES>
@@ -230,22 +219,13 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(AttnArgs a) {
                 static_cast<float*>(a.out)[(size_t)t * qstride + h * HD + d] = o;
         } else {
             float* pp = a.part + (((size_t)t * a.n_heads + h) * a.n_split + split) * (HD + 2);
-            st_agent(pp + d, A);
+            pp[d] = A;
             if (d == 0) {
-                st_agent(pp + HD, M);
-                st_agent(pp + HD + 1, L);
+                pp[HD] = M;
+                pp[HD + 1] = L;
             }
         }
     }
-    if (a.n_split == 1) return;
-
-    // Last workgroup of this (row, kv head) to arrive merges the splits; the partials went
-    // out as device-coherent stores and are read back the same way.
-    __shared__ int s_last;
-    int* counter = &a.counters[(size_t)t * a.n_kv_heads + kvh];
-    if (!arrive_last(counter, a.n_split, &s_last)) return;
-    merge_splits<HD, NREP, OUT_BF16>(a, t, kvh, tid, blockDim.x);
-    if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -258,7 +238,7 @@ __global__ __launch_bounds__(64 * WAVES) void attn_rows_kernel(AttnArgs a) {
 // remainder (two MFMAs) to keep fp32-softmax accuracy.  K (row-major) and V^T tiles of 64
 // keys are staged in LDS, double-buffered, with one barrier per tile; each of the four waves
 // takes 16 keys of a tile and keeps its own online-softmax state, merged at the end through
-// LDS.  Splits merge as in the kernel above.
+// LDS.  Splits are combined by the merge pass.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
@@ -311,24 +291,26 @@ __global__ __launch_bounds__(256) void attn_gqa_decode_kernel(AttnArgs a) {
 
     // staging: chunk c of a tile is key c % KT, dims (c / KT) * 8 .. + 7 (key-fastest, so the
     // V^T stores of a wave spread over banks)
-    uint4 kreg[CPT], vreg[CPT];
-    auto load_tile = [&](int k0) {
+    // two tiles of loads in flight: register sets R = 0, 1 hold tiles it and it + 1 while
+    // tile it - 1 is computed
+    uint4 kreg[2][CPT], vreg[2][CPT];
+    auto load_tile = [&](int k0, int R) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = tid + 256 * i;
             const int key = c % KT, d8 = (c / KT) * 8;
             const int kk = min(k0 + key, j1 - 1);          // clamped: masked below
-            kreg[i] = ld16(kbase + (size_t)kk * kv_row + d8);
-            vreg[i] = ld16(vbase + (size_t)kk * kv_row + d8);
+            kreg[R][i] = ld16(kbase + (size_t)kk * kv_row + d8);
+            vreg[R][i] = ld16(vbase + (size_t)kk * kv_row + d8);
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf, int R) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = tid + 256 * i;
             const int key = c % KT, d8 = (c / KT) * 8;
-            *reinterpret_cast<uint4*>(&Ks[buf][key][d8]) = kreg[i];
-            const uint32_t w[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
+            *reinterpret_cast<uint4*>(&Ks[buf][key][d8]) = kreg[R][i];
+            const uint32_t w[4] = {vreg[R][i].x, vreg[R][i].y, vreg[R][i].z, vreg[R][i].w};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 Vt[buf][d8 + 2 * q][key] = static_cast<uint16_t>(w[q] & 0xffffu);
@@ -343,13 +325,13 @@ __global__ __launch_bounds__(256) void attn_gqa_decode_kernel(AttnArgs a) {
     for (int d = 0; d < DT; ++d) o[d] = f32x4v{0.f, 0.f, 0.f, 0.f};
 
     const int n_tiles = (j1 - j0 + KT - 1) / KT;
-    if (n_tiles > 0) load_tile(j0);
-    for (int it = 0; it < n_tiles; ++it) {
-        const int buf = it & 1;
+    if (n_tiles > 0) load_tile(j0, 0);
+    if (n_tiles > 1) load_tile(j0 + KT, 1);
+    auto tile_step = [&](int it, int buf) {   // buf = it & 1 = register set of tile it
         const int k0 = j0 + it * KT;
-        store_tile(buf);
+        store_tile(buf, buf);
         __syncthreads();
-        if (it + 1 < n_tiles) load_tile(k0 + KT);     // in flight under this tile's products
+        if (it + 2 < n_tiles) load_tile(k0 + 2 * KT, buf);   // in flight under two tiles' products
 
         // S^T for keys k0 + 16 wid + (4g + e), head fr
         f32x4v st = f32x4v{0.f, 0.f, 0.f, 0.f};
@@ -391,6 +373,10 @@ __global__ __launch_bounds__(256) void attn_gqa_decode_kernel(AttnArgs a) {
             o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, phi, o[d], 0, 0, 0);
             o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, plo, o[d], 0, 0, 0);
         }
+    };
+    for (int it = 0; it < n_tiles; it += 2) {
+        tile_step(it, 0);
+        if (it + 1 < n_tiles) tile_step(it + 1, 1);
     }
 
     // merge the four waves: lane (fr, g) holds O^T[16 d + 4 g + e][fr]
@@ -429,19 +415,13 @@ __global__ __launch_bounds__(256) void attn_gqa_decode_kernel(AttnArgs a) {
                 static_cast<float*>(a.out)[(size_t)t * qstride + h * HD + d] = ov;
         } else {
             float* pp = a.part + (((size_t)t * a.n_heads + h) * a.n_split + split) * (HD + 2);
-            st_agent(pp + d, A);
+            pp[d] = A;
             if (d == 0) {
-                st_agent(pp + HD, M);
-                st_agent(pp + HD + 1, L);
+                pp[HD] = M;
+                pp[HD + 1] = L;
             }
         }
     }
-    if (a.n_split == 1) return;
-    __shared__ int s_last;
-    int* counter = &a.counters[(size_t)t * a.n_kv_heads + kvh];
-    if (!arrive_last(counter, a.n_split, &s_last)) return;
-    merge_splits<HD, NREP, OUT_BF16>(a, t, kvh, tid, 256);
-    if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Waves per workgroup: many for single-token rows (decode: one workgroup covers a short
@@ -470,8 +450,13 @@ hipError_t launch4(const AttnArgs& args, hipStream_t s) {
                                dim3(64 * kDecodeWaves<NREP>), 0, s, a);
         else
             launch_kernel((attn_rows_kernel<KT, HD, NREP, OB, 4>), grid, dim3(256), 0, s, a);
-        const hipError_t e = hipGetLastError();
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (a.n_split > 1) {
+            launch_kernel((attn_merge_kernel<OB>), dim3(a.n_heads, n), dim3(128), 0, s, a);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     return hipSuccess;
 }

@@ -105,29 +105,6 @@ __device__ __forceinline__ float group_sum<16>(float v) {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
-// Device-coherent fp32 store / load: relaxed atomics at agent scope, which bypass the
-// XCD-private L2, so partial results can be handed between workgroups of one launch
-// without a fence that writes back or invalidates a whole L2.
-__device__ __forceinline__ void st_agent(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_agent(const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Arrival count of a split: every lane's device-coherent stores issued so far have
-// completed (vmcnt 0), the workgroup has synchronised, then one relaxed agent-scope add.
-// Returns true in the workgroup that arrives last.
-__device__ __forceinline__ bool arrive_last(int* counter, int n, int* s_flag) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *s_flag = (old == n - 1);
-    }
-    __syncthreads();
-    return *s_flag != 0;
-}
 
 // Fragment-major position of element (m, k) of a bf16 activation matrix kept as mt tiles of
 // 16 rows: the 16 x 32 block (row tile m / 16, k-step k / 32) is 1 KB laid out in the lane

@@ -107,7 +107,6 @@ struct AttnArgs {
     int out_bf16;
     int out_frag_mt;       // bf16 out: > 0 writes it fragment-major for that many row tiles
     float* part;           // [rows][n_heads][n_split][hd + 2] partials when n_split > 1
-    int* counters;         // [rows][n_kv_heads] arrival counters (zero between launches)
     int rows, n_heads, n_kv_heads, head_dim, max_seq;
     int row0;              // first row of this launch (launches are split at 65535 rows)
     int start_pos, seqlen; // row t -> b = t / seqlen, position start_pos + t % seqlen

@@ -38,7 +38,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t k_cache, v_cache, rope, h32, q32, o32, g32, act16, g16, part, counters, splitk, qkv32, step, total;
+    size_t k_cache, v_cache, rope, h32, q32, o32, g32, act16, g16, part, splitk, qkv32, step, total;
     size_t kv_layer_elems;   // elements of one layer's K (or V) cache
 };
 
@@ -94,7 +94,6 @@ Layout layout_of(const llama_args& a) {
     L.act16 = fp32 ? off : take(rows16 * (size_t)(a.dim > (int)nq ? a.dim : (int)nq) * 2);
     L.g16 = fp32 ? off : take(rows16 * (size_t)a.hidden_dim * 2);
     L.part = take(maxB * (size_t)a.n_heads * kMaxSplit * (hd + 2) * sizeof(float));
-    L.counters = take(maxB * (size_t)a.n_kv_heads * sizeof(int));
     // split-K partials of the residual GEMMs, used while a prefill has at most kSplitKRows rows
     L.splitk = fp32 ? off : take((size_t)kMaxSplitK * std::min(maxT, (size_t)kSplitKRows) * a.dim * sizeof(float));
     // fp32 [wq;wk;wv] projections of long prefills (RoPE and bf16 storage in a second pass)
@@ -212,9 +211,12 @@ int decode_splits(const llama_ctx* c, int rows, int ctx) {
     const int n_rep = c->a.n_heads / c->a.n_kv_heads;
     // keys one workgroup takes in one round: 16-lane slots x 4 keys (vector kernel), or two
     // 64-key tiles (MFMA kernel for bf16 GQA with n_rep >= 4)
-    const int slots = (c->bf16 && n_rep >= 4) ? 32 : 4 * (n_rep <= 2 ? 16 : 8);
+    const bool mfma = c->bf16 && n_rep >= 4;
+    const int slots = mfma ? 32 : 4 * (n_rep <= 2 ? 16 : 8);
     const int pairs = rows * c->a.n_kv_heads;
-    const int want = (512 + pairs - 1) / pairs;
+    // workgroups wanted: about one per CU for the MFMA kernel (more splits cost more in
+    // per-workgroup start-up than they gain), two per CU for the vector kernel
+    const int want = ((mfma ? 256 : 512) + pairs - 1) / pairs;
     const int by_len = (ctx + 4 * slots - 1) / (4 * slots);
     return std::max(1, std::min(kMaxSplit, std::min(want, by_len)));
 }
@@ -230,7 +232,6 @@ llama_status run_attention(const llama_ctx* c, int l, int rows, int seqlen, int 
     at.out_bf16 = out_bf16 ? 1 : 0;
     at.out_frag_mt = out_frag_mt;
     at.part = c->at<float>(c->L.part);
-    at.counters = c->at<int>(c->L.counters);
     at.rows = rows;
     at.n_heads = c->a.n_heads;
     at.n_kv_heads = c->a.n_kv_heads;
@@ -483,7 +484,6 @@ llama_status llama_init(const llama_args* a, const llama_weights* w, void* d_wor
         }
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (hipMemcpyAsync(c->ws + L.rope, tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice, s) != hipSuccess ||
-        hipMemsetAsync(c->ws + L.counters, 0, (size_t)a->max_batch_size * a->n_kv_heads * sizeof(int), s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess) {
         delete c;
         return LLAMA_ERR_HIP;
