@@ -233,15 +233,35 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs a, int n_
     epilogue<BN, WGN, TM, TN, EPI>(a, acc, m0, tile_n, wm, wn, lane);
 }
 
-// resid[m][n] += sum over splits of part[z][m][n], in split order.
-__global__ void splitk_reduce_kernel(const float* part, int splits, int M, int N, float* resid,
-                                     int64_t ldr) {
+// resid[m][n] += sum over splits of part[z][m][n] (rows ldp apart), in split order.
+__global__ void splitk_reduce_kernel(const float* part, int splits, int M, int N, int64_t ldp,
+                                     float* resid, int64_t ldr) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (size_t)M * N) return;
     const int m = (int)(i / N), n = (int)(i - (size_t)m * N);
     float v = 0.f;
-    for (int z = 0; z < splits; ++z) v += part[(size_t)z * M * N + i];
+    for (int z = 0; z < splits; ++z) v += part[((size_t)z * M + m) * ldp + n];
     resid[(size_t)m * ldr + n] += v;
+}
+
+// SiLU gate from split partials of the [w1; w3] product: unit u of row m has its gate in
+// B row p and its up projection in B row p + half, where (tile, wave column, offset) of u
+// give p (the interleaving the MFMA kernels load w1 and w3 rows in).
+__global__ void swiglu_reduce_kernel(const float* part, int splits, int M, int N, int64_t ldp,
+                                     int bn, int wn_cols, uint16_t* out, int64_t ldo) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)M * N) return;
+    const int m = (int)(i / N), u = (int)(i - (size_t)m * N);
+    const int half = wn_cols / 2;
+    const int tile = u / (bn / 2), r = u % (bn / 2);
+    const int p = tile * bn + (r / half) * wn_cols + r % half;
+    float g = 0.f, v = 0.f;
+    for (int z = 0; z < splits; ++z) {
+        const float* row = part + ((size_t)z * M + m) * ldp;
+        g += row[p];
+        v += row[p + half];
+    }
+    out[(size_t)m * ldo + u] = f32_to_bf16(silu(g) * v);
 }
 
 template <int BM, int BN, int WGM, int WGN, int EPI>
@@ -256,42 +276,46 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     if (e != hipSuccess || splits == 1) return e;
     const size_t n = (size_t)a.M * a.N;
     launch_kernel(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       a.part, splits, a.M, a.N, a.resid, a.ldr);
+                  a.part, splits, a.M, a.N, (int64_t)a.N, a.resid, a.ldr);
     return hipGetLastError();
 }
 
 
 // ---------------------------------------------------------------------------------------
-// Large-M variant: 256x256 tiles, 8 waves (4 x 2, 64 x 128 each), K in stages of 32 through
-// a 4-deep LDS ring filled by global_load_lds_dwordx4 (global -> LDS without registers),
-// loads issued 3 stages ahead.  A wave's load instruction fills 1 KB of LDS contiguously
+// LDS-ring variant: BM x 256 tiles (BM = 256: 8 waves as 4 x 2 of 64 x 128; BM = 128: 8 waves
+// as 2 x 4 of 64 x 64), K in stages of 32 through a 4-deep LDS ring filled by
+// global_load_lds_dwordx4 (global -> LDS without registers), loads issued 3 stages ahead.
+// Long prefills use it as is; short ones (a few hundred rows, where the weights are the
+// traffic) split K over gridDim.z so enough workgroups stream the weights: each split
+// stores its raw fp32 tile [z][M][B row] and a reduce pass applies the epilogue.  A wave's load instruction fills 1 KB of LDS contiguously
 // (lane i -> bytes 16i..16i+15), i.e. 16 rows x 4 chunks of a 64-byte row; each lane fetches
 // the global chunk (chunk ^ swz(row)), so a fragment read of (row, chunk) finds it at slot
 // chunk ^ swz(row) and the 16 rows of a fragment land on distinct banks without padding.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-constexpr int kBigBM = 256, kBigBN = 256, kBigBK = 32, kBigStages = 4;
+constexpr int kBigBN = 256, kBigBK = 32;
 
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
-// One LDS ring slot: a distinct object per stage, so the compiler can tell a fragment read
-// of one stage from the DMA writes into another and keeps the later stages in flight.
-#define LLK_BIG_SLOT(n)                                                                 \
-    __shared__ __attribute__((aligned(1024))) uint16_t As##n[kBigBM * kBigBK];         \
-    __shared__ __attribute__((aligned(1024))) uint16_t Bs##n[kBigBN * kBigBK];
+// Tile shapes: wave grid, accumulator tiles per wave, LDS ring slots (NS - 1 stages of
+// loads in flight).  The 128-row tile is for short prefills, where the weights are the
+// traffic: its smaller A tile leaves room for a deeper ring.
+template <int BM> struct BigShape;
+template <> struct BigShape<256> { static constexpr int WGN = 2, TN = 8, NS = 4; };   // 4 x 2 waves of 64 x 128; 128 KB
+template <> struct BigShape<128> { static constexpr int WGN = 4, TN = 4, NS = 6; };   // 2 x 4 waves of 64 x 64; 144 KB
 
-template <int EPI>
+template <int BM, int EPI>
 __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int n_tn) {
-    constexpr int BM = kBigBM, BN = kBigBN, BKS = kBigBK;
-    constexpr int WGN = 2, TM = 4, TN = 8, WM = 64, WN = 128;
-    static_assert(kBigStages == 4, "the ring below has four slots");
-    LLK_BIG_SLOT(0)
-    LLK_BIG_SLOT(1)
-    LLK_BIG_SLOT(2)
-    LLK_BIG_SLOT(3)
-    uint16_t* const Aslot[4] = {As0, As1, As2, As3};
-    uint16_t* const Bslot[4] = {Bs0, Bs1, Bs2, Bs3};
+    constexpr int BN = kBigBN, BKS = kBigBK;
+    constexpr int WGN = BigShape<BM>::WGN, TM = 4, TN = BigShape<BM>::TN, WM = 64, WN = BN / WGN;
+    constexpr int A_INS = BM / 128, B_INS = BN / 128;    // 16-row load instructions per wave
+    constexpr int NS = BigShape<BM>::NS;
+    constexpr int kWait = (NS - 2) * (A_INS + B_INS);    // loads of the later stages in flight
+    constexpr int kSlot = (BM + BN) * BKS;                 // elements of one ring slot (A then B)
+    // The fragment reads are asm blocks that wait for their own results, so the compiler
+    // sees no LDS read it would have to order after the ring's DMA writes.
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[NS * kSlot];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wm = wid / WGN, wn = wid % WGN;
@@ -299,15 +323,21 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
     if (!tile_of(blockIdx.x, n_tm, n_tn, tile_m, tile_n)) return;
     const int m0 = tile_m * BM;
 
-    // This lane's two A rows and two B rows (one per load instruction of the wave).
-    const uint16_t* ap[2];
-    const uint16_t* bp[2];
+    // This lane's A rows and B rows (one per load instruction of the wave: rows
+    // (INS * wid + i) * 16 + lane / 4 of the tile).
+    const uint16_t* ap[A_INS];
+    const uint16_t* bp[B_INS];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = (2 * wid + i) * 16 + (lane >> 2);
+    for (int i = 0; i < A_INS; ++i) {
+        const int row = (A_INS * wid + i) * 16 + (lane >> 2);
         const int gc = (lane & 3) ^ swz(row);
         const int gm = min(m0 + row, a.M - 1);
         ap[i] = static_cast<const uint16_t*>(a.a) + (size_t)gm * a.lda + gc * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < B_INS; ++i) {
+        const int row = (B_INS * wid + i) * 16 + (lane >> 2);
+        const int gc = (lane & 3) ^ swz(row);
         bool ok = true;
         bp[i] = b_row_ptr<BN, WGN, EPI>(a, tile_n, row, ok) + gc * 8;
     }
@@ -336,12 +366,13 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
 
     auto issue = [&](int kt, uint16_t* Ad, uint16_t* Bd) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < A_INS; ++i)
             __builtin_amdgcn_global_load_lds((gbl_void_t*)(ap[i] + (size_t)kt * BKS),
-                                             (lds_void_t*)(Ad + (2 * wid + i) * 16 * BKS), 16, 0, 0);
+                                             (lds_void_t*)(Ad + (A_INS * wid + i) * 16 * BKS), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < B_INS; ++i)
             __builtin_amdgcn_global_load_lds((gbl_void_t*)(bp[i] + (size_t)kt * BKS),
-                                             (lds_void_t*)(Bd + (2 * wid + i) * 16 * BKS), 16, 0, 0);
-        }
+                                             (lds_void_t*)(Bd + (B_INS * wid + i) * 16 * BKS), 16, 0, 0);
     };
     auto compute = [&](const uint16_t* As_, const uint16_t* Bs_) {
         // Fragment reads go out in asm blocks that wait for their own results: the compiler
@@ -387,63 +418,104 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
         }
     };
 
-    // Prologue: stages 0..2 (past the end: duplicates of the last stage, so every step has
+    // Prologue: stages 0..NS-2 (past the end: duplicates of the last stage, so every step has
     // the same number of loads outstanding).
-    issue(min(kt0 + 0, kt1 - 1), As0, Bs0);
-    issue(min(kt0 + 1, kt1 - 1), As1, Bs1);
-    issue(min(kt0 + 2, kt1 - 1), As2, Bs2);
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i) issue(min(kt0 + i, kt1 - 1), ring + i * kSlot, ring + i * kSlot + BM * BKS);
 
-    // Step for stage kt held in slot S: wait for this wave's loads of that stage (the 8
-    // loads of the two later stages may stay in flight) and for its LDS reads of the
-    // previous slot, barrier (now every wave's are done), refill the previous slot with
-    // stage kt+3, compute.
-#define LLK_BIG_STEP(S, PREV)                                                     \
-    if (kt + S < kt1) {                                                           \
-        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");  \
-        issue(min(kt + S + 3, kt1 - 1), As##PREV, Bs##PREV);                      \
-        compute(As##S, Bs##S);                                                    \
+    // Step for stage kt held in slot S: wait for this wave's loads of that stage (those of the
+    // NS - 2 later stages may stay in flight) and for its LDS reads of the previous slot,
+    // barrier (now every wave's are done), refill the previous slot with stage kt + NS - 1,
+    // compute.
+    for (int kt = kt0; kt < kt1; kt += NS) {
+#pragma unroll
+        for (int S = 0; S < NS; ++S) {
+            if (kt + S < kt1) {
+                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kWait) : "memory");
+                uint16_t* prev = ring + ((S + NS - 1) % NS) * kSlot;
+                issue(min(kt + S + NS - 1, kt1 - 1), prev, prev + BM * BKS);
+                compute(ring + S * kSlot, ring + S * kSlot + BM * BKS);
+            }
+        }
     }
-    for (int kt = kt0; kt < kt1; kt += 4) {
-        LLK_BIG_STEP(0, 3)
-        LLK_BIG_STEP(1, 0)
-        LLK_BIG_STEP(2, 1)
-        LLK_BIG_STEP(3, 2)
-    }
-#undef LLK_BIG_STEP
-    (void)Aslot;
-    (void)Bslot;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the duplicate tail loads
+    if (gridDim.z > 1) {
+        // split K: raw fp32 tile of this split, [z][M][B row] with B rows n_tn * BN wide
+        const int fr = lane & 15, rq = (lane >> 4) * 4;
+        const size_t ldp = (size_t)n_tn * BN;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int p = tile_n * BN + wn * WN + j * 16 + fr;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = m0 + wm * WM + i * 16 + rq + e;
+                    if (m < a.M) a.part[((size_t)blockIdx.z * a.M + m) * ldp + p] = acc[i][j][e];
+                }
+            }
+        return;
+    }
     epilogue<BN, WGN, TM, TN, EPI>(a, acc, m0, tile_n, wm, wn, lane);
 }
-#undef LLK_BIG_SLOT
 
-template <int EPI>
+// K splits for a short prefill (M <= kShortRows) on the LDS-ring kernel: about one
+// workgroup per CU, at least 8 k-stages per split, partials within the workspace.
+constexpr int kShortRows = 512;
+
+template <int BM, int EPI>
 hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
     const int ncols = (EPI == EPI_SWIGLU) ? kBigBN / 2 : kBigBN;
-    const int splits = (EPI == EPI_RESID && a.part) ? std::max(1, a.splits) : 1;
-    const int n_tn = (a.N + ncols - 1) / ncols, n_tm = (a.M + kBigBM - 1) / kBigBM;
+    const int n_tn = (a.N + ncols - 1) / ncols, n_tm = (a.M + BM - 1) / BM;
     const int per_xcd = (n_tn * n_tm + kXcds - 1) / kXcds;
-    launch_kernel((gemm_big_kernel<EPI>), dim3(per_xcd * kXcds, 1, splits), dim3(512), 0, s, a,
-                       n_tm, n_tn);
+    const size_t ldp = (size_t)n_tn * kBigBN;
+    int splits = 1;
+    if (a.M <= kShortRows && a.part && (EPI == EPI_QKV || EPI == EPI_RESID || EPI == EPI_SWIGLU)) {
+        // one workgroup per CU (its LDS ring takes most of the CU), all in one round
+        const int tiles = n_tn * n_tm;
+        splits = std::max(1, 256 / tiles);
+        splits = std::min(splits, std::max(1, a.K / kBigBK / 8));
+        splits = std::min(splits, kMaxBigSplit);
+        while (splits > 1 && (size_t)splits * a.M * ldp > a.part_cap) --splits;
+    }
+    launch_kernel((gemm_big_kernel<BM, EPI>), dim3(per_xcd * kXcds, 1, splits), dim3(512), 0, s, a,
+                  n_tm, n_tn);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     const size_t n = (size_t)a.M * a.N;
-    launch_kernel(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       a.part, splits, a.M, a.N, a.resid, a.ldr);
+    const dim3 rgrid((unsigned)((n + 255) / 256));
+    if constexpr (EPI == EPI_RESID) {
+        launch_kernel(splitk_reduce_kernel, rgrid, dim3(256), 0, s, a.part, splits, a.M, a.N,
+                      (int64_t)ldp, a.resid, a.ldr);
+    } else if constexpr (EPI == EPI_SWIGLU) {
+        launch_kernel(swiglu_reduce_kernel, rgrid, dim3(256), 0, s, a.part, splits, a.M, a.N,
+                      (int64_t)ldp, kBigBN, kBigBN / BigShape<BM>::WGN, static_cast<uint16_t*>(a.out16),
+                      a.ldo16);
+    } else {
+        return launch_rope_scatter_parts(a.part, splits, (int64_t)ldp, a.M, a.qkv, s);
+    }
     return hipGetLastError();
 }
 
 template <int EPI>
 hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
-    // Small M (short prefill): narrower tiles so enough workgroups stream the weights.
+    // Small M: narrow register-staged tiles.
     if (a.M <= 64) return launch_tile<64, 64, 2, 2, EPI>(a, s);
+    // Short prefills: the weights are the traffic; the LDS-ring kernel with K split so about
+    // one workgroup per CU streams them, the epilogue applied by a reduce pass.
+    if constexpr (EPI == EPI_QKV || EPI == EPI_RESID || EPI == EPI_SWIGLU) {
+        if (a.M <= kShortRows && a.part) {
+            if (a.M <= 128) return launch_big<128, EPI>(a, s);
+            return launch_big<256, EPI>(a, s);
+        }
+    }
     if (a.M <= 256) return launch_tile<128, 64, 2, 2, EPI>(a, s);
     // (the RoPE/KV-append epilogue does not fit 256x256 tiles without spilling)
     if constexpr (EPI == EPI_QKV) {
         return launch_tile<128, 128, 2, 2, EPI>(a, s);
     } else {
         if (a.M <= 2048) return launch_tile<128, 128, 2, 2, EPI>(a, s);
-        return launch_big<EPI>(a, s);
+        return launch_big<256, EPI>(a, s);
     }
 }
 

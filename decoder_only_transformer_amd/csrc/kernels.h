@@ -80,9 +80,12 @@ struct GemmArgs {
     void* out16; int64_t ldo16;    // SWIGLU (bf16)
     float* resid; int64_t ldr;
     QkvTarget qkv;
-    int splits;            // K splits (RESID only): partials [splits][M][N] -> `part`, then reduced
-    float* part;
+    int splits;            // K splits of the small-tile residual GEMM: partials [splits][M][N]
+    float* part;           // split-K partials (also used by short prefills on the LDS-ring kernel)
+    size_t part_cap;       // floats available at `part`
 };
+
+constexpr int kMaxBigSplit = 16;
 
 // y = x W^T for M <= 32 rows on bf16 MFMA (decode with batch > 4).  x is bf16 in
 // fragment-major order for MT = ceil(M / 16) row tiles (frag_index).
@@ -128,6 +131,9 @@ struct FlashArgs {
 
 hipError_t launch_flash_prefill(const FlashArgs& a, hipStream_t s);
 hipError_t launch_rope_scatter(const float* y, int T, const QkvTarget& t, hipStream_t s);
+// Same from the sum of `splits` partial projections [splits][T][ldy] (in split order).
+hipError_t launch_rope_scatter_parts(const float* y, int splits, int64_t ldy, int T, const QkvTarget& t,
+                                     hipStream_t s);
 hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, const void* table,
                         int wbf16, int vocab, int dim, float* h, const StepState* st, hipStream_t s);
 hipError_t launch_set_step(StepState* st, int pos, int64_t ld, const int32_t* tokens, float* logits,

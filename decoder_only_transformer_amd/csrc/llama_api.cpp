@@ -31,6 +31,7 @@ namespace {
 constexpr int kMaxSplit = 32;
 constexpr int kMaxSplitK = 8;      // K splits of a residual GEMM at small prefill sizes
 constexpr int kSplitKRows = 512;   // prefill rows up to which split-K is considered
+constexpr size_t kSplitKRowsCap = 2048;  // splits x rows the split-K workspace holds
 constexpr int kPlainQkvRows = 2048; // above this many prefill rows the QKV GEMM stores plainly
 constexpr int kSkinnyRows = 4;      // bf16 decode batches above this use the skinny MFMA kernel
 constexpr size_t kAlign = 256;
@@ -39,6 +40,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
     size_t k_cache, v_cache, rope, h32, q32, o32, g32, act16, g16, part, splitk, qkv32, step, total;
+    size_t splitk_floats;
     size_t kv_layer_elems;   // elements of one layer's K (or V) cache
 };
 
@@ -63,6 +65,15 @@ llama_status check_args(const llama_args* a) {
     if (a->vocab_size % 2 != 0) return LLAMA_ERR_UNSUPPORTED;
     if (a->max_seq_len > 65536) return LLAMA_ERR_UNSUPPORTED;
     return LLAMA_OK;
+}
+
+// Widest B-row space of a prefill GEMM on the LDS-ring kernel (256-column tiles; the [w1;w3]
+// product interleaves both matrices, so 2 * hidden_dim).
+size_t splitk_cols(const llama_args& a) {
+    const size_t hd = head_dim_of(a);
+    const size_t widest = std::max({(size_t)a.n_heads * hd + 2 * (size_t)a.n_kv_heads * hd,
+                                    2 * (size_t)a.hidden_dim, (size_t)a.dim});
+    return (widest + 255) / 256 * 256;
 }
 
 Layout layout_of(const llama_args& a) {
@@ -95,7 +106,11 @@ Layout layout_of(const llama_args& a) {
     L.g16 = fp32 ? off : take(rows16 * (size_t)a.hidden_dim * 2);
     L.part = take(maxB * (size_t)a.n_heads * kMaxSplit * (hd + 2) * sizeof(float));
     // split-K partials of the residual GEMMs, used while a prefill has at most kSplitKRows rows
-    L.splitk = fp32 ? off : take((size_t)kMaxSplitK * std::min(maxT, (size_t)kSplitKRows) * a.dim * sizeof(float));
+    // split-K partials: small-tile residual GEMMs (kMaxSplitK x 512 rows x dim) and short
+    // prefills on the LDS-ring kernel (splits x rows x B rows, capped at kSplitKRowsCap rows)
+    L.splitk_floats = fp32 ? 0 : std::max((size_t)kMaxSplitK * std::min(maxT, (size_t)kSplitKRows) * a.dim,
+                                          kSplitKRowsCap * splitk_cols(a));
+    L.splitk = fp32 ? off : take(L.splitk_floats * sizeof(float));
     // fp32 [wq;wk;wv] projections of long prefills (RoPE and bf16 storage in a second pass)
     L.qkv32 = (fp32 || maxT <= (size_t)kPlainQkvRows) ? off : take(maxT * (nq + 2 * (size_t)a.n_kv_heads * hd) * sizeof(float));
     L.step = take(sizeof(StepState));
@@ -370,6 +385,7 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
         LAUNCH(c, LLAMA_KC_GEMM_QKV, s, launch_gemm(EPI_STORE_QKV, g, s));
         LAUNCH(c, LLAMA_KC_GEMM_QKV, s, launch_rope_scatter(g.out, T, g.qkv, s));
     } else {
+        g.part = c->at<float>(c->L.splitk); g.part_cap = c->L.splitk_floats;
         LAUNCH(c, LLAMA_KC_GEMM_QKV, s, launch_gemm(EPI_QKV, g, s));
     }
 
@@ -396,19 +412,20 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
     g = GemmArgs{};
     g.a = act; g.lda = c->nq; g.M = T; g.K = c->nq; g.N = D;
     g.w0 = W.wo; g.resid = h; g.ldr = D;
-    g.splits = residual_splits(c, T, c->nq); g.part = c->at<float>(c->L.splitk);
+    g.splits = residual_splits(c, T, c->nq); g.part = c->at<float>(c->L.splitk); g.part_cap = c->L.splitk_floats;
     LAUNCH(c, LLAMA_KC_GEMM_WO, s, launch_gemm(EPI_RESID, g, s));
 
     LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.ffn_norm, c->a.norm_eps, act, D, 0, s));
     g = GemmArgs{};
     g.a = act; g.lda = D; g.M = T; g.K = D; g.N = F;
     g.w0 = W.w1; g.w1 = W.w3; g.out16 = g16; g.ldo16 = F;
+    g.part = c->at<float>(c->L.splitk); g.part_cap = c->L.splitk_floats;
     LAUNCH(c, LLAMA_KC_GEMM_W13, s, launch_gemm(EPI_SWIGLU, g, s));
 
     g = GemmArgs{};
     g.a = g16; g.lda = F; g.M = T; g.K = F; g.N = D;
     g.w0 = W.w2; g.resid = h; g.ldr = D;
-    g.splits = residual_splits(c, T, F); g.part = c->at<float>(c->L.splitk);
+    g.splits = residual_splits(c, T, F); g.part = c->at<float>(c->L.splitk); g.part_cap = c->L.splitk_floats;
     LAUNCH(c, LLAMA_KC_GEMM_W2, s, launch_gemm(EPI_RESID, g, s));
     return LLAMA_OK;
 }

@@ -119,14 +119,18 @@ __global__ void select_kernel(const int32_t* next, int32_t* tokens, int64_t ld, 
 
 // RoPE + bf16 storage of q and the K/V cache append from fp32 projections y [T][nq+2nk]
 // (used when the [wq;wk;wv] GEMM stores plainly).  One thread per (row, pair).
-__global__ void rope_scatter_kernel(const float* y, int T, QkvTarget t) {
+__global__ void rope_scatter_kernel(const float* y, int splits, int64_t ldy, int T, QkvTarget t) {
     const int npairs = (t.nq + 2 * t.nk) / 2;
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (size_t)T * npairs) return;
     const int m = (int)(i / npairs);
     const int n0 = 2 * (int)(i - (size_t)m * npairs);
-    const float2 v = *reinterpret_cast<const float2*>(y + (size_t)m * (t.nq + 2 * t.nk) + n0);
-    float y0 = v.x, y1 = v.y;
+    float y0 = 0.f, y1 = 0.f;
+    for (int z = 0; z < splits; ++z) {     // partial projections, summed in split order
+        const float2 v = *reinterpret_cast<const float2*>(y + ((size_t)z * T + m) * ldy + n0);
+        y0 += v.x;
+        y1 += v.y;
+    }
     const int b = m / t.seqlen;
     const int pos = t.start_pos + (m - b * t.seqlen);
     if (n0 < t.nq + t.nk) {
@@ -148,10 +152,16 @@ __global__ void rope_scatter_kernel(const float* y, int T, QkvTarget t) {
 
 }  // namespace
 
-hipError_t launch_rope_scatter(const float* y, int T, const QkvTarget& t, hipStream_t s) {
+hipError_t launch_rope_scatter_parts(const float* y, int splits, int64_t ldy, int T, const QkvTarget& t,
+                                     hipStream_t s) {
     const size_t n = (size_t)T * ((t.nq + 2 * t.nk) / 2);
-    launch_kernel(rope_scatter_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, T, t);
+    launch_kernel(rope_scatter_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, splits,
+                  ldy, T, t);
     return hipGetLastError();
+}
+
+hipError_t launch_rope_scatter(const float* y, int T, const QkvTarget& t, hipStream_t s) {
+    return launch_rope_scatter_parts(y, 1, (int64_t)(t.nq + 2 * t.nk), T, t, s);
 }
 
 hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, const void* table,
