@@ -3,7 +3,8 @@
 // A workgroup owns one batch row, one kv head and 64 query rows, a query row being a
 // (position, head) pair of the n_rep heads that read this kv head (GQA is never
 // materialised: the K/V tile in LDS serves all of them).  Four waves own 16 rows each.
-// K/V advance in tiles of 64 keys up to the last position any row of the workgroup sees.
+// K/V advance in tiles of 64 keys up to the last position any row of the workgroup sees; the
+// next tile's loads are in flight while the current tile is computed.
 //
 //  S^T = K Q^T    keys are the MFMA M dimension, so after the product each lane holds
 //                 4 consecutive keys of one query; per-query max and sum need only two
@@ -26,6 +27,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kRows = 64;     // query rows per workgroup
+
+// Position of key `key` (0..63) of a tile in a V^T row: each 32-key half is stored in the
+// permuted k order of the O^T product, so lane group g's 8 keys {4g..4g+3, 16+4g..16+4g+3}
+// are one contiguous 16-byte read.
+__device__ __forceinline__ int vt_pos(int key) {
+    const int half = key & ~31, r = key & 31;
+    return half + ((r & 15) >> 2) * 8 + (r >> 4) * 4 + (r & 3);
+}
 constexpr int kKeys = 64;     // keys per tile
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u16x8_t v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -36,12 +45,25 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
     constexpr int DT = HD / 16;            // 16-row tiles of head_dim in O^T
     constexpr int KLD = HD + 8;            // padded K row (elements)
     constexpr int VLD = kKeys + 8;         // padded V^T row (elements)
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[kKeys][KLD];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[HD][VLD];
+    constexpr int CH = HD / 8;                   // 16-byte chunks per key row
+    constexpr int CPT = kKeys * CH / 256;        // chunks per thread per tile
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKeys][KLD];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][HD][VLD];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int fr = lane & 15, g = lane >> 4;
-    const int qtile = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    // Workgroup -> (batch row, kv head, query tile).  The dispatcher deals workgroup ids
+    // round-robin over the 8 XCDs; ids are mapped so each XCD gets a contiguous run of
+    // (pair, tile), i.e. all query tiles of a (row, kv head) pair run on one XCD and share its
+    // K/V through that XCD's L2.  Within a pair the longest tiles (most keys) go first.
+    const int n_qt = (a.seqlen * (a.n_heads / a.n_kv_heads) + kRows - 1) / kRows;
+    const int total = n_qt * a.n_kv_heads * a.bsz;
+    const int per_xcd = (total + 7) / 8;
+    const int lin = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if (lin >= total) return;
+    const int pair = lin / n_qt;
+    const int qtile = n_qt - 1 - (lin - pair * n_qt);
+    const int kvh = pair % a.n_kv_heads, b = pair / a.n_kv_heads;
     const int n_rep = a.n_heads / a.n_kv_heads;
     const int qstride = a.n_heads * HD;
     const int64_t kv_row = (int64_t)a.n_kv_heads * HD;
@@ -81,24 +103,40 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
     const uint16_t* vbase = static_cast<const uint16_t*>(a.cache_v) + (size_t)b * a.max_seq * kv_row + (size_t)kvh * HD;
     const float scale = a.scale;
 
-    for (int k0 = 0; k0 < kend; k0 += kKeys) {
-        // ---- stage K (row-major) and V (transposed) of keys [k0, k0+64) in LDS
-        __syncthreads();
-        constexpr int CH = HD / 8;                   // 16-byte chunks per key row
-        for (int c = tid; c < kKeys * CH; c += 256) {
+    // K/V tiles of 64 keys: the next tile's loads are in flight (registers) while the current
+    // one is computed from LDS; two LDS buffers, one barrier per tile.
+    uint4 kreg[CPT], vreg[CPT];
+    auto load_tile = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + 256 * i;
             const int key = c % kKeys, d8 = (c / kKeys) * 8;   // key-fastest: V^T stores spread over banks
             const int kk = min(k0 + key, kend - 1);   // clamp: rows past kend are masked anyway
-            const uint4 kv = ld16(kbase + (size_t)kk * kv_row + d8);
-            *reinterpret_cast<uint4*>(&Ks[key][d8]) = kv;
-            const uint4 vv = ld16(vbase + (size_t)kk * kv_row + d8);
-            const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+            kreg[i] = ld16(kbase + (size_t)kk * kv_row + d8);
+            vreg[i] = ld16(vbase + (size_t)kk * kv_row + d8);
+        }
+    };
+    auto store_tile = [&](int buf) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                Vt[d8 + 2 * i][key] = static_cast<uint16_t>(w[i] & 0xffffu);
-                Vt[d8 + 2 * i + 1][key] = static_cast<uint16_t>(w[i] >> 16);
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + 256 * i;
+            const int key = c % kKeys, d8 = (c / kKeys) * 8;
+            *reinterpret_cast<uint4*>(&Ks[buf][key][d8]) = kreg[i];
+            const uint32_t w[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                Vt[buf][d8 + 2 * q][vt_pos(key)] = static_cast<uint16_t>(w[q] & 0xffffu);
+                Vt[buf][d8 + 2 * q + 1][vt_pos(key)] = static_cast<uint16_t>(w[q] >> 16);
             }
         }
+    };
+
+    if (kend > 0) load_tile(0);
+    for (int k0 = 0, it = 0; k0 < kend; k0 += kKeys, ++it) {
+        const int buf = it & 1;
+        store_tile(buf);
         __syncthreads();
+        if (k0 + kKeys < kend) load_tile(k0 + kKeys);
 
         // ---- S^T for 4 key tiles of 16: lane holds keys k0 + 16j + 4g + e, query fr
         f32x4 st[4];
@@ -107,7 +145,7 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
             st[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&Ks[16 * j + fr][ks * 32 + g * 8]);
+                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&Ks[buf][16 * j + fr][ks * 32 + g * 8]);
                 st[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], st[j], 0, 0, 0);
             }
         }
@@ -157,13 +195,8 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
             for (int t = 0; t < DT; ++t) {
-                const uint16_t* vr = &Vt[16 * t + fr][32 * kk];
-                const uint2 v0 = *reinterpret_cast<const uint2*>(vr + 4 * g);
-                const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * g);
-                u16x8_t vv;
-                vv[0] = v0.x & 0xffffu; vv[1] = v0.x >> 16; vv[2] = v0.y & 0xffffu; vv[3] = v0.y >> 16;
-                vv[4] = v1.x & 0xffffu; vv[5] = v1.x >> 16; vv[6] = v1.y & 0xffffu; vv[7] = v1.y >> 16;
-                const bf16x8_t vf = as_bf16x8(vv);
+                // the 8 keys of lane group g in this half, already in k-slot order
+                const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(&Vt[buf][16 * t + fr][32 * kk + 8 * g]);
                 o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, as_bf16x8(phi[kk]), o[t], 0, 0, 0);
                 o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, as_bf16x8(plo[kk]), o[t], 0, 0, 0);
             }
@@ -184,7 +217,9 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
 
 hipError_t launch_flash_prefill(const FlashArgs& a, hipStream_t s) {
     const int n_rep = a.n_heads / a.n_kv_heads;
-    const dim3 grid((a.seqlen * n_rep + kRows - 1) / kRows, a.n_kv_heads, a.bsz);
+    const int n_qt = (a.seqlen * n_rep + kRows - 1) / kRows;
+    const int total = n_qt * a.n_kv_heads * a.bsz;
+    const dim3 grid((unsigned)((total + 7) / 8 * 8));     // padded: bijective XCD mapping
     if (a.head_dim == 128)
         launch_kernel(flash_prefill_kernel<128>, grid, dim3(256), 0, s, a);
     else if (a.head_dim == 64)
