@@ -290,17 +290,49 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
 // stores its raw fp32 tile [z][M][B row] and a reduce pass applies the epilogue.  A wave's load instruction fills 1 KB of LDS contiguously
 // (lane i -> bytes 16i..16i+15), i.e. 16 rows x 4 chunks of a 64-byte row; each lane fetches
 // the global chunk (chunk ^ swz(row)), so a fragment read of (row, chunk) finds it at slot
-// chunk ^ swz(row) and the 16 rows of a fragment land on distinct banks without padding.
+// chunk ^ swz(row) and the rows of a fragment land on distinct banks without padding.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 constexpr int kBigBN = 256, kBigBK = 32;
 
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+// The LDS serves a 16-byte read 8 lanes at a time from a 128-byte bank window; rows are 64
+// bytes, so rows r and r + 2 share a window offset.  XOR-ing the chunk with (row / 2) % 4
+// puts the 8 rows of a lane group on 8 distinct 16-byte slots (measured: the previous
+// (row / 4) % 4 gave every fragment read a 2-way conflict).
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
 
 // Tile shapes: wave grid, accumulator tiles per wave, LDS ring slots (NS - 1 stages of
 // loads in flight).  The 128-row tile is for short prefills, where the weights are the
 // traffic: its smaller A tile leaves room for a deeper ring.
+// Eight MFMAs of one fragment group, c[i][jj] += a[i] * b[jj] (i < 4, jj < 2), with the two
+// B fragment reads of the next group issued ahead of them and waited for at the end of the
+// block: the reads are in flight while the MFMAs run, and no asm output is left pending.
+// The accumulators chain MFMA to MFMA on the same registers (no wait states needed); the
+// new fragments go to registers no MFMA of this block reads (early clobber).
+__device__ __forceinline__ void mfma8_read2(f32x4& c00, f32x4& c10, f32x4& c20, f32x4& c30,
+                                            f32x4& c01, f32x4& c11, f32x4& c21, f32x4& c31,
+                                            const u32x4_t& a0, const u32x4_t& a1, const u32x4_t& a2,
+                                            const u32x4_t& a3, const u32x4_t& b0, const u32x4_t& b1,
+                                            u32x4_t& n0, u32x4_t& n1, uint32_t addr0, uint32_t addr1) {
+    asm volatile(
+        "ds_read_b128 %8, %10\n\t"
+        "ds_read_b128 %9, %11\n\t"
+        "v_mfma_f32_16x16x32_bf16 %0, %12, %16, %0\n\t"
+        "v_mfma_f32_16x16x32_bf16 %1, %13, %16, %1\n\t"
+        "v_mfma_f32_16x16x32_bf16 %2, %14, %16, %2\n\t"
+        "v_mfma_f32_16x16x32_bf16 %3, %15, %16, %3\n\t"
+        "v_mfma_f32_16x16x32_bf16 %4, %12, %17, %4\n\t"
+        "v_mfma_f32_16x16x32_bf16 %5, %13, %17, %5\n\t"
+        "v_mfma_f32_16x16x32_bf16 %6, %14, %17, %6\n\t"
+        "v_mfma_f32_16x16x32_bf16 %7, %15, %17, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "+v"(c00), "+v"(c10), "+v"(c20), "+v"(c30), "+v"(c01), "+v"(c11), "+v"(c21), "+v"(c31),
+          "=&v"(n0), "=&v"(n1)
+        : "v"(addr0), "v"(addr1), "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b0), "v"(b1)
+        : "memory");
+}
+
 template <int BM> struct BigShape;
 template <> struct BigShape<256> { static constexpr int WGN = 2, TN = 8, NS = 4; };   // 4 x 2 waves of 64 x 128; 128 KB
 template <> struct BigShape<128> { static constexpr int WGN = 4, TN = 4, NS = 6; };   // 2 x 4 waves of 64 x 64; 144 KB
@@ -394,27 +426,23 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
             : "v"(ab + 2 * a_off[0]), "v"(ab + 2 * a_off[1]), "v"(ab + 2 * a_off[2]),
               "v"(ab + 2 * a_off[3]), "v"(bb + 2 * b_off[0]), "v"(bb + 2 * b_off[1])
             : "memory");
-        bf16x8_t af[TM];
+        static_assert(TM == 4, "mfma8_read2 covers four A fragments");
+        // groups 0 .. TN/2 - 2: MFMAs of group jg with group jg + 1's B reads in flight
 #pragma unroll
-        for (int i = 0; i < TM; ++i) af[i] = __builtin_bit_cast(bf16x8_t, ra[i]);
+        for (int jg = 0; jg + 1 < TN / 2; ++jg)
+            mfma8_read2(acc[0][2 * jg], acc[1][2 * jg], acc[2][2 * jg], acc[3][2 * jg],
+                        acc[0][2 * jg + 1], acc[1][2 * jg + 1], acc[2][2 * jg + 1], acc[3][2 * jg + 1],
+                        ra[0], ra[1], ra[2], ra[3], rb[2 * jg], rb[2 * jg + 1], rb[2 * jg + 2], rb[2 * jg + 3],
+                        bb + 2 * b_off[2 * jg + 2], bb + 2 * b_off[2 * jg + 3]);
+        // last group
+        constexpr int jl = TN / 2 - 1;
 #pragma unroll
-        for (int jg = 0; jg < TN / 2; ++jg) {
-            if (jg > 0) {
-                asm volatile(
-                    "ds_read_b128 %0, %2\n\t"
-                    "ds_read_b128 %1, %3\n\t"
-                    "s_waitcnt lgkmcnt(0)"
-                    : "=&v"(rb[2 * jg]), "=&v"(rb[2 * jg + 1])
-                    : "v"(bb + 2 * b_off[2 * jg]), "v"(bb + 2 * b_off[2 * jg + 1])
-                    : "memory");
-            }
+        for (int jj = 0; jj < 2; ++jj) {
+            const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, rb[2 * jl + jj]);
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, rb[2 * jg + jj]);
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    acc[i][2 * jg + jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf, acc[i][2 * jg + jj], 0, 0, 0);
-            }
+            for (int i = 0; i < TM; ++i)
+                acc[i][2 * jl + jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, ra[i]), bf, acc[i][2 * jl + jj], 0, 0, 0);
         }
     };
 
@@ -438,7 +466,9 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
             }
         }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // drain the duplicate tail loads
+    // drain the duplicate tail loads; the nops keep the epilogue's reads of the accumulators
+    // clear of the last asm MFMAs (the compiler cannot see their latency)
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     if (gridDim.z > 1) {
         // split K: raw fp32 tile of this split, [z][M][B row] with B rows n_tn * BN wide
         const int fr = lane & 15, rq = (lane >> 4) * 4;
