@@ -38,7 +38,7 @@ __device__ __forceinline__ const uint16_t* b_row_ptr(const GemmArgs& a, int tile
         const int wn = brow / (BN / WGN), jj = brow % (BN / WGN);
         n = tile_n * (BN / 2) + wn * half + (jj % half);
         mat = static_cast<const uint16_t*>(jj < half ? a.w0 : a.w1);
-    } else if (EPI == EPI_QKV || EPI == EPI_STORE_QKV) {
+    } else if (EPI == EPI_QKV) {
         n = tile_n * BN + brow;
         ok = n < a.N;
         const int nn = ok ? n : 0;
@@ -540,13 +540,8 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
         }
     }
     if (a.M <= 256) return launch_tile<128, 64, 2, 2, EPI>(a, s);
-    // (the RoPE/KV-append epilogue does not fit 256x256 tiles without spilling)
-    if constexpr (EPI == EPI_QKV) {
-        return launch_tile<128, 128, 2, 2, EPI>(a, s);
-    } else {
-        if (a.M <= 2048) return launch_tile<128, 128, 2, 2, EPI>(a, s);
-        return launch_big<256, EPI>(a, s);
-    }
+    if (a.M <= 2048) return launch_tile<128, 128, 2, 2, EPI>(a, s);
+    return launch_big<256, EPI>(a, s);
 }
 
 }  // namespace
@@ -556,7 +551,6 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
         case EPI_QKV: return launch_epi<EPI_QKV>(a, s);
         case EPI_RESID: return launch_epi<EPI_RESID>(a, s);
         case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(a, s);
-        case EPI_STORE_QKV: return launch_epi<EPI_STORE_QKV>(a, s);
         default: return launch_epi<EPI_STORE>(a, s);
     }
 }

@@ -29,8 +29,7 @@ enum Epilogue : int {
     EPI_QKV = 0,     // rows of [wq; wk; wv]: RoPE on q and k, q -> q buffer, k/v -> KV cache
     EPI_RESID = 1,   // resid[m][n] += y
     EPI_SWIGLU = 2,  // out[m][n] = silu(x.w1[n]) * (x.w3[n])
-    EPI_STORE = 3,   // out[m][n] = y (fp32 logits)
-    EPI_STORE_QKV = 4  // plain fp32 store of the [wq; wk; wv] rows (B rows picked as for EPI_QKV)
+    EPI_STORE = 3    // out[m][n] = y (fp32 logits)
 };
 
 // Per-call values of a decode step kept in device memory, so one captured graph serves

@@ -32,14 +32,13 @@ constexpr int kMaxSplit = 32;
 constexpr int kMaxSplitK = 8;      // K splits of a residual GEMM at small prefill sizes
 constexpr int kSplitKRows = 512;   // prefill rows up to which split-K is considered
 constexpr size_t kSplitKRowsCap = 2048;  // splits x rows the split-K workspace holds
-constexpr int kPlainQkvRows = 2048; // above this many prefill rows the QKV GEMM stores plainly
 constexpr int kSkinnyRows = 4;      // bf16 decode batches above this use the skinny MFMA kernel
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t k_cache, v_cache, rope, h32, q32, o32, g32, act16, g16, part, splitk, qkv32, step, total;
+    size_t k_cache, v_cache, rope, h32, q32, o32, g32, act16, g16, part, splitk, step, total;
     size_t splitk_floats;
     size_t kv_layer_elems;   // elements of one layer's K (or V) cache
 };
@@ -111,8 +110,6 @@ Layout layout_of(const llama_args& a) {
     L.splitk_floats = fp32 ? 0 : std::max((size_t)kMaxSplitK * std::min(maxT, (size_t)kSplitKRows) * a.dim,
                                           kSplitKRowsCap * splitk_cols(a));
     L.splitk = fp32 ? off : take(L.splitk_floats * sizeof(float));
-    // fp32 [wq;wk;wv] projections of long prefills (RoPE and bf16 storage in a second pass)
-    L.qkv32 = (fp32 || maxT <= (size_t)kPlainQkvRows) ? off : take(maxT * (nq + 2 * (size_t)a.n_kv_heads * hd) * sizeof(float));
     L.step = take(sizeof(StepState));
     L.total = off;
     return L;
@@ -379,15 +376,8 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
     g.a = act; g.lda = D; g.M = T; g.K = D; g.N = c->nq + 2 * c->nk;
     g.w0 = W.wq; g.w1 = W.wk; g.w2 = W.wv;
     g.qkv = qkv_target(c, l, start_pos, seqlen);
-    if (T > kPlainQkvRows) {
-        // large tiles with a plain fp32 store, then RoPE + bf16 storage in a light pass
-        g.out = c->at<float>(c->L.qkv32); g.ldo = g.N;
-        LAUNCH(c, LLAMA_KC_GEMM_QKV, s, launch_gemm(EPI_STORE_QKV, g, s));
-        LAUNCH(c, LLAMA_KC_GEMM_QKV, s, launch_rope_scatter(g.out, T, g.qkv, s));
-    } else {
-        g.part = c->at<float>(c->L.splitk); g.part_cap = c->L.splitk_floats;
-        LAUNCH(c, LLAMA_KC_GEMM_QKV, s, launch_gemm(EPI_QKV, g, s));
-    }
+    g.part = c->at<float>(c->L.splitk); g.part_cap = c->L.splitk_floats;
+    LAUNCH(c, LLAMA_KC_GEMM_QKV, s, launch_gemm(EPI_QKV, g, s));
 
     if (c->hd == 64 || c->hd == 128) {
         FlashArgs fa{};
