@@ -98,23 +98,36 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[TM][TN]
             }
         return;
     }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
+    if (EPI == EPI_QKV) {
+        // Rotate q/k pairs (neighbouring columns, one lane apart) with the position's
+        // cos/sin, then store q and append k, v to the cache rows of (sequence, position).
+        // Column and row terms are computed once per fragment column and row.
+        const QkvTarget& t = a.qkv;
+        const int hd2 = t.head_dim / 2;
+        int ncol[TN], rofs[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int n = tile_n * BN + wn * WN + j * 16 + fr;
+            ncol[j] = tile_n * BN + wn * WN + j * 16 + fr;
+            rofs[j] = (ncol[j] % t.head_dim) / 2;
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int m = m0 + wm * WM + i * 16 + rq + e;
-                float v = acc[i][j][e];
-                if (EPI == EPI_QKV) {
+                const int b = m / t.seqlen;
+                const int pos = t.start_pos + (m - b * t.seqlen);
+                const float2* rope_row = t.rope + (size_t)pos * hd2;
+                const size_t cache_row = ((size_t)b * t.max_seq + pos) * (size_t)t.nk;
+                const bool row_ok = m < a.M;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int n = ncol[j];
+                    float v = acc[i][j][e];
                     const float partner = __shfl_xor(v, 1, kWave);
-                    if (m >= a.M || n >= a.N) continue;
-                    const QkvTarget& t = a.qkv;
-                    const int b = m / t.seqlen;
-                    const int pos = t.start_pos + (m - b * t.seqlen);
+                    if (!row_ok || n >= a.N) continue;
                     if (n < t.nq + t.nk) {
-                        const float2 cs = t.rope[(size_t)pos * (t.head_dim / 2) + (n % t.head_dim) / 2];
+                        const float2 cs = rope_row[rofs[j]];
                         v = (n & 1) ? partner * cs.y + v * cs.x : v * cs.x - partner * cs.y;
                     }
                     if (n < t.nq) {
@@ -123,9 +136,22 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[TM][TN]
                         const bool is_k = n < t.nq + t.nk;
                         const int c = is_k ? n - t.nq : n - t.nq - t.nk;
                         uint16_t* cache = static_cast<uint16_t*>(is_k ? t.cache_k : t.cache_v);
-                        cache[((size_t)b * t.max_seq + pos) * (size_t)t.nk + c] = f32_to_bf16(v);
+                        cache[cache_row + c] = f32_to_bf16(v);
                     }
-                } else if (m < a.M && n < a.N) {
+                }
+            }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = tile_n * BN + wn * WN + j * 16 + fr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = m0 + wm * WM + i * 16 + rq + e;
+                const float v = acc[i][j][e];
+                if (m < a.M && n < a.N) {
                     if (EPI == EPI_RESID) {
                         if (gridDim.z > 1)
                             a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = v;
