@@ -12,9 +12,12 @@
 //    LDS banks;
 //  - activations arrive in fragment-major order (their producer wrote them that way; see
 //    frag_index), so a wave's B fragment is one contiguous 1 KB load.
-// A workgroup owns 16 output rows; its waves take interleaved stages of 64 k (128 bytes of
-// each row), each wave through a ring of its own (D slots, D - 1 stages in flight), with no
-// barrier inside the loop.  At the end the waves' partial sums meet in LDS.
+// A workgroup owns NT blocks of 16 output rows; its waves take interleaved stages of 64 k
+// (128 bytes of each row), each wave through a ring of its own (D slots, D - 1 stages in
+// flight), with no barrier inside the loop.  Every activation fragment a wave loads feeds
+// the MFMAs of all NT (x NW matrices) weight blocks: with 32 batch rows the activations are
+// as many bytes per stage as one weight block, and the bytes a CU takes in per stage, not
+// the weights alone, set the pace.  At the end the waves' partial sums meet in LDS.
 // Epilogues: RoPE + bf16 q / KV append, residual add, SiLU gate (bf16 out, optionally in
 // fragment-major order for the next product), fp32 logits.
 #include "common.h"
@@ -111,28 +114,33 @@ __device__ __forceinline__ void sk_epilogue(const SkinnyArgs& a, const f32x4 (&a
     }
 }
 
-template <int NW, int MT, int EPI, int D, int NWV>
+template <int NW, int NT, int MT, int EPI, int D, int NWV>
 __global__ __launch_bounds__(64 * NWV) void skinny_kernel(SkinnyArgs a) {
-    constexpr int kStage = NW * kSkWBytes;        // one wave's ring slot
-    constexpr int kOps = 2 * NW + 2 * MT;         // loads per wave per stage (DMA + fragments)
+    constexpr int NB = NT * NW;                   // weight blocks (16 rows each) per stage
+    constexpr int kStage = NB * kSkWBytes;        // one wave's ring slot
+    constexpr int kOps = 2 * NB + 2 * MT;         // loads per wave per stage (DMA + fragments)
     constexpr int kWait = (D - 2) * kOps;         // loads of later stages left in flight
     static_assert(kWait < 64, "vmcnt holds at most 63");
-    static_assert(NWV * D * kStage >= NWV * NW * MT * 64 * 16, "the reduction reuses the ring");
+    static_assert(NWV * D * kStage >= NWV * NB * MT * 64 * 16, "the reduction reuses the ring");
+    static_assert(NT * MT <= NWV, "one wave per result tile in the epilogue");
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NWV * D * kStage];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int fr = lane & 15, g = lane >> 4;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * 16 * NT;
     const int nst = a.K / kSkBK;
     const int n_my = (nst - wid + NWV - 1) / NWV;     // stages wid, wid + NWV, ... of this wave
 
-    // DMA sources of this lane: rows n0 + 8h + r8 (clamped past N), chunk c8
+    // DMA sources of this lane: rows n0 + 16t + 8h + r8 (clamped past N), chunk c8
     const int r8 = lane >> 3, c8 = (lane & 7) ^ r8;
-    const uint16_t* wsrc[NW][2];
+    const uint16_t* wsrc[NT][NW][2];
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) wsrc[w][h] = sk_row<EPI>(a, w, min(n0 + 8 * h + r8, a.N - 1)) + c8 * 8;
+        for (int w = 0; w < NW; ++w)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                wsrc[t][w][h] = sk_row<EPI>(a, w, min(n0 + 16 * t + 8 * h + r8, a.N - 1)) + c8 * 8;
     // fragment-major activations: tile t of k-step s is the 1 KB at element (s * MT + t) * 512
     const uint16_t* xsrc = static_cast<const uint16_t*>(a.x) + lane * 8;
 
@@ -148,11 +156,11 @@ __global__ __launch_bounds__(64 * NWV) void skinny_kernel(SkinnyArgs a) {
         kt = kt >= nst ? kt - nst : kt;
         const int k = kt * kSkBK;
 #pragma unroll
-        for (int w = 0; w < NW; ++w)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-                __builtin_amdgcn_global_load_lds((gbl_void_t*)(wsrc[w][h] + k),
-                                                 (lds_void_t*)(wring + u * kStage + w * kSkWBytes + h * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((gbl_void_t*)(wsrc[b / NW][b % NW][h] + k),
+                                                 (lds_void_t*)(wring + u * kStage + b * kSkWBytes + h * 1024), 16, 0, 0);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -163,30 +171,30 @@ __global__ __launch_bounds__(64 * NWV) void skinny_kernel(SkinnyArgs a) {
     const uint32_t aoff0 = (fr >> 3) * 1024 + sk_slot(fr & 7, g);
     const uint32_t aoff1 = (fr >> 3) * 1024 + sk_slot(fr & 7, 4 + g);
 
-    f32x4 acc[NW][MT];
+    f32x4 acc[NB][MT];    // block b = weight rows n0 + 16 (b / NW), matrix b % NW
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc[w][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < MT; ++t) acc[b][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // live = 0 (a step past this wave's last stage): the weight fragments are masked to zero,
     // so the product adds nothing; no branch, so the loop body stays straight-line
     auto compute = [&](int u, uint32_t live) {
         const uint32_t sb = wring_addr + u * kStage;
-        u32x4_t ra[NW][2];
+        u32x4_t ra[NB][2];
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            lds_read2(ra[w][0], ra[w][1], sb + w * kSkWBytes + aoff0, sb + w * kSkWBytes + aoff1);
-            ra[w][0] &= live;
-            ra[w][1] &= live;
+        for (int b = 0; b < NB; ++b) {
+            lds_read2(ra[b][0], ra[b][1], sb + b * kSkWBytes + aoff0, sb + b * kSkWBytes + aoff1);
+            ra[b][0] &= live;
+            ra[b][1] &= live;
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int w = 0; w < NW; ++w)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
-                    acc[w][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag(ra[w][j]), frag(xr[u][j][t]), acc[w][t], 0, 0, 0);
+                    acc[b][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag(ra[b][j]), frag(xr[u][j][t]), acc[b][t], 0, 0, 0);
     };
 
 #pragma unroll
@@ -206,45 +214,53 @@ __global__ __launch_bounds__(64 * NWV) void skinny_kernel(SkinnyArgs a) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the repeated tail loads
 
-    // sum the waves' partials: red[wave][w][t][lane] in the ring's memory
+    // sum the waves' partials: red[wave][b][t][lane] in the ring's memory
     __syncthreads();
     f32x4* red = reinterpret_cast<f32x4*>(ring);
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int t = 0; t < MT; ++t) red[((wid * NW + w) * MT + t) * 64 + lane] = acc[w][t];
+        for (int t = 0; t < MT; ++t) red[((wid * NB + b) * MT + t) * 64 + lane] = acc[b][t];
     __syncthreads();
-    // wave t finishes result tile t (batch rows 16t .. 16t + 15)
-    if (wid >= MT) return;
+    // wave q finishes result tile (row block q / MT, batch rows 16 (q % MT) .. + 15)
+    if (wid >= NT * MT) return;
+    const int tb = wid / MT, tm = wid % MT;
     f32x4 sum[NW];
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
         sum[w] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q = 0; q < NWV; ++q) sum[w] += red[((q * NW + w) * MT + wid) * 64 + lane];
+        for (int q = 0; q < NWV; ++q) sum[w] += red[((q * NB + tb * NW + w) * MT + tm) * 64 + lane];
     }
-    sk_epilogue<NW, EPI>(a, sum, 16 * wid + fr, n0, g);
+    sk_epilogue<NW, EPI>(a, sum, 16 * tm + fr, n0 + 16 * tb, g);
 }
 
-template <int NW, int EPI, int D, int NWV>
+template <int NW, int NT, int MT, int EPI, int D, int NWV>
 hipError_t launch_waves(const SkinnyArgs& a, hipStream_t s) {
-    const dim3 grid((a.N + 15) / 16);
-    if (a.M <= 16)
-        launch_kernel((skinny_kernel<NW, 1, EPI, D, NWV>), grid, dim3(64 * NWV), 0, s, a);
-    else
-        launch_kernel((skinny_kernel<NW, 2, EPI, D, NWV>), grid, dim3(64 * NWV), 0, s, a);
+    const dim3 grid((a.N + 16 * NT - 1) / (16 * NT));
+    launch_kernel((skinny_kernel<NW, NT, MT, EPI, D, NWV>), grid, dim3(64 * NWV), 0, s, a);
     return hipGetLastError();
 }
 
-// Ring depth per wave and waves per workgroup: 8 waves when there are too few 16-row tiles
-// for two 4-wave workgroups per CU; the LDS of a workgroup stays at or under 128 KB.
+// Row blocks per workgroup (NT), ring depth per wave (D) and waves per workgroup (NWV), from
+// timings at the decode shapes (batch 8 .. 32 of the 7B, 13B and 70B layer widths):
+//  - SiLU gate: gate and up rows already share each activation fragment: NT = 1, D = 4, and
+//    8 waves when there are too few 16-row tiles for two 4-wave workgroups per CU;
+//  - wide products (q/k/v, logits: 640 or more tiles): NT = 4 for up to 16 batch rows, 2 for
+//    up to 32, 4 waves;
+//  - the others (wo, w2): NT = 2 with 8 waves for up to 16 rows, NT = 1 with 4 for more.
+// The LDS of a workgroup stays at or under 128 KB.
 template <int EPI>
 hipError_t launch_epi(const SkinnyArgs& a, hipStream_t s) {
-    constexpr int NW = (EPI == EPI_SWIGLU) ? 2 : 1;
-    constexpr int D = NW == 1 ? 8 : 4;
     const int tiles = (a.N + 15) / 16;
-    if (tiles >= 512) return launch_waves<NW, EPI, D, 4>(a, s);
-    return launch_waves<NW, EPI, D, 8>(a, s);
+    const bool m16 = a.M <= 16;     // one 16-row batch tile (MT = 1) or two
+    if constexpr (EPI == EPI_SWIGLU) {
+        if (tiles >= 512) return m16 ? launch_waves<2, 1, 1, EPI, 4, 4>(a, s) : launch_waves<2, 1, 2, EPI, 4, 4>(a, s);
+        return m16 ? launch_waves<2, 1, 1, EPI, 4, 8>(a, s) : launch_waves<2, 1, 2, EPI, 4, 8>(a, s);
+    } else {
+        if (tiles >= 640) return m16 ? launch_waves<1, 4, 1, EPI, 4, 4>(a, s) : launch_waves<1, 2, 2, EPI, 4, 4>(a, s);
+        return m16 ? launch_waves<1, 2, 1, EPI, 4, 8>(a, s) : launch_waves<1, 1, 2, EPI, 8, 4>(a, s);
+    }
 }
 
 }  // namespace
