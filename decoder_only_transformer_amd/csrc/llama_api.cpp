@@ -450,6 +450,8 @@ llama_status llama_init(const llama_args* a, const llama_weights* w, void* d_wor
     const llama_status st = check_args(a);
     if (st != LLAMA_OK) return st;
     if (!w->tok_embeddings || !w->norm || !w->output || !w->layers) return LLAMA_ERR_INVALID_ARG;
+    for (const void* q : {w->tok_embeddings, w->norm, w->output})
+        if (reinterpret_cast<uintptr_t>(q) & 15) return LLAMA_ERR_INVALID_ARG;
     for (int l = 0; l < a->n_layers; ++l) {
         const llama_layer_weights& L = w->layers[l];
         const void* p[9] = {L.attention_norm, L.wq, L.wk, L.wv, L.wo, L.ffn_norm, L.w1, L.w2, L.w3};

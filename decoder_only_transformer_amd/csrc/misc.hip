@@ -51,6 +51,41 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const float* h, int64
     }
 }
 
+// Same, for rows of at most 1024 * NV elements: every load of the row (and of the weights)
+// is issued before the first use and the row stays in registers for the second half, so a
+// row costs one memory round trip instead of one per chunk and pass.
+template <int NV>
+__global__ __launch_bounds__(256) void rmsnorm_reg_kernel(const float* h, int64_t ldh, int dim, const bf16* w,
+                                                          float eps, uint16_t* out, int64_t ldo, int frag_mt) {
+    __shared__ float red[4];
+    const float* x = h + (size_t)blockIdx.x * ldh;
+    float4 v[NV];
+    uint2 wv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int k = (threadIdx.x + 256 * i) * 4;
+        v[i] = k < dim ? *reinterpret_cast<const float4*>(x + k) : float4{0.f, 0.f, 0.f, 0.f};
+        wv[i] = k < dim ? *reinterpret_cast<const uint2*>(w + k) : uint2{0u, 0u};
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float r = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)dim + eps);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int k = (threadIdx.x + 256 * i) * 4;
+        if (k >= dim) continue;
+        uint2 p;
+        p.x = pack_bf16x2(v[i].x * r * bf16lo(wv[i].x), v[i].y * r * bf16hi(wv[i].x));
+        p.y = pack_bf16x2(v[i].z * r * bf16lo(wv[i].y), v[i].w * r * bf16hi(wv[i].y));
+        const size_t o = frag_mt ? frag_index(blockIdx.x, k, frag_mt) : (size_t)blockIdx.x * ldo + k;
+        *reinterpret_cast<uint2*>(out + o) = p;
+    }
+}
+
 // Better of two (value, index) candidates: larger value wins, ties -> lower index, NaN never wins.
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
     if (i2 < 0) return;
@@ -184,8 +219,20 @@ hipError_t launch_set_step(StepState* st, int pos, int64_t ld, const int32_t* to
 
 hipError_t launch_rmsnorm_bf16(const float* h, int64_t ldh, int rows, int dim, const void* w,
                                float eps, void* out, int64_t ldo, int frag_mt, hipStream_t s) {
-    launch_kernel(rmsnorm_bf16_kernel<bf16>, dim3(rows), dim3(256), 0, s, h, ldh, dim,
-                  static_cast<const bf16*>(w), eps, static_cast<uint16_t*>(out), ldo, frag_mt);
+    const bf16* wb = static_cast<const bf16*>(w);
+    uint16_t* o = static_cast<uint16_t*>(out);
+    switch ((dim + 1023) / 1024) {
+        case 1: launch_kernel(rmsnorm_reg_kernel<1>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt); break;
+        case 2: launch_kernel(rmsnorm_reg_kernel<2>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt); break;
+        case 3:
+        case 4: launch_kernel(rmsnorm_reg_kernel<4>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt); break;
+        case 5:
+        case 6: launch_kernel(rmsnorm_reg_kernel<6>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt); break;
+        case 7:
+        case 8: launch_kernel(rmsnorm_reg_kernel<8>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt); break;
+        default:
+            launch_kernel(rmsnorm_bf16_kernel<bf16>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt);
+    }
     return hipGetLastError();
 }
 

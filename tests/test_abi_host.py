@@ -92,6 +92,12 @@ def test_init_rejects_bad_arguments_without_touching_the_device(lib):
     assert st == abi.LLAMA_ERR_INVALID_ARG
     st, _ = abi.llama_init(tiny(n_kv_heads=3), w, 256, need, 0)
     assert st == abi.LLAMA_ERR_INVALID_ARG
+    for i in range(3):                                      # misaligned embeddings / norm / output
+        ptrs = [16, 16, 16]
+        ptrs[i] = 18
+        wm = abi.llama_weights(*ptrs, ctypes.cast(layers, ctypes.POINTER(abi.llama_layer_weights)))
+        st, _ = abi.llama_init(a, wm, 256, need, 0)
+        assert st == abi.LLAMA_ERR_INVALID_ARG
 
 
 def test_calls_reject_bad_arguments(lib):
