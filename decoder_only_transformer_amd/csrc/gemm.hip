@@ -359,6 +359,97 @@ __device__ __forceinline__ void mfma8_read2(f32x4& c00, f32x4& c10, f32x4& c20, 
         : "memory");
 }
 
+// Epilogue of the 256 x 256 kernel through LDS.  A wave's accumulators (64 rows x 128
+// columns, 4 consecutive rows of one column per lane and tile) go to its own 16 KB of the
+// then idle ring as fp32, 64 columns per pass, and come back as 16-byte row chunks, 16 lanes
+// to a row: the residual rows are read and written, and the q / K / V / gated rows written,
+// in whole 256-byte segments rather than 4-byte pieces.  Chunks (4 floats) are XOR-swizzled
+// by row so that both the column-wise writes and the row-wise reads spread over the banks.
+// RoPE is applied on the row chunks: a lane holds two whole (even, odd) pairs.
+template <int EPI>
+__device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[4][8], int m0, int tile_n,
+                                                int wm, int wn, int lane, float* stage) {
+    constexpr int TM = 4, WM = 64, WN = 128;
+    const int fr = lane & 15, rq = (lane >> 4) * 4;
+    const int row0 = m0 + wm * WM;
+    auto phys = [](int r, int chunk) { return r * 64 + ((chunk ^ (4 * ((r >> 2) & 3))) << 2); };
+    constexpr int kPasses = (EPI == EPI_SWIGLU) ? 1 : 2;
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass) {
+        __syncthreads();    // the ring's last reads (or the previous pass's) are done
+        // phase 1: the 4 column tiles of this pass, fp32
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = i * 16 + rq + e, col = jj * 16 + fr;
+                    float v;
+                    if constexpr (EPI == EPI_SWIGLU)
+                        v = silu(acc[i][jj][e]) * acc[i][jj + 4][e];
+                    else
+                        v = acc[i][pass * 4 + jj][e];
+                    stage[phys(r, col >> 2) + (col & 3)] = v;
+                }
+        __syncthreads();
+        // phase 2: row chunks, 4 rows per step
+#pragma unroll 4
+        for (int it = 0; it < 16; ++it) {
+            const int r = it * 4 + (lane >> 4), c = lane & 15;
+            const int m = row0 + r;
+            if (m >= a.M) continue;
+            const float4 v = *reinterpret_cast<const float4*>(stage + phys(r, c));
+            if constexpr (EPI == EPI_RESID) {
+                const int n = tile_n * 256 + wn * WN + pass * 64 + c * 4;
+                if (n >= a.N) continue;
+                float4* dst = reinterpret_cast<float4*>(a.resid + (size_t)m * a.ldr + n);
+                float4 h = *dst;
+                h.x += v.x;
+                h.y += v.y;
+                h.z += v.z;
+                h.w += v.w;
+                *dst = h;
+            } else if constexpr (EPI == EPI_SWIGLU) {
+                const int n = tile_n * 128 + wn * 64 + c * 4;
+                if (n >= a.N) continue;
+                uint2 p;
+                p.x = pack_bf16x2(v.x, v.y);
+                p.y = pack_bf16x2(v.z, v.w);
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out16) + (size_t)m * a.ldo16 + n) = p;
+            } else {
+                const QkvTarget& t = a.qkv;
+                const int n = tile_n * 256 + wn * WN + pass * 64 + c * 4;
+                if (n >= a.N) continue;
+                const int b = m / t.seqlen;
+                const int pos = t.start_pos + (m - b * t.seqlen);
+                float4 y = v;
+                if (n < t.nq + t.nk) {
+                    // (cos, sin) of the pairs (n, n + 1) and (n + 2, n + 3)
+                    const float4 cs = *reinterpret_cast<const float4*>(
+                        t.rope + (size_t)pos * (t.head_dim / 2) + (n % t.head_dim) / 2);
+                    y.x = v.x * cs.x - v.y * cs.y;
+                    y.y = v.y * cs.x + v.x * cs.y;
+                    y.z = v.z * cs.z - v.w * cs.w;
+                    y.w = v.w * cs.z + v.z * cs.w;
+                }
+                if (n < t.nq) {
+                    *reinterpret_cast<float4*>(t.q + (size_t)m * t.nq + n) =
+                        float4{round_bf16(y.x), round_bf16(y.y), round_bf16(y.z), round_bf16(y.w)};
+                } else {
+                    const bool is_k = n < t.nq + t.nk;
+                    const int cc = is_k ? n - t.nq : n - t.nq - t.nk;
+                    uint16_t* cache = static_cast<uint16_t*>(is_k ? t.cache_k : t.cache_v);
+                    uint2 p;
+                    p.x = pack_bf16x2(y.x, y.y);
+                    p.y = pack_bf16x2(y.z, y.w);
+                    *reinterpret_cast<uint2*>(cache + ((size_t)b * t.max_seq + pos) * (size_t)t.nk + cc) = p;
+                }
+            }
+        }
+    }
+}
+
 template <int BM> struct BigShape;
 template <> struct BigShape<256> { static constexpr int WGN = 2, TN = 8, NS = 4; };   // 4 x 2 waves of 64 x 128; 128 KB
 template <> struct BigShape<128> { static constexpr int WGN = 4, TN = 4, NS = 6; };   // 2 x 4 waves of 64 x 64; 144 KB
@@ -512,7 +603,12 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
             }
         return;
     }
-    epilogue<BN, WGN, TM, TN, EPI>(a, acc, m0, tile_n, wm, wn, lane);
+    if constexpr (BM == 256 && EPI != EPI_STORE) {
+        static_assert(TN == 8 && WN == 128 && NS * kSlot >= 8 * 64 * 64 * 2, "16 KB of ring per wave");
+        epilogue_staged<EPI>(a, acc, m0, tile_n, wm, wn, lane, reinterpret_cast<float*>(ring) + wid * 64 * 64);
+    } else {
+        epilogue<BN, WGN, TM, TN, EPI>(a, acc, m0, tile_n, wm, wn, lane);
+    }
 }
 
 // K splits for a short prefill (M <= kShortRows) on the LDS-ring kernel: about one
