@@ -1,8 +1,9 @@
 // Causal grouped-query attention for prefill on bf16 MFMA (gfx950 v_mfma_f32_16x16x32_bf16).
 //
-// A workgroup owns one batch row, one kv head and 64 query rows, a query row being a
+// A workgroup owns one batch row, one kv head and 128 query rows, a query row being a
 // (position, head) pair of the n_rep heads that read this kv head (GQA is never
-// materialised: the K/V tile in LDS serves all of them).  Four waves own 16 rows each.
+// materialised: the K/V tile in LDS serves all of them).  Four waves own 32 rows each, as
+// two 16-row tiles that share every K and V fragment read.
 // K/V advance in tiles of 64 keys up to the last position any row of the workgroup sees; the
 // next tile's loads are in flight while the current tile is computed.
 //
@@ -26,7 +27,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kRows = 64;     // query rows per workgroup
+constexpr int kRows = 128;    // query rows per workgroup: 4 waves x 2 tiles of 16
+constexpr int kQT = 2;        // 16-row query tiles per wave (each K/V fragment read feeds both)
 
 // Position of key `key` (0..63) of a tile in a V^T row: each 32-key half is stored in the
 // permuted k order of the O^T product, so lane group g's 8 keys {4g..4g+3, 16+4g..16+4g+3}
@@ -37,10 +39,19 @@ __device__ __forceinline__ int vt_pos(int key) {
 }
 constexpr int kKeys = 64;     // keys per tile
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u16x8_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// Two floats to two round-to-nearest-even bf16 in one word (low half = a).
+__device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_t));
+}
+
 template <int HD>
-__global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
+__global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
     constexpr int KS = HD / 32;            // MFMA k-steps over head_dim
     constexpr int DT = HD / 16;            // 16-row tiles of head_dim in O^T
     constexpr int KLD = HD + 8;            // padded K row (elements)
@@ -68,23 +79,26 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
     const int qstride = a.n_heads * HD;
     const int64_t kv_row = (int64_t)a.n_kv_heads * HD;
 
-    // This lane's query row (column fr of the wave's S^T tile).
-    const int r_local = qtile * kRows + wid * 16 + fr;
-    const int s_idx = r_local / n_rep;                     // position within the prompt
-    const int head = kvh * n_rep + r_local % n_rep;
-    const bool row_ok = s_idx < a.seqlen;
-    const int qpos = a.start_pos + (row_ok ? s_idx : a.seqlen - 1);   // absolute position
-
-    // Q fragments (bf16-valued fp32 in the q buffer -> exact bf16).
-    bf16x8_t qf[KS];
-    {
-        const float* qp = a.q + ((size_t)b * a.seqlen + (row_ok ? s_idx : 0)) * qstride + head * HD;
+    // This lane's query rows: column fr of the wave's S^T tiles qt = 0, 1.  Rows past the
+    // prompt compute with the last position's keys and are not stored.
+    int s_idx[kQT], head[kQT], qpos[kQT];
+    bool row_ok[kQT];
+    bf16x8_t qf[kQT][KS];
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
+        const int r_local = qtile * kRows + wid * 16 * kQT + qt * 16 + fr;
+        s_idx[qt] = r_local / n_rep;                       // position within the prompt
+        head[qt] = kvh * n_rep + r_local % n_rep;
+        row_ok[qt] = s_idx[qt] < a.seqlen;
+        qpos[qt] = a.start_pos + (row_ok[qt] ? s_idx[qt] : a.seqlen - 1);   // absolute position
+        // Q fragments (bf16-valued fp32 in the q buffer -> exact bf16)
+        const float* qp = a.q + ((size_t)b * a.seqlen + (row_ok[qt] ? s_idx[qt] : 0)) * qstride + head[qt] * HD;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u16x8_t v;
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = f32_to_bf16(qp[ks * 32 + g * 8 + e]);
-            qf[ks] = as_bf16x8(v);
+            qf[qt][ks] = as_bf16x8(v);
         }
     }
 
@@ -94,14 +108,22 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
     const int first_row = qtile * kRows;
     const int kfull = a.start_pos + first_row / n_rep + 1;   // keys < kfull are visible to all rows
 
-    float m = -INFINITY, l = 0.f;
-    f32x4 o[DT];
+    // Online softmax in base 2: scores are scaled by scale * log2(e), p = 2^(s - m).  The
+    // running max m is raised (and O, l rescaled) only when some row's tile max exceeds it by
+    // more than 8, so p <= 2^8 between raises; the final O / l is the same quotient.
+    const float c2 = a.scale * 1.4426950408889634f;
+    float m[kQT], l[kQT];
+    f32x4 o[kQT][DT];
 #pragma unroll
-    for (int t = 0; t < DT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qt = 0; qt < kQT; ++qt) {
+        m[qt] = -INFINITY;
+        l[qt] = 0.f;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) o[qt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     const uint16_t* kbase = static_cast<const uint16_t*>(a.cache_k) + (size_t)b * a.max_seq * kv_row + (size_t)kvh * HD;
     const uint16_t* vbase = static_cast<const uint16_t*>(a.cache_v) + (size_t)b * a.max_seq * kv_row + (size_t)kvh * HD;
-    const float scale = a.scale;
 
     // K/V tiles of 64 keys: the next tile's loads are in flight (registers) while the current
     // one is computed from LDS; two LDS buffers, one barrier per tile.
@@ -138,57 +160,76 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
         __syncthreads();
         if (k0 + kKeys < kend) load_tile(k0 + kKeys);
 
-        // ---- S^T for 4 key tiles of 16: lane holds keys k0 + 16j + 4g + e, query fr
-        f32x4 st[4];
+        // ---- S^T for 4 key tiles of 16: lane holds keys k0 + 16j + 4g + e of query column fr
+        f32x4 st[kQT][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            st[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int qt = 0; qt < kQT; ++qt) st[qt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&Ks[buf][16 * j + fr][ks * 32 + g * 8]);
-                st[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], st[j], 0, 0, 0);
+#pragma unroll
+                for (int qt = 0; qt < kQT; ++qt)
+                    st[qt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qt][ks], st[qt][j], 0, 0, 0);
             }
         }
-        // ---- scale, causal mask, online softmax (per query = per lane column)
-        const bool need_mask = (k0 + kKeys > kfull) || !row_ok;
-        float tmax = -INFINITY;
+        // ---- scale, causal mask (tiles reaching past the first row's position only), online
+        //      softmax per query (= per lane column; lanes l, l^16, l^32, l^48 share one)
+        const bool diag = k0 + kKeys > kfull;
+        u32x4_t phi[kQT][2], plo[kQT][2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int qt = 0; qt < kQT; ++qt) {
+            float tmax = -INFINITY;
+            if (diag) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float v = st[j][e] * scale;
-                if (need_mask) {
-                    const int key = k0 + 16 * j + 4 * g + e;
-                    if (key > qpos || key >= kend || !row_ok) v = -INFINITY;
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int key = k0 + 16 * j + 4 * g + e;
+                        const float v = key > qpos[qt] ? -INFINITY : st[qt][j][e] * c2;
+                        st[qt][j][e] = v;
+                        tmax = fmaxf(tmax, v);
+                    }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float v = st[qt][j][e] * c2;
+                        st[qt][j][e] = v;
+                        tmax = fmaxf(tmax, v);
+                    }
+            }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+            if (__any(tmax > m[qt] + 8.f)) {
+                const float mn = fmaxf(m[qt], tmax);
+                const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn);   // 0 on the first tile
+                l[qt] *= alpha;
+#pragma unroll
+                for (int t = 0; t < DT; ++t) o[qt][t] *= alpha;
+                m[qt] = mn;
+            }
+            float psum = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; e += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(st[qt][j][e] - m[qt]);
+                    const float p1 = __builtin_amdgcn_exp2f(st[qt][j][e + 1] - m[qt]);
+                    psum += p0 + p1;
+                    // P = hi + lo, both bf16; k-slot of key (j, e) in the permuted PV order:
+                    // half kk = j / 2, slot (j % 2) * 4 + e of the lane group's 8
+                    const uint32_t hi = cvt_pk(p0, p1);
+                    const uint32_t lo = cvt_pk(p0 - __uint_as_float(hi << 16), p1 - __uint_as_float(hi & 0xffff0000u));
+                    phi[qt][j >> 1][(j & 1) * 2 + e / 2] = hi;
+                    plo[qt][j >> 1][(j & 1) * 2 + e / 2] = lo;
                 }
-                st[j][e] = v;
-                tmax = fmaxf(tmax, v);
-            }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-        const float mn = fmaxf(m, tmax);
-        const float alpha = (mn == -INFINITY) ? 1.f : __expf(m - mn);
-        float psum = 0.f;
-        u16x8_t phi[2], plo[2];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float p = (mn == -INFINITY) ? 0.f : __expf(st[j][e] - mn);
-                psum += p;
-                const uint16_t hi = f32_to_bf16(p);
-                const uint16_t lo = f32_to_bf16(p - bf16_to_f32(hi));
-                // k-slot of this key in the permuted PV order: tile pair kk = j / 2,
-                // slot (j % 2) * 4 + e within the lane group's 8
-                phi[j >> 1][(j & 1) * 4 + e] = hi;
-                plo[j >> 1][(j & 1) * 4 + e] = lo;
-            }
-        psum += __shfl_xor(psum, 16, kWave);
-        psum += __shfl_xor(psum, 32, kWave);
-        l = l * alpha + psum;
-        m = mn;
-#pragma unroll
-        for (int t = 0; t < DT; ++t) o[t] *= alpha;
+            psum += __shfl_xor(psum, 16, kWave);
+            psum += __shfl_xor(psum, 32, kWave);
+            l[qt] += psum;
+        }
 
         // ---- O^T += V^T P^T over the two 32-key halves (permuted k order)
 #pragma unroll
@@ -197,20 +238,29 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
             for (int t = 0; t < DT; ++t) {
                 // the 8 keys of lane group g in this half, already in k-slot order
                 const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(&Vt[buf][16 * t + fr][32 * kk + 8 * g]);
-                o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, as_bf16x8(phi[kk]), o[t], 0, 0, 0);
-                o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, as_bf16x8(plo[kk]), o[t], 0, 0, 0);
+#pragma unroll
+                for (int qt = 0; qt < kQT; ++qt) {
+                    o[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(bf16x8_t, phi[qt][kk]), o[qt][t], 0, 0, 0);
+                    o[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(bf16x8_t, plo[qt][kk]), o[qt][t], 0, 0, 0);
+                }
             }
         }
     }
 
-    // ---- O = O^T / l, stored bf16 at [b*seqlen + s][head*hd + d]
-    if (!row_ok) return;
-    const float inv = 1.f / l;
-    uint16_t* out = static_cast<uint16_t*>(a.out) + ((size_t)b * a.seqlen + s_idx) * qstride + head * HD;
+    // ---- O = O^T / l, stored bf16 at [b*seqlen + s][head*hd + d]: 4 consecutive d per store
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+    for (int qt = 0; qt < kQT; ++qt) {
+        if (!row_ok[qt]) continue;
+        const float inv = 1.f / l[qt];
+        uint16_t* out = static_cast<uint16_t*>(a.out) + ((size_t)b * a.seqlen + s_idx[qt]) * qstride + head[qt] * HD;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) out[16 * t + 4 * g + e] = f32_to_bf16(o[t][e] * inv);
+        for (int t = 0; t < DT; ++t) {
+            uint2 w;
+            w.x = cvt_pk(o[qt][t][0] * inv, o[qt][t][1] * inv);
+            w.y = cvt_pk(o[qt][t][2] * inv, o[qt][t][3] * inv);
+            *reinterpret_cast<uint2*>(out + 16 * t + 4 * g) = w;
+        }
+    }
 }
 
 }  // namespace
