@@ -445,7 +445,11 @@ hipError_t launch4(const AttnArgs& args, hipStream_t s) {
             }
         }
         if (done) {
-        } else if (a.seqlen == 1)
+        } else if (a.seqlen == 1 && NREP == 1 && n * a.n_kv_heads >= 512)
+            // many (row, head) pairs, each a workgroup: 4 waves, so that all of them are
+            // resident at once (16-wave workgroups would leave a partial second round)
+            launch_kernel((attn_rows_kernel<KT, HD, NREP, OB, 4>), grid, dim3(256), 0, s, a);
+        else if (a.seqlen == 1)
             launch_kernel((attn_rows_kernel<KT, HD, NREP, OB, kDecodeWaves<NREP>>), grid,
                                dim3(64 * kDecodeWaves<NREP>), 0, s, a);
         else

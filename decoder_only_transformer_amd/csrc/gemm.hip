@@ -55,6 +55,7 @@ __device__ __forceinline__ const uint16_t* b_row_ptr(const GemmArgs& a, int tile
 }
 
 constexpr int kXcds = 8;
+constexpr int kCUs = 256;      // compute units of the device (one 256 x 256 tile each at a time)
 constexpr int kGroupM = 8;
 
 // Tile (tm, tn) of linear workgroup id `id` (see the header comment).  The grid is padded to
@@ -115,8 +116,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[TM][TN]
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int m = m0 + wm * WM + i * 16 + rq + e;
-                const int b = m / t.seqlen;
-                const int pos = t.start_pos + (m - b * t.seqlen);
+                const int mm = t.row0 + m;    // row of the bsz x seqlen rectangle
+                const int b = mm / t.seqlen;
+                const int pos = t.start_pos + (mm - b * t.seqlen);
                 const float2* rope_row = t.rope + (size_t)pos * hd2;
                 const size_t cache_row = ((size_t)b * t.max_seq + pos) * (size_t)t.nk;
                 const bool row_ok = m < a.M;
@@ -131,7 +133,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[TM][TN]
                         v = (n & 1) ? partner * cs.y + v * cs.x : v * cs.x - partner * cs.y;
                     }
                     if (n < t.nq) {
-                        t.q[(size_t)m * t.nq + n] = round_bf16(v);
+                        t.q[(size_t)mm * t.nq + n] = round_bf16(v);
                     } else {
                         const bool is_k = n < t.nq + t.nk;
                         const int c = is_k ? n - t.nq : n - t.nq - t.nk;
@@ -421,8 +423,9 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[
                 const QkvTarget& t = a.qkv;
                 const int n = tile_n * 256 + wn * WN + pass * 64 + c * 4;
                 if (n >= a.N) continue;
-                const int b = m / t.seqlen;
-                const int pos = t.start_pos + (m - b * t.seqlen);
+                const int mm = t.row0 + m;    // row of the bsz x seqlen rectangle
+                const int b = mm / t.seqlen;
+                const int pos = t.start_pos + (mm - b * t.seqlen);
                 float4 y = v;
                 if (n < t.nq + t.nk) {
                     // (cos, sin) of the pairs (n, n + 1) and (n + 2, n + 3)
@@ -434,7 +437,7 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[
                     y.w = v.w * cs.z + v.z * cs.w;
                 }
                 if (n < t.nq) {
-                    *reinterpret_cast<float4*>(t.q + (size_t)m * t.nq + n) =
+                    *reinterpret_cast<float4*>(t.q + (size_t)mm * t.nq + n) =
                         float4{round_bf16(y.x), round_bf16(y.y), round_bf16(y.z), round_bf16(y.w)};
                 } else {
                     const bool is_k = n < t.nq + t.nk;
@@ -663,6 +666,43 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
     }
     if (a.M <= 256) return launch_tile<128, 64, 2, 2, EPI>(a, s);
     if (a.M <= 2048) return launch_tile<128, 128, 2, 2, EPI>(a, s);
+    if constexpr (EPI == EPI_QKV || EPI == EPI_RESID || EPI == EPI_SWIGLU) {
+        // 256 x 256 tiles run one per CU, in rounds of kCUs.  When the last round would be
+        // nearly empty, the last one or two tile rows (at most kShortRows rows) go to the
+        // split-K short path instead, which spreads them over every CU; the choice follows a
+        // cost estimate in rounds (the split rows' share of a round, plus a fixed charge for
+        // the extra launches and the reduce pass).
+        if (a.part) {
+            const int ncols = (EPI == EPI_SWIGLU) ? kBigBN / 2 : kBigBN;
+            const int n_tn = (a.N + ncols - 1) / ncols, n_tm = (a.M + 255) / 256;
+            auto rounds = [&](int tiles) { return (double)((tiles + kCUs - 1) / kCUs); };
+            double best = rounds(n_tm * n_tn);
+            int best_t = 0;
+            for (int t = 1; t <= 2; ++t) {
+                const int M1 = (n_tm - t) * 256, M2 = a.M - M1;
+                if (M1 <= 2048 || M2 > kShortRows) continue;
+                const double r = rounds((n_tm - t) * n_tn) + 1.3 * M2 / 256.0 * n_tn / kCUs + 0.15;
+                if (r < best) {
+                    best = r;
+                    best_t = t;
+                }
+            }
+            if (best_t > 0) {
+                const int M1 = (n_tm - best_t) * 256, M2 = a.M - M1;
+                GemmArgs a1 = a;
+                a1.M = M1;
+                const hipError_t e = launch_big<256, EPI>(a1, s);
+                if (e != hipSuccess) return e;
+                GemmArgs a2 = a;
+                a2.M = M2;
+                a2.a = static_cast<const uint16_t*>(a.a) + (size_t)M1 * a.lda;
+                if constexpr (EPI == EPI_RESID) a2.resid = a.resid + (size_t)M1 * a.ldr;
+                if constexpr (EPI == EPI_SWIGLU) a2.out16 = static_cast<uint16_t*>(a.out16) + (size_t)M1 * a.ldo16;
+                if constexpr (EPI == EPI_QKV) a2.qkv.row0 = a.qkv.row0 + M1;
+                return M2 <= 128 ? launch_big<128, EPI>(a2, s) : launch_big<256, EPI>(a2, s);
+            }
+        }
+    }
     return launch_big<256, EPI>(a, s);
 }
 

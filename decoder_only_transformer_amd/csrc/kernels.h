@@ -53,6 +53,8 @@ struct QkvTarget {
     int max_seq;
     int start_pos, seqlen;
     const StepState* st;   // if set, start_pos comes from st->pos
+    int row0;              // prefill GEMM paths: rows of the launch start at this row of the
+                           // bsz x seqlen rectangle (decode paths: 0)
 };
 
 // y[m][n] = sum_k x[m][k] * W[n][k]  (VALU, fp32 activations, weights streamed once per

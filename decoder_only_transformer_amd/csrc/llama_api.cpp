@@ -33,6 +33,7 @@ constexpr int kMaxSplitK = 8;      // K splits of a residual GEMM at small prefi
 constexpr int kSplitKRows = 512;   // prefill rows up to which split-K is considered
 constexpr size_t kSplitKRowsCap = 2048;  // splits x rows the split-K workspace holds
 constexpr int kSkinnyRows = 4;      // bf16 decode batches above this use the skinny MFMA kernel
+constexpr int kSkinnyMaxRows = 32;  // ... up to this many rows; larger ones the prefill GEMMs
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -364,7 +365,8 @@ llama_status block_skinny(const llama_ctx* c, int l, int M, int start_pos, hipSt
 }
 
 // One transformer block on the bf16 MFMA path for T = bsz*seqlen prefill rows.
-llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_pos, hipStream_t s) {
+llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_pos, hipStream_t s,
+                        bool decode = false) {
     const llama_layer_weights& W = c->layers[l];
     const int D = c->a.dim, F = c->a.hidden_dim;
     float* h = c->at<float>(c->L.h32);
@@ -379,7 +381,11 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
     g.part = c->at<float>(c->L.splitk); g.part_cap = c->L.splitk_floats;
     LAUNCH(c, LLAMA_KC_GEMM_QKV, s, launch_gemm(EPI_QKV, g, s));
 
-    if (c->hd == 64 || c->hd == 128) {
+    if (decode) {
+        // single-token rows: the decode attention kernel (key splits allowed)
+        llama_status st = run_attention(c, l, T, 1, start_pos, act, true, true, s);
+        if (st != LLAMA_OK) return st;
+    } else if (c->hd == 64 || c->hd == 128) {
         FlashArgs fa{};
         fa.q = c->at<const float>(c->L.q32);
         fa.cache_k = c->kcache(l);
@@ -539,6 +545,16 @@ static llama_status decode_plan(llama_ctx* c, const int32_t* d_tokens, int64_t l
     float* h = c->at<float>(c->L.h32);
     HIP_TRY(launch_embed(d_tokens, ld_tokens, bsz, 1, c->w.tok_embeddings, c->bf16 ? 1 : 0,
                          c->a.vocab_size, D, h, st, s));
+    if (c->bf16 && bsz > kSkinnyMaxRows) {
+        // more rows than the skinny kernels take: the prefill GEMMs with the decode attention
+        // (launch arguments only, so not under graph capture)
+        if (st) return LLAMA_ERR_UNSUPPORTED;
+        for (int l = 0; l < c->a.n_layers; ++l) {
+            const llama_status r = block_mfma(c, l, bsz, 1, start_pos, s, true);
+            if (r != LLAMA_OK) return r;
+        }
+        return final_logits(c, h, D, bsz, d_logits, s);
+    }
     const bool skinny = c->bf16 && bsz > kSkinnyRows;
     for (int l = 0; l < c->a.n_layers; ++l) {
         const llama_status r = skinny ? block_skinny(c, l, bsz, start_pos, s, st, graph_splits)
@@ -591,7 +607,7 @@ llama_status llama_decode_step(llama_ctx* c, const int32_t* d_tokens, int64_t ld
         ld_tokens < 1)
         return LLAMA_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (!c->use_graphs || c->prof_class != 0)
+    if (!c->use_graphs || c->prof_class != 0 || (c->bf16 && bsz > kSkinnyMaxRows))
         return decode_plan(c, d_tokens, ld_tokens, bsz, start_pos, d_logits, s, nullptr, 0);
     // graph replay: per-step values go to the device step state, then one graph launch
     const int splits = decode_splits(c, bsz, start_pos + 1);

@@ -166,8 +166,9 @@ __global__ void rope_scatter_kernel(const float* y, int splits, int64_t ldy, int
         y0 += v.x;
         y1 += v.y;
     }
-    const int b = m / t.seqlen;
-    const int pos = t.start_pos + (m - b * t.seqlen);
+    const int mm = t.row0 + m;             // row of the bsz x seqlen rectangle
+    const int b = mm / t.seqlen;
+    const int pos = t.start_pos + (mm - b * t.seqlen);
     if (n0 < t.nq + t.nk) {
         const float2 cs = t.rope[(size_t)pos * (t.head_dim / 2) + (n0 % t.head_dim) / 2];
         const float r0 = y0 * cs.x - y1 * cs.y;
@@ -176,7 +177,7 @@ __global__ void rope_scatter_kernel(const float* y, int splits, int64_t ldy, int
         y1 = r1;
     }
     if (n0 < t.nq) {
-        *reinterpret_cast<float2*>(t.q + (size_t)m * t.nq + n0) = make_float2(round_bf16(y0), round_bf16(y1));
+        *reinterpret_cast<float2*>(t.q + (size_t)mm * t.nq + n0) = make_float2(round_bf16(y0), round_bf16(y1));
         return;
     }
     const bool is_k = n0 < t.nq + t.nk;

@@ -141,7 +141,9 @@ llama_status llama_prefill(llama_ctx *c, const int32_t *d_tokens, int64_t ld_tok
 /* One single-token step, Transformer.forward(tokens[:, None], start_pos): row b's token is
  * d_tokens[b*ld_tokens].  Writes K/V at position start_pos, attends over
  * [0, start_pos] (no mask: every cached key is visible), and writes fp32 logits
- * [bsz][vocab_size] to d_logits.
+ * [bsz][vocab_size] to d_logits.  Any bsz up to max_batch_size is served: bf16 batches of
+ * 5..32 rows stream the weights through the skinny MFMA kernels, larger ones run the
+ * prefill GEMMs with the single-token attention kernel.
  * Errors: INVALID_ARG if bsz < 1, bsz > max_batch_size, start_pos < 0,
  * start_pos >= max_seq_len, ld_tokens < 1, or a NULL pointer. */
 llama_status llama_decode_step(llama_ctx *c, const int32_t *d_tokens, int64_t ld_tokens,

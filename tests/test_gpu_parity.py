@@ -33,6 +33,14 @@ COS_MIN = 0.999
 MARGIN = 0.1
 
 
+def greedy_margin(tol):
+    """Oracle top-1/top-2 margin above which the GPU's greedy token must equal the oracle's.
+    If every logit is within tol, a margin above 2 * tol forces the pick; at the stated bar
+    (3e-2) that is below 0.1, so 0.1 holds there, and with the bar derived at depth the
+    rule scales with it (reading R19)."""
+    return max(MARGIN, 2.0 * tol)
+
+
 def say(msg):
     print(msg, flush=True)
     sys.stdout.flush()
@@ -92,7 +100,7 @@ def verify_generate(wl, prompts, tokens, call_logits, tf_logits, tol, cos_min=No
         margin = srt[:, -1] - srt[:, -2]
         top = np.argmax(o, -1)
         for b in range(len(prompts)):
-            if p + 1 >= len(prompts[b]) and margin[b] > MARGIN:
+            if p + 1 >= len(prompts[b]) and margin[b] > greedy_margin(tol):
                 assert tokens[b, p + 1] == top[b], f"greedy token differs at row {b} pos {p + 1}"
                 checked += 1
     say(f"  max|dlogit|={worst:.3e} min cos={worst_cos:.6f} greedy tokens checked={checked}")
@@ -377,6 +385,26 @@ def test_llama2_7b_widths_one_layer_generate_matches_oracle():
     a = oracle.args_from_workload(wl)
     tf = oracle.teacher_forced_logits(a, host_weights(wl, W), tokens[:, :-1], np.float32, storage="bf16")
     verify_generate(wl, prompts, tokens, logits, tf, BF16_TOL, COS_MIN)
+
+
+@pytest.mark.timeout(600)
+def test_llama2_7b_widths_one_layer_tail_rows_match_oracle():
+    """33 x 256 prefill rows at the 7B widths: the 256x256 tiles of the first 8192 rows fill
+    whole rounds of one tile per CU, so the last 256 rows of every projection (q/k/v with
+    RoPE and the cache append, wo and w2 with the residual add, the SiLU gate) run on the
+    split-K path with its reduce passes.  The first and the last batch row (all of whose
+    prompt rows are in that tail) are checked against the oracle."""
+    wl = synth.WORKLOADS["llama2_7b_b1"].with_(name="llama2_7b_b33_one_layer", n_layers=1, batch=33,
+                                               prompt_len=256, gen_steps=4)
+    say(f"case {wl.name}")
+    W = synth.gen_weights(wl, device="cuda")
+    prompts = synth.prompts(wl)
+    assert len(prompts) * min(len(p) for p in prompts) == 33 * 256
+    tokens, logits, _ = gpu_generate(wl, W, prompts)
+    rows = [0, 32]
+    a = oracle.args_from_workload(wl)
+    tf = oracle.teacher_forced_logits(a, host_weights(wl, W), tokens[rows, :-1], np.float32, storage="bf16")
+    verify_generate(wl, [prompts[r] for r in rows], tokens[rows], logits[:, rows], tf, BF16_TOL, COS_MIN)
 
 
 @pytest.mark.timeout(900)
