@@ -311,14 +311,16 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
 
 // ---------------------------------------------------------------------------------------
 // LDS-ring variant: BM x 256 tiles (BM = 256: 8 waves as 4 x 2 of 64 x 128; BM = 128: 8 waves
-// as 2 x 4 of 64 x 64), K in stages of 32 through a 4-deep LDS ring filled by
-// global_load_lds_dwordx4 (global -> LDS without registers), loads issued 3 stages ahead.
-// Long prefills use it as is; short ones (a few hundred rows, where the weights are the
-// traffic) split K over gridDim.z so enough workgroups stream the weights: each split
-// stores its raw fp32 tile [z][M][B row] and a reduce pass applies the epilogue.  A wave's load instruction fills 1 KB of LDS contiguously
-// (lane i -> bytes 16i..16i+15), i.e. 16 rows x 4 chunks of a 64-byte row; each lane fetches
-// the global chunk (chunk ^ swz(row)), so a fragment read of (row, chunk) finds it at slot
-// chunk ^ swz(row) and the rows of a fragment land on distinct banks without padding.
+// as 2 x 4 of 64 x 64), K in stages of 32 through an LDS ring (4 slots at BM = 256, 6 at 128)
+// filled by global_load_lds_dwordx4 (global -> LDS without registers), loads issued NS - 1
+// stages ahead.  Long prefills use it with the LDS-staged epilogue below; short ones (a few
+// hundred rows, where the weights are the traffic) split K over gridDim.z so enough
+// workgroups stream the weights: each split stores its raw fp32 tile [z][M][B row] and a
+// reduce pass applies the epilogue.  A wave's load instruction fills 1 KB of LDS
+// contiguously (lane i -> bytes 16i..16i+15), i.e. 16 rows x 4 chunks of a 64-byte row; each
+// lane fetches the global chunk (chunk ^ swz(row)), so a fragment read of (row, chunk) finds
+// it at slot chunk ^ swz(row) and the rows of a fragment land on distinct banks without
+// padding.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 

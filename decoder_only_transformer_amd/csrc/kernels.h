@@ -131,8 +131,9 @@ struct FlashArgs {
 };
 
 hipError_t launch_flash_prefill(const FlashArgs& a, hipStream_t s);
-hipError_t launch_rope_scatter(const float* y, int T, const QkvTarget& t, hipStream_t s);
-// Same from the sum of `splits` partial projections [splits][T][ldy] (in split order).
+// RoPE, q store and K/V cache append from the sum of `splits` partial [wq; wk; wv]
+// projections [splits][T][ldy] (summed in split order); row m is row t.row0 + m of the
+// bsz x seqlen rectangle.
 hipError_t launch_rope_scatter_parts(const float* y, int splits, int64_t ldy, int T, const QkvTarget& t,
                                      hipStream_t s);
 hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, const void* table,

@@ -196,9 +196,6 @@ hipError_t launch_rope_scatter_parts(const float* y, int splits, int64_t ldy, in
     return hipGetLastError();
 }
 
-hipError_t launch_rope_scatter(const float* y, int T, const QkvTarget& t, hipStream_t s) {
-    return launch_rope_scatter_parts(y, 1, (int64_t)(t.nq + 2 * t.nk), T, t, s);
-}
 
 hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, const void* table,
                         int wbf16, int vocab, int dim, float* h, const StepState* st, hipStream_t s) {
