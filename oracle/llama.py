@@ -258,6 +258,48 @@ def argmax_lowest(logits: np.ndarray) -> np.ndarray:
     return np.argmax(logits, axis=-1)   # numpy returns the first maximal index
 
 
+def sample_top_p(logits: np.ndarray, temperature: float, top_p: float, u: np.ndarray):
+    """Temperature + nucleus sampling of one token per row ([AG] 8.5, temperature > 0: softmax
+    of logits / temperature, then sample_top_p; [AG] 6.3 and [ST] "Sampling, Stopping, and the
+    Chat Template": sort the probabilities descending, zero the tokens beyond the cumulative
+    top-p mass, renormalise, draw one token from the multinomial).  float64 throughout.
+
+    Readings: R20 a token is beyond the top-p mass when the mass of the tokens sorted before
+    it exceeds top_p (so the first token always stays; top_p >= 1 keeps every token); R21 equal
+    probabilities sort by lower token index first; R22 the draw is the inverse CDF of the
+    renormalised kept distribution in sorted order at the caller's uniform u[b] in [0, 1),
+    i.e. the first sorted token whose cumulative mass exceeds u[b]; R23 the returned log-prob
+    is log_softmax of the raw (untempered) logits at the drawn token.
+
+    logits: (B, V); u: (B,).  Returns (tokens int64 (B,), logprobs float64 (B,))."""
+    x = np.asarray(logits, dtype=np.float64)
+    if not np.isfinite(x).all():
+        raise ValueError("non-finite logit")
+    B, V = x.shape
+    z = x / float(temperature)
+    z = z - z.max(axis=-1, keepdims=True)
+    p = np.exp(z)
+    p = p / p.sum(axis=-1, keepdims=True)
+    lse = np.log(np.exp(x - x.max(axis=-1, keepdims=True)).sum(axis=-1)) + x.max(axis=-1)
+    tokens = np.empty(B, dtype=np.int64)
+    logprobs = np.empty(B, dtype=np.float64)
+    for b in range(B):
+        order = np.lexsort((np.arange(V), -p[b]))          # descending p, then lower index
+        ps = p[b][order]
+        before = np.cumsum(ps) - ps                          # mass sorted before each token
+        kept = ps.copy()
+        if top_p < 1.0:
+            kept[before > top_p] = 0.0
+        kept = kept / kept.sum()
+        cdf = np.cumsum(kept)
+        n_kept = int((kept > 0).sum()) if top_p < 1.0 else V
+        i = int(np.searchsorted(cdf, float(u[b]), side="right"))   # first cdf > u
+        i = min(i, n_kept - 1)
+        tokens[b] = order[i]
+        logprobs[b] = x[b, order[i]] - lse[b]
+    return tokens, logprobs
+
+
 def greedy_generate(model: Oracle, prompts: List[List[int]], max_gen_len: int,
                     eos_id: int = -1, pad_id: int = -1):
     """Llama.generate at temperature 0 ([AG] 8.5; [ST] "Sampling, Stopping"): prompts sit

@@ -413,3 +413,60 @@ def test_bf16_storage_keeps_prefill_equal_to_decode_and_cache_in_bf16():
     plain = oracle.Oracle(a, W, 2, dtype=np.float64).forward(tokens, 0)
     d = np.abs(plain - lf).max()
     assert 1e-6 < d < 5e-2     # rounding changes the logits, a little
+
+
+# ----------------------------------------------------------------------------- sampling
+# [AG] 8.5 (temperature > 0 branch), 6.3 and [ST] "Sampling, Stopping, and the Chat Template";
+# the cases [AG] 8.9 lists for sample_top_p (greedy threshold, threshold below the largest
+# single mass), hand-derived draws on a known distribution, and closed forms.
+
+def test_sample_top_p_known_distribution_hand_derived():
+    # p = [0.1, 0.4, 0.2, 0.3]; sorted 0.4 (t1), 0.3 (t3), 0.2 (t2), 0.1 (t0) with mass before
+    # 0, 0.4, 0.7, 0.9; top_p = 0.6 keeps t1 and t3, renormalised 4/7 and 3/7
+    logits = np.log(np.array([[0.1, 0.4, 0.2, 0.3]]))
+    for u, want in [(0.0, 1), (0.5, 1), (4 / 7 - 1e-9, 1), (4 / 7 + 1e-9, 3), (0.999999, 3)]:
+        tok, _ = oracle.sample_top_p(logits, 1.0, 0.6, np.array([u]))
+        assert tok[0] == want, (u, tok)
+    # top_p = 0.75 also keeps t2 (mass before it 0.7 <= 0.75): 4/9, 3/9, 2/9
+    for u, want in [(0.44, 1), (0.45, 3), (0.77, 3), (0.78, 2)]:
+        tok, _ = oracle.sample_top_p(logits, 1.0, 0.75, np.array([u]))
+        assert tok[0] == want, (u, tok)
+
+
+def test_sample_top_p_threshold_below_largest_mass_and_greedy():
+    rng = np.random.default_rng(7)
+    logits = rng.normal(0.0, 2.0, size=(6, 50))
+    top = np.argmax(logits, axis=-1)
+    p = np.exp(logits - logits.max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    for top_p in (0.0, float(p.max(-1).min()) * 0.99):
+        for u in (0.0, 0.3, 0.999):
+            tok, _ = oracle.sample_top_p(logits, 1.0, top_p, np.full(6, u))
+            assert (tok == top).all()
+
+
+def test_sample_top_p_draw_frequencies_are_the_distribution():
+    # evenly spaced u: each token is drawn for a fraction of u equal to its probability
+    logits = np.log(np.array([[0.05, 0.25, 0.1, 0.35, 0.25]]))
+    n = 20000
+    u = (np.arange(n) + 0.5) / n
+    toks = np.array([oracle.sample_top_p(logits, 1.0, 1.0, u[i:i + 1])[0][0] for i in range(0, n, 1)])
+    freq = np.bincount(toks, minlength=5) / n
+    assert np.allclose(freq, [0.05, 0.25, 0.1, 0.35, 0.25], atol=2.0 / n)
+    # ties sort by token index: t1 and t4 both 0.25, t1 first (cdf 0.35 -> 0.6 -> 0.85)
+    assert oracle.sample_top_p(logits, 1.0, 1.0, np.array([0.61]))[0][0] == 4
+    assert oracle.sample_top_p(logits, 1.0, 1.0, np.array([0.59]))[0][0] == 1
+
+
+def test_sample_top_p_temperature_closed_form_and_logprob():
+    p1 = np.array([0.1, 0.4, 0.2, 0.3])
+    logits = np.log(p1)[None] + 3.0          # shift: softmax and log_softmax unchanged
+    # temperature 2 -> probabilities proportional to sqrt(p1)
+    q = np.sqrt(p1) / np.sqrt(p1).sum()
+    n = 8000
+    u = (np.arange(n) + 0.5) / n
+    toks = np.array([oracle.sample_top_p(logits, 2.0, 1.0, u[i:i + 1])[0][0] for i in range(n)])
+    assert np.allclose(np.bincount(toks, minlength=4) / n, q, atol=2.0 / n)
+    # the log-prob is of the untempered softmax
+    tok, lp = oracle.sample_top_p(logits, 2.0, 1.0, np.array([0.0]))
+    assert abs(lp[0] - np.log(p1[tok[0]])) < 1e-12
