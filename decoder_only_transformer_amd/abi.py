@@ -23,7 +23,7 @@ LLAMA_FP32 = 1
 
 # Every symbol include/llama_mi355x.h declares.
 EXPORTED = ("llama_check_args", "llama_workspace_bytes", "llama_init", "llama_prefill",
-            "llama_decode_step", "llama_argmax", "llama_select_next", "llama_destroy",
+            "llama_decode_step", "llama_argmax", "llama_sample_top_p", "llama_select_next", "llama_destroy",
             "llama_status_str", "llama_profile_select", "llama_profile_read")
 
 # Kernel classes for llama_profile_select (llama_kernel_class in the header).
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.llama_decode_step.restype = ctypes.c_int
         L.llama_argmax.argtypes = [P, I32, I32, I64, P, P]
         L.llama_argmax.restype = ctypes.c_int
+        L.llama_sample_top_p.argtypes = [P, I32, I32, I64, ctypes.c_float, ctypes.c_float, P, P, P, P]
+        L.llama_sample_top_p.restype = ctypes.c_int
         L.llama_select_next.argtypes = [P, P, I64, I32, P, I32, P]
         L.llama_select_next.restype = ctypes.c_int
         L.llama_destroy.argtypes = [P]
@@ -120,6 +122,12 @@ def llama_decode_step(ctx: int, d_tokens: int, ld_tokens: int, bsz: int, start_p
 def llama_argmax(d_logits: int, bsz: int, vocab: int, row_stride: int, d_out: int,
                  stream: int) -> int:
     return lib().llama_argmax(d_logits, bsz, vocab, row_stride, d_out, stream)
+
+
+def llama_sample_top_p(d_logits: int, bsz: int, vocab: int, row_stride: int, temperature: float,
+                       top_p: float, d_uniform: int, d_out: int, d_logprob: int, stream: int) -> int:
+    return lib().llama_sample_top_p(d_logits, bsz, vocab, row_stride, temperature, top_p, d_uniform, d_out,
+                                    d_logprob, stream)
 
 
 def llama_select_next(d_next: int, d_tokens: int, ld_tokens: int, cur_pos: int,

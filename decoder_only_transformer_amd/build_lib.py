@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libllama_mi355x.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["gemv.hip", "gemm.hip", "attention.hip", "flash_attention.hip", "skinny.hip", "misc.hip", "llama_api.cpp"]
+SOURCES = ["gemv.hip", "gemm.hip", "attention.hip", "flash_attention.hip", "skinny.hip", "misc.hip", "sampling.hip",
+           "llama_api.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function"]

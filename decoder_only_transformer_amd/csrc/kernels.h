@@ -130,6 +130,10 @@ struct FlashArgs {
     float scale;
 };
 
+// Temperature + top-p draw, one token per row (vocab <= kMaxSampleVocab); see sampling.hip.
+constexpr int kMaxSampleVocab = 32768;
+hipError_t launch_sample_top_p(const float* logits, int bsz, int vocab, int64_t stride, float temperature,
+                               float top_p, const float* uniform, int32_t* out, float* logprob, hipStream_t s);
 hipError_t launch_flash_prefill(const FlashArgs& a, hipStream_t s);
 // RoPE, q store and K/V cache append from the sum of `splits` partial [wq; wk; wv]
 // projections [splits][T][ldy] (summed in split order); row m is row t.row0 + m of the

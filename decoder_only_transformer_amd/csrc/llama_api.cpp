@@ -626,6 +626,18 @@ llama_status llama_argmax(const float* d_logits, int32_t bsz, int32_t vocab, int
     return LLAMA_OK;
 }
 
+llama_status llama_sample_top_p(const float* d_logits, int32_t bsz, int32_t vocab, int64_t row_stride,
+                                float temperature, float top_p, const float* d_uniform, int32_t* d_out,
+                                float* d_logprob, void* stream) {
+    if (!d_logits || !d_uniform || !d_out || bsz < 1 || vocab < 1 || row_stride < vocab ||
+        !(temperature > 0.f) || !std::isfinite(temperature) || !(top_p >= 0.f))
+        return LLAMA_ERR_INVALID_ARG;
+    if (vocab > kMaxSampleVocab) return LLAMA_ERR_UNSUPPORTED;
+    HIP_TRY(launch_sample_top_p(d_logits, bsz, vocab, row_stride, temperature, top_p, d_uniform, d_out, d_logprob,
+                                static_cast<hipStream_t>(stream)));
+    return LLAMA_OK;
+}
+
 llama_status llama_select_next(const int32_t* d_next, int32_t* d_tokens, int64_t ld_tokens,
                                int32_t cur_pos, const int32_t* d_prompt_len, int32_t bsz,
                                void* stream) {

@@ -99,13 +99,25 @@ def select_next(nxt: torch.Tensor, tokens: torch.Tensor, cur_pos: int, prompt_le
         tokens.shape[0], stream_handle()))
 
 
+def sample_top_p(logits: torch.Tensor, temperature: float, top_p: float, uniform: torch.Tensor,
+                 out: torch.Tensor, logprob: torch.Tensor = None) -> None:
+    """Temperature + top-p draw per row at the given uniforms (llama_sample_top_p)."""
+    check("llama_sample_top_p", abi.llama_sample_top_p(
+        logits.data_ptr(), logits.shape[0], logits.shape[1], logits.stride(0), float(temperature),
+        float(top_p), uniform.data_ptr(), out.data_ptr(), logprob.data_ptr() if logprob is not None else 0,
+        stream_handle()))
+
+
 class GreedyRun:
-    """Device buffers and schedule of one greedy generate call (generate at temperature 0:
-    prompts left-aligned in a pad-filled rectangle, one prefill of the shortest prompt,
-    then one single-token call per position; prompt tokens are never overwritten)."""
+    """Device buffers and schedule of one generate call: prompts left-aligned in a pad-filled
+    rectangle, one prefill of the shortest prompt, then one single-token call per position;
+    prompt tokens are never overwritten.  At temperature 0 the pick is the argmax; above it,
+    the temperature + top-p draw with one uniform per (call, row), drawn up front from a
+    seeded generator (`uniforms`, on the device) so no step waits on the host."""
 
     def __init__(self, model: LlamaModel, prompts: Sequence[Sequence[int]], max_gen_len: int,
-                 keep_logits: bool = True, pad_id: int = -1):
+                 keep_logits: bool = True, pad_id: int = -1, temperature: float = 0.0,
+                 top_p: float = 0.9, seed: int = 0):
         self.model = model
         self.bsz = len(prompts)
         self.min_len = min(len(p) for p in prompts)
@@ -123,6 +135,12 @@ class GreedyRun:
         self.logits = torch.empty((nbuf, self.bsz, V), dtype=torch.float32, device="cuda")
         self.next = torch.empty(self.bsz, dtype=torch.int32, device="cuda")
         self.keep = keep_logits
+        self.temperature, self.top_p = float(temperature), float(top_p)
+        if self.temperature > 0.0:
+            import numpy as np
+            u = np.random.Generator(np.random.Philox(seed)).random((self.n_calls, self.bsz), dtype=np.float32)
+            self.uniforms = torch.from_numpy(u).cuda()
+            self.logprobs = torch.empty((self.n_calls, self.bsz), dtype=torch.float32, device="cuda")
 
     def reset(self) -> None:
         self.tokens.copy_(self.tokens0)
@@ -130,10 +148,16 @@ class GreedyRun:
     def _buf(self, i: int) -> torch.Tensor:
         return self.logits[i if self.keep else 0]
 
+    def _pick(self, i: int, lg: torch.Tensor) -> None:
+        if self.temperature > 0.0:
+            sample_top_p(lg, self.temperature, self.top_p, self.uniforms[i], self.next, self.logprobs[i])
+        else:
+            argmax(lg, self.next)
+
     def prefill(self) -> None:
         lg = self._buf(0)
         self.model.prefill(self.tokens, self.bsz, self.min_len, 0, lg)
-        argmax(lg, self.next)
+        self._pick(0, lg)
         select_next(self.next, self.tokens, self.min_len, self.prompt_len)
 
     def decode(self, i: int) -> None:
@@ -141,7 +165,7 @@ class GreedyRun:
         cur = self.min_len + i
         lg = self._buf(i)
         self.model.decode_step(self.tokens, self.bsz, cur - 1, cur - 1, lg)
-        argmax(lg, self.next)
+        self._pick(i, lg)
         select_next(self.next, self.tokens, cur, self.prompt_len)
 
     def run(self) -> None:

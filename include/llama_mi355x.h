@@ -156,6 +156,27 @@ llama_status llama_decode_step(llama_ctx *c, const int32_t *d_tokens, int64_t ld
 llama_status llama_argmax(const float *d_logits, int32_t bsz, int32_t vocab,
                           int64_t row_stride, int32_t *d_out, void *stream);
 
+/* Temperature + top-p draw ([AG] section 8.5, temperature > 0: softmax(logits / temperature)
+ * and then sample_top_p, which [ST] "Sampling, Stopping, and the Chat Template" describes as
+ * sort descending, zero the tokens beyond the cumulative top-p mass, renormalise, draw one
+ * token).  For each row b in [0, bsz), over v in [0, vocab):
+ *   p = softmax(d_logits[b*row_stride + v] / temperature);
+ *   tokens sorted by descending p, equal p by lower index;
+ *   a token is dropped when the mass sorted before it exceeds top_p (the first token always
+ *   stays; top_p >= 1 keeps every token); the kept mass is renormalised;
+ *   d_out[b] = the first sorted kept token whose cumulative mass exceeds d_uniform[b]
+ *   (a caller-supplied uniform in [0, 1); values outside are clamped into it).
+ * If d_logprob is not NULL, d_logprob[b] = log_softmax(d_logits[b, :])[d_out[b]] (untempered).
+ * Logits must be finite.  Buffers are device memory owned by the caller; d_out and d_logprob
+ * are written only.  Sums are fp32 workgroup reductions: a uniform within ~1e-6 of a
+ * cumulative boundary may select the neighbouring token relative to exact arithmetic.
+ * Errors: INVALID_ARG if bsz < 1, vocab < 1, row_stride < vocab, temperature <= 0 or not
+ * finite, top_p < 0 or NaN, or a NULL d_logits / d_uniform / d_out; UNSUPPORTED if
+ * vocab > 32768. */
+llama_status llama_sample_top_p(const float *d_logits, int32_t bsz, int32_t vocab, int64_t row_stride,
+                                float temperature, float top_p, const float *d_uniform, int32_t *d_out,
+                                float *d_logprob, void *stream);
+
 /* Generate's token bookkeeping (section 8.5, torch.where on input_text_mask): for each row
  * b, if cur_pos >= d_prompt_len[b] then d_tokens[b*ld_tokens + cur_pos] = d_next[b];
  * otherwise the prompt token already there is kept.

@@ -512,3 +512,123 @@ def test_full_width_first_layers_generate_rows_match_oracle(name):
     tokens, logits, _ = gpu_generate(wl, W, prompts)
     assert np.isfinite(logits).all()
     check_rows(wl, W, prompts, tokens, logits, rows=[0])
+
+
+# ----------------------------------------------------------------------------- sampling
+
+def _draw_ok(logits64, temperature, top_p, u, tok, tol):
+    """The GPU's draw equals the oracle's for top_p and u each moved by at most tol (the GPU
+    sums in fp32, so a draw point or cutoff within ~1e-6 of a boundary may fall either way)."""
+    for dp in (0.0, -tol, tol):
+        for du in (0.0, -tol, tol):
+            uu = np.clip(np.array([u + du]), 0.0, 1.0 - 1e-12)
+            if oracle.sample_top_p(logits64[None], temperature, max(0.0, top_p + dp), uu)[0][0] == tok:
+                return True
+    return False
+
+
+@pytest.mark.parametrize("vocab", [7, 1000, 32000])
+def test_sample_top_p_matches_oracle(vocab):
+    """llama_sample_top_p against the oracle, with the same uniforms.  Logits are a shuffled
+    evenly spaced grid (no two probabilities within fp32 rounding of each other), plus a row
+    of exactly equal logits (ties sort by index) and a row with one dominant token."""
+    rng = np.random.default_rng(60 + vocab)
+    B = 16
+    grid = np.linspace(-6.0, 6.0, vocab)
+    logits = np.stack([rng.permutation(grid) for _ in range(B)]).astype(np.float32)
+    logits[0, :] = 0.5
+    logits[1, rng.integers(vocab)] = 40.0
+    L = torch.from_numpy(logits).cuda()
+    out = torch.empty(B, dtype=torch.int32, device="cuda")
+    lp = torch.empty(B, dtype=torch.float32, device="cuda")
+    n_exact = n_near = 0
+    for temperature, top_p in [(1.0, 0.9), (0.7, 0.5), (1.5, 1.0), (1.0, 0.0), (2.0, 0.95), (0.3, 0.99)]:
+        u = rng.random(B).astype(np.float32)
+        U = torch.from_numpy(u).cuda()
+        runtime.sample_top_p(L, temperature, top_p, U, out, lp)
+        torch.cuda.synchronize()
+        g_tok, g_lp = out.cpu().numpy(), lp.cpu().numpy()
+        r_tok, r_lp = oracle.sample_top_p(logits.astype(np.float64), temperature, top_p, u.astype(np.float64))
+        for b in range(B):
+            if g_tok[b] == r_tok[b]:
+                n_exact += 1
+            else:
+                assert _draw_ok(logits[b].astype(np.float64), temperature, top_p, float(u[b]), g_tok[b], 2e-5), \
+                    (temperature, top_p, b, g_tok[b], r_tok[b])
+                n_near += 1
+            assert abs(g_lp[b] - r_lp[b]) <= 1e-4 * max(1.0, abs(r_lp[b])), (b, g_lp[b], r_lp[b])
+        if top_p == 0.0:
+            assert (g_tok == np.argmax(logits, -1)).all()
+    say(f"  vocab {vocab}: {n_exact} draws equal to the oracle's, {n_near} at a boundary within 2e-5")
+    # every other draw was checked above; fp32 sums over up to 32768 terms put a few draws
+    # per hundred within 2e-5 of a boundary when single probabilities are ~1e-4
+    assert n_near <= 0.1 * (n_exact + n_near)
+
+
+def test_sample_top_p_timing_and_errors():
+    B, V = 32, 32000
+    rng = np.random.default_rng(5)
+    L = torch.from_numpy(rng.normal(0.0, 3.0, size=(B, V)).astype(np.float32)).cuda()
+    U = torch.from_numpy(rng.random(B).astype(np.float32)).cuda()
+    out = torch.empty(B, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        runtime.sample_top_p(L, 0.8, 0.9, U, out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        runtime.sample_top_p(L, 0.8, 0.9, U, out)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / 20 * 1e3
+    import time
+    host = L.cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.sample_top_p(host, 0.8, 0.9, U.cpu().numpy().astype(np.float64))
+    ms_oracle = (time.perf_counter() - t0) * 1e3
+    say(f"  llama_sample_top_p {B} x {V}: {us:.1f} us per call; oracle (fp64 NumPy, one host thread "
+        f"for the sorts): {ms_oracle:.1f} ms")
+    s = runtime.stream_handle()
+    p = L.data_ptr()
+    assert abi.llama_sample_top_p(p, B, V, V, 0.0, 0.9, U.data_ptr(), out.data_ptr(), 0, s) == abi.LLAMA_ERR_INVALID_ARG
+    assert abi.llama_sample_top_p(p, B, V, V, 0.8, -0.1, U.data_ptr(), out.data_ptr(), 0, s) == abi.LLAMA_ERR_INVALID_ARG
+    assert abi.llama_sample_top_p(p, B, V, V - 1, 0.8, 0.9, U.data_ptr(), out.data_ptr(), 0, s) == abi.LLAMA_ERR_INVALID_ARG
+    assert abi.llama_sample_top_p(p, B, V, V, 0.8, 0.9, 0, out.data_ptr(), 0, s) == abi.LLAMA_ERR_INVALID_ARG
+    assert abi.llama_sample_top_p(p, 1, 40000, 40000, 0.8, 0.9, U.data_ptr(), out.data_ptr(), 0, s) == \
+        abi.LLAMA_ERR_UNSUPPORTED
+
+
+def test_tiny_fp32_sampled_generate_matches_oracle():
+    """Generate with temperature 0.8 and top_p 0.9 on the tiny workload: every drawn token is
+    the oracle's draw (teacher-forced logits on the GPU's tokens, the same uniforms), up to
+    boundary cases within the fp32 logit tolerance; log-probs agree."""
+    wl = synth.WORKLOADS["tiny_fp32"]
+    W = synth.gen_weights(wl, device="cuda")
+    prompts = synth.prompts(wl)
+    model = runtime.LlamaModel(args_of(wl, len(prompts)), W)
+    run = runtime.GreedyRun(model, prompts, wl.gen_steps, temperature=0.8, top_p=0.9, seed=11)
+    run.run()
+    torch.cuda.synchronize()
+    tokens = run.tokens.cpu().numpy().astype(np.int64)
+    u = run.uniforms.cpu().numpy().astype(np.float64)
+    g_lp = run.logprobs.cpu().numpy()
+    model.close()
+    a = oracle.args_from_workload(wl)
+    tf = oracle.teacher_forced_logits(a, host_weights(wl, W), tokens[:, :-1], np.float64)
+    min_len = min(len(p) for p in prompts)
+    checked = near = 0
+    for i in range(run.n_calls):
+        pos = min_len - 1 + i
+        for b in range(len(prompts)):
+            if pos + 1 < len(prompts[b]):
+                continue
+            tok = tokens[b, pos + 1]
+            r_tok, r_lp = oracle.sample_top_p(tf[b, pos][None], 0.8, 0.9, u[i, b:b + 1])
+            if r_tok[0] != tok:
+                assert _draw_ok(tf[b, pos], 0.8, 0.9, u[i, b], tok, 1e-3), (i, b)
+                near += 1
+            assert abs(g_lp[i, b] - r_lp[0]) <= 1e-3, (i, b, g_lp[i, b], r_lp[0])
+            checked += 1
+    say(f"  sampled tokens checked={checked} (at a boundary: {near})")
+    assert checked > 0 and near <= 2
+    for b, p in enumerate(prompts):
+        assert tokens[b, :len(p)].tolist() == list(p)
