@@ -208,8 +208,14 @@ SMALL_BF16 = {
                                               n_kv_heads=8, dim=1024, hidden_dim=2816, vocab_size=1000,
                                               batch=32, prompt_len=0, prompt_len_range=(12, 40),
                                               gen_steps=12, weight_seed=16, prompt_seed=116, max_seq_len=96),
-    # long prompts: 4 x 600 = 2400 prefill rows take the large-M GEMM path (ragged tiles)
-    # and the plain-store QKV projection followed by the RoPE / bf16-storage pass
+    # RoPE base 500000 instead of 10000 (theta is an argument of the ABI, not a constant)
+    "theta": synth.WORKLOADS["tiny_fp32"].with_(name="small_bf16_theta", dtype="bf16", n_heads=8,
+                                                n_kv_heads=2, dim=512, hidden_dim=1536, vocab_size=1000,
+                                                batch=2, prompt_len=0, prompt_len_range=(40, 180),
+                                                gen_steps=20, weight_seed=17, prompt_seed=117,
+                                                max_seq_len=256, rope_theta=500000.0),
+    # long prompts: 4 x 600 = 2400 prefill rows take the 256x256 GEMM path (ragged tiles)
+    # with its fused RoPE / cache-append epilogue
     "long": synth.WORKLOADS["tiny_fp32"].with_(name="small_bf16_long", dtype="bf16", n_heads=4,
                                                n_kv_heads=4, dim=512, hidden_dim=1536, vocab_size=1024,
                                                batch=4, prompt_len=600, gen_steps=6, weight_seed=14,
@@ -252,7 +258,7 @@ def test_small_bf16_prefill_equals_token_by_token_decode():
     model.close()
 
 
-@pytest.mark.parametrize("name", ["gqa8", "mha"])
+@pytest.mark.parametrize("name", ["gqa8", "mha", "theta"])
 def test_small_bf16_chunked_prefill_all_positions(name):
     """Prefill in two chunks (the second at start_pos > 0, ragged against the 64-row tiles)
     against the oracle's full forward, every position."""
@@ -279,6 +285,44 @@ def test_small_bf16_chunked_prefill_all_positions(name):
     say(f"  max|dlogit|={d:.3e} min cos={cos:.6f}")
     assert d <= BF16_TOL and cos >= COS_MIN
     model.close()
+
+
+@pytest.mark.timeout(600)
+def test_llama2_7b_widths_one_layer_chunked_prefill_all_positions():
+    """Chunked prefill at the 7B widths: 3 x 1536 tokens in a chunk of 1024 (3072 rows: the
+    256x256 GEMM) and a chunk of 512 at start_pos 1024 (flash attention over a cached prefix
+    twice the chunk), every position against the oracle's full forward (one layer: 3e-2)."""
+    wl = synth.WORKLOADS["llama2_7b_b1"].with_(name="llama2_7b_chunked_one_layer", n_layers=1, batch=3,
+                                               prompt_len=1536, gen_steps=1)
+    say(f"case {wl.name}")
+    W = synth.gen_weights(wl, device="cuda")
+    P = synth.prompts(wl)
+    tok = np.array(P, dtype=np.int32)
+    B, S = tok.shape
+    c = 1024
+    model = runtime.LlamaModel(args_of(wl), W)
+    dtok = torch.from_numpy(tok).cuda()
+    a = torch.empty((B, c, wl.vocab_size), device="cuda")
+    b = torch.empty((B, S - c, wl.vocab_size), device="cuda")
+    model.prefill(dtok, B, c, 0, a, all_positions=True)
+    model.prefill(dtok, B, S - c, c, b, all_positions=True, col=c)
+    torch.cuda.synchronize()
+    got = np.concatenate([a.cpu().numpy(), b.cpu().numpy()], 1)
+    del a, b
+    model.close()
+    a_ = oracle.args_from_workload(wl)
+    base = cached_provider(W)
+    ref = oracle.Oracle(a_, base, B, np.float32, storage="bf16").forward(tok, 0)
+    # the bar over this many positions: the oracle's own spread against a second correct
+    # fp32 evaluation (consistently permuted model and FFN dimensions), as at depth (R19)
+    ref2 = oracle.Oracle(a_, permuted_provider(base, wl.dim, wl.hidden_dim), B, np.float32,
+                         storage="bf16").forward(tok, 0)
+    spread = float(np.abs(ref - ref2).max())
+    tol = max(BF16_TOL, 1.5 * spread)
+    d = np.abs(got - ref).max()
+    cos = ((got * ref).sum(-1) / np.linalg.norm(got, axis=-1) / np.linalg.norm(ref, axis=-1)).min()
+    say(f"  max|dlogit|={d:.3e} min cos={cos:.6f} (oracle spread {spread:.3e} -> bar {tol:.3e})")
+    assert d <= tol and cos >= COS_MIN
 
 
 @pytest.mark.parametrize("name", ["gqa8", "mha", "b6"])
