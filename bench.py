@@ -51,6 +51,16 @@ def prefill_flops(wl, B: int, S: int) -> float:
     return 2.0 * B * S * per_layer * L + 4.0 * hd * H * L * B * S * (S + 1) / 2 + 2.0 * B * V * D
 
 
+def prefill_bytes(wl, B: int, S: int) -> float:
+    """Algorithmic HBM bytes of one prefill call: every weight once (embedding: the B*S rows
+    read), the K/V of the B*S positions written, the last positions' logits written."""
+    D, L, F, V = wl.dim, wl.n_layers, wl.hidden_dim, wl.vocab_size
+    hd, H, KVH = wl.head_dim, wl.n_heads, wl.n_kv_heads
+    e = 2 if wl.dtype == "bf16" else 4
+    per_layer = (H * hd * D + 2 * KVH * hd * D + D * H * hd + 3 * F * D + 2 * D) * e
+    return L * per_layer + V * D * e + D * e + B * S * D * e + B * S * L * 2 * KVH * hd * e + B * V * 4
+
+
 def w13_launch_bytes(wl) -> float:
     """Per launch of the decode [w1;w3] GEMV: both weight matrices, the norm weight, the
     residual rows read and the gated rows written."""
@@ -252,6 +262,7 @@ def main() -> int:
         "decode_hbm_frac": round(decode_hbm_frac, 4),
         "prefill_tflops": round(prefill_tflops, 2),
         "prefill_mfma_frac": round(prefill_tflops / BF16_PEAK_TFLOPS, 4),
+        "prefill_hbm_frac": round(prefill_bytes(wl, B, S) * args.steps / (pre_ms / 1e3) / (HBM_PEAK_GBS * 1e9), 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.profile_class, wl.name),

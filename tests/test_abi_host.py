@@ -106,6 +106,19 @@ def test_calls_reject_bad_arguments(lib):
     assert abi.llama_argmax(16, 0, 10, 10, 16, 0) == abi.LLAMA_ERR_INVALID_ARG
     assert abi.llama_argmax(16, 1, 10, 9, 16, 0) == abi.LLAMA_ERR_INVALID_ARG
     assert abi.llama_argmax(0, 1, 10, 10, 16, 0) == abi.LLAMA_ERR_INVALID_ARG
+    # sampling: every host-checkable precondition, before anything is launched
+    for args in [(0, 2, 10, 10, 0.8, 0.9, 16, 16, 0, 0),           # NULL logits
+                 (16, 0, 10, 10, 0.8, 0.9, 16, 16, 0, 0),          # bsz < 1
+                 (16, 2, 0, 10, 0.8, 0.9, 16, 16, 0, 0),           # vocab < 1
+                 (16, 2, 10, 9, 0.8, 0.9, 16, 16, 0, 0),           # row_stride < vocab
+                 (16, 2, 10, 10, 0.0, 0.9, 16, 16, 0, 0),          # temperature 0 (argmax's case)
+                 (16, 2, 10, 10, float("inf"), 0.9, 16, 16, 0, 0), # temperature not finite
+                 (16, 2, 10, 10, 0.8, -0.5, 16, 16, 0, 0),         # top_p < 0
+                 (16, 2, 10, 10, 0.8, float("nan"), 16, 16, 0, 0), # top_p NaN
+                 (16, 2, 10, 10, 0.8, 0.9, 0, 16, 0, 0),           # NULL uniforms
+                 (16, 2, 10, 10, 0.8, 0.9, 16, 0, 0, 0)]:          # NULL out
+        assert abi.llama_sample_top_p(*args) == abi.LLAMA_ERR_INVALID_ARG, args
+    assert abi.llama_sample_top_p(16, 2, 40000, 40000, 0.8, 0.9, 16, 16, 0, 0) == abi.LLAMA_ERR_UNSUPPORTED
     assert abi.llama_select_next(16, 16, 8, 8, 16, 1, 0) == abi.LLAMA_ERR_INVALID_ARG
     assert abi.llama_select_next(16, 16, 8, -1, 16, 1, 0) == abi.LLAMA_ERR_INVALID_ARG
     assert abi.llama_select_next(16, 16, 8, 3, 0, 1, 0) == abi.LLAMA_ERR_INVALID_ARG
