@@ -12,7 +12,7 @@ Sources (cited by page title and section):
   [ST] the pyshine.com source tour of meta-llama/llama, sections "One model.py, Four
        Ideas" and "Sampling, Stopping, and the Chat Template".
 
-Readings taken where the pages leave a step open (each also listed in the design doc):
+Readings taken where the pages leave a step open:
   R1  RoPE frequency of pair i is theta**(-2i/head_dim)  (the pages fix only theta and
       "one frequency per pair"; parity unpinned beyond that convention).
   R2  RoPE pairs are adjacent elements (2i, 2i+1) of each head = (real, imag).
