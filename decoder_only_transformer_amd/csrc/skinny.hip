@@ -246,8 +246,9 @@ hipError_t launch_waves(const SkinnyArgs& a, hipStream_t s) {
 // timings at the decode shapes (batch 8 .. 32 of the 7B, 13B and 70B layer widths):
 //  - SiLU gate: gate and up rows already share each activation fragment: NT = 1, D = 4, and
 //    8 waves when there are too few 16-row tiles for two 4-wave workgroups per CU;
-//  - wide products (q/k/v, logits: 640 or more tiles): NT = 4 for up to 16 batch rows, 2 for
-//    up to 32, 4 waves;
+//  - wide products (q/k/v, logits: 640 or more tiles): NT = 4 for up to 16 batch rows; for up
+//    to 32, NT = 3 with 8 waves and a 2-slot ring at up to 1024 tiles (the 7B q/k/v: one
+//    workgroup per CU), else NT = 2 with 4 waves;
 //  - the others (wo, w2): NT = 2 with 8 waves for up to 16 rows, NT = 1 with 4 for more.
 // The LDS of a workgroup stays at or under 128 KB.
 template <int EPI>
@@ -258,8 +259,13 @@ hipError_t launch_epi(const SkinnyArgs& a, hipStream_t s) {
         if (tiles >= 512) return m16 ? launch_waves<2, 1, 1, EPI, 4, 4>(a, s) : launch_waves<2, 1, 2, EPI, 4, 4>(a, s);
         return m16 ? launch_waves<2, 1, 1, EPI, 4, 8>(a, s) : launch_waves<2, 1, 2, EPI, 4, 8>(a, s);
     } else {
-        if (tiles >= 640) return m16 ? launch_waves<1, 4, 1, EPI, 4, 4>(a, s) : launch_waves<1, 2, 2, EPI, 4, 4>(a, s);
-        return m16 ? launch_waves<1, 2, 1, EPI, 4, 8>(a, s) : launch_waves<1, 1, 2, EPI, 8, 4>(a, s);
+        if (tiles >= 640) {
+            if (m16) return launch_waves<1, 4, 1, EPI, 4, 4>(a, s);
+            // about one workgroup per CU: 3 row blocks, 8 waves, a 2-slot ring each
+            if (tiles <= 1024) return launch_waves<1, 3, 2, EPI, 2, 8>(a, s);
+            return launch_waves<1, 2, 2, EPI, 4, 4>(a, s);
+        }
+        return m16 ? launch_waves<1, 2, 1, EPI, 4, 8>(a, s) : launch_waves<1, 1, 2, EPI, 6, 4>(a, s);
     }
 }
 
