@@ -97,6 +97,8 @@ struct SkinnyArgs {
     float* out; void* out16; int64_t ldo;   // STORE (fp32) / SWIGLU (bf16)
     int out_frag_mt;       // SWIGLU: > 0 writes out16 fragment-major for that many row tiles
     float* resid; int64_t ldr;
+    int ksplit;            // RESID: > 1 splits K over gridDim.y, each split writing its sum
+    float* part;           //   to part[split][M][N] in place of adding it to resid
     QkvTarget qkv;
     const StepState* st;   // if set, the STORE epilogue writes st->logits
 };
@@ -145,11 +147,18 @@ hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, 
 hipError_t launch_set_step(StepState* st, int pos, int64_t ld, const int32_t* tokens, float* logits,
                            hipStream_t s);
 // RMSNorm of fp32 rows to bf16; frag_mt > 0 writes the rows fragment-major (frag_index).
-hipError_t launch_rmsnorm_bf16(const float* h, int64_t ldh, int rows, int dim, const void* w,
-                               float eps, void* out, int64_t ldo, int frag_mt, hipStream_t s);
+// nsplit > 1 (at most kMaxNormFold): h[r] += part[0][r] + ... + part[nsplit-1][r] first (the
+// K-split partials [nsplit][rows][dim] of the residual product that precedes the norm),
+// written back to h.
+constexpr int kMaxNormFold = 4;
+hipError_t launch_rmsnorm_bf16(float* h, int64_t ldh, int rows, int dim, const void* w,
+                               float eps, void* out, int64_t ldo, int frag_mt, hipStream_t s,
+                               const float* part = nullptr, int nsplit = 0);
 hipError_t launch_gemv(int wbf16, int epi, const GemvArgs& a, hipStream_t s);
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
 hipError_t launch_skinny(int epi, const SkinnyArgs& a, hipStream_t s);
+// K splits the skinny residual product of M x K by K x N takes (SkinnyArgs::ksplit).
+int skinny_resid_splits(int M, int N, int K);
 hipError_t launch_attn_rows(int kv_bf16, const AttnArgs& a, hipStream_t s);
 hipError_t launch_argmax(const float* logits, int bsz, int vocab, int64_t stride, int32_t* out,
                          hipStream_t s);

@@ -324,9 +324,16 @@ int residual_splits(const llama_ctx* c, int T, int K) {
     return std::max(1, std::min(sp, kMaxSplitK));
 }
 
+// K splits of the skinny wo and w2 products at M rows; their partials [splits][M][dim] sit in
+// the split-K region (idle during a decode step; it holds 8 x min(rows, 512) x dim floats or
+// more, and M <= 32 rows of the batch) until the RMSNorm that follows adds them to h.
+int wo_splits(const llama_ctx* c, int M) { return skinny_resid_splits(M, c->a.dim, c->nq); }
+int w2_splits(const llama_ctx* c, int M) { return skinny_resid_splits(M, c->a.dim, c->a.hidden_dim); }
+
 // One decode block for a bf16 model at batch > kSkinnyRows: projections on the skinny MFMA
 // kernel, whose activation operands (RMSNorm output, attention output, SiLU gate) are written
-// bf16 in fragment-major order for MT = ceil(M / 16) row tiles.
+// bf16 in fragment-major order for MT = ceil(M / 16) row tiles.  The attention norm takes in
+// the previous block's w2 partials, the FFN norm this block's wo partials.
 llama_status block_skinny(const llama_ctx* c, int l, int M, int start_pos, hipStream_t s,
                           const StepState* st, int graph_splits) {
     const llama_layer_weights& W = c->layers[l];
@@ -335,8 +342,12 @@ llama_status block_skinny(const llama_ctx* c, int l, int M, int start_pos, hipSt
     float* h = c->at<float>(c->L.h32);
     void* act = c->at<void>(c->L.act16);
     void* g16 = c->at<void>(c->L.g16);
+    float* part = c->at<float>(c->L.splitk);
+    const int s_wo = wo_splits(c, M), s_w2 = w2_splits(c, M);
+    if ((size_t)std::max(s_wo, s_w2) * M * D > c->L.splitk_floats) return LLAMA_ERR_WORKSPACE;
 
-    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, M, D, W.attention_norm, c->a.norm_eps, act, 0, mt, s));
+    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, M, D, W.attention_norm, c->a.norm_eps, act, 0, mt, s,
+                                                       part, l > 0 ? s_w2 : 0));
     SkinnyArgs k{};
     k.x = act; k.M = M; k.K = D; k.N = c->nq + 2 * c->nk;
     k.w0 = W.wq; k.w1 = W.wk; k.w2 = W.wv;
@@ -348,10 +359,11 @@ llama_status block_skinny(const llama_ctx* c, int l, int M, int start_pos, hipSt
 
     k = SkinnyArgs{};
     k.x = act; k.M = M; k.K = c->nq; k.N = D;
-    k.w0 = W.wo; k.resid = h; k.ldr = D;
+    k.w0 = W.wo; k.resid = h; k.ldr = D; k.ksplit = s_wo; k.part = part;
     LAUNCH(c, LLAMA_KC_GEMV_WO, s, launch_skinny(EPI_RESID, k, s));
 
-    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, M, D, W.ffn_norm, c->a.norm_eps, act, 0, mt, s));
+    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, M, D, W.ffn_norm, c->a.norm_eps, act, 0, mt, s,
+                                                       part, s_wo));
     k = SkinnyArgs{};
     k.x = act; k.M = M; k.K = D; k.N = F;
     k.w0 = W.w1; k.w1 = W.w3; k.out16 = g16; k.out_frag_mt = mt;
@@ -359,7 +371,7 @@ llama_status block_skinny(const llama_ctx* c, int l, int M, int start_pos, hipSt
 
     k = SkinnyArgs{};
     k.x = g16; k.M = M; k.K = F; k.N = D;
-    k.w0 = W.w2; k.resid = h; k.ldr = D;
+    k.w0 = W.w2; k.resid = h; k.ldr = D; k.ksplit = s_w2; k.part = part;
     LAUNCH(c, LLAMA_KC_GEMV_W2, s, launch_skinny(EPI_RESID, k, s));
     return LLAMA_OK;
 }
@@ -563,7 +575,9 @@ static llama_status decode_plan(llama_ctx* c, const int32_t* d_tokens, int64_t l
     }
     if (!skinny) return final_logits(c, h, D, bsz, d_logits, s, st);
     void* act = c->at<void>(c->L.act16);
-    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, bsz, D, c->w.norm, c->a.norm_eps, act, 0, (bsz + 15) / 16, s));
+    // the final norm takes in the last block's w2 partials
+    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, bsz, D, c->w.norm, c->a.norm_eps, act, 0, (bsz + 15) / 16, s,
+                                                       c->at<float>(c->L.splitk), w2_splits(c, bsz)));
     SkinnyArgs k{};
     k.x = act; k.M = bsz; k.K = D; k.N = c->a.vocab_size;
     k.w0 = c->w.output; k.out = d_logits; k.ldo = c->a.vocab_size; k.st = st;

@@ -25,15 +25,28 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* tokens, int64
 }
 
 // out[r][:] = bf16( h[r][:] * rsqrt(mean(h[r]^2) + eps) * w ), fp32 reduction.
+// With nsplit > 1, h[r] first takes the K-split partial sums of the residual product that
+// wrote them, part[0][r] + ... + part[nsplit - 1][r] (part is [nsplit][rows][dim], summed in
+// split order), and is stored back.
 template <typename WT>
-__global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const float* h, int64_t ldh, int dim,
+__global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(float* h, int64_t ldh, int dim,
                                                            const WT* w, float eps, uint16_t* out,
-                                                           int64_t ldo, int frag_mt) {
+                                                           int64_t ldo, int frag_mt,
+                                                           const float* part, int nsplit) {
     __shared__ float red[4];
-    const float* x = h + (size_t)blockIdx.x * ldh;
+    float* x = h + (size_t)blockIdx.x * ldh;
     float ss = 0.f;
     for (int k = threadIdx.x * 4; k < dim; k += 256 * 4) {
-        const float4 v = *reinterpret_cast<const float4*>(x + k);
+        float4 v = *reinterpret_cast<const float4*>(x + k);
+        if (nsplit > 1) {
+            float4 p = *reinterpret_cast<const float4*>(part + (size_t)blockIdx.x * dim + k);
+            for (int sp = 1; sp < nsplit; ++sp) {
+                const float4 q = *reinterpret_cast<const float4*>(part + ((size_t)sp * gridDim.x + blockIdx.x) * dim + k);
+                p.x += q.x; p.y += q.y; p.z += q.z; p.w += q.w;
+            }
+            v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+            *reinterpret_cast<float4*>(x + k) = v;
+        }
         ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
     }
     ss = wave_sum(ss);
@@ -51,21 +64,40 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(const float* h, int64
     }
 }
 
-// Same, for rows of at most 1024 * NV elements: every load of the row (and of the weights)
-// is issued before the first use and the row stays in registers for the second half, so a
-// row costs one memory round trip instead of one per chunk and pass.
-template <int NV>
-__global__ __launch_bounds__(256) void rmsnorm_reg_kernel(const float* h, int64_t ldh, int dim, const bf16* w,
-                                                          float eps, uint16_t* out, int64_t ldo, int frag_mt) {
+// Same, for rows of at most 1024 * NV elements: every load of the row (and of the weights and
+// NS partials) is issued before the first use and the row stays in registers for the second
+// half, so a row costs one memory round trip instead of one per chunk and pass.
+template <int NV, int NS>
+__global__ __launch_bounds__(256) void rmsnorm_reg_kernel(float* h, int64_t ldh, int dim, const bf16* w,
+                                                          float eps, uint16_t* out, int64_t ldo, int frag_mt,
+                                                          const float* part) {
     __shared__ float red[4];
-    const float* x = h + (size_t)blockIdx.x * ldh;
+    float* x = h + (size_t)blockIdx.x * ldh;
     float4 v[NV];
     uint2 wv[NV];
+    float4 p[NV][NS > 0 ? NS : 1];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int k = (threadIdx.x + 256 * i) * 4;
         v[i] = k < dim ? *reinterpret_cast<const float4*>(x + k) : float4{0.f, 0.f, 0.f, 0.f};
         wv[i] = k < dim ? *reinterpret_cast<const uint2*>(w + k) : uint2{0u, 0u};
+#pragma unroll
+        for (int sp = 0; sp < NS; ++sp)
+            p[i][sp] = k < dim ? *reinterpret_cast<const float4*>(part + ((size_t)sp * gridDim.x + blockIdx.x) * dim + k)
+                               : float4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (NS > 0) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            float4 t = p[i][0];
+#pragma unroll
+            for (int sp = 1; sp < NS; ++sp) {
+                t.x += p[i][sp].x; t.y += p[i][sp].y; t.z += p[i][sp].z; t.w += p[i][sp].w;
+            }
+            v[i].x += t.x; v[i].y += t.y; v[i].z += t.z; v[i].w += t.w;
+            const int k = (threadIdx.x + 256 * i) * 4;
+            if (k < dim) *reinterpret_cast<float4*>(x + k) = v[i];
+        }
     }
     float ss = 0.f;
 #pragma unroll
@@ -215,22 +247,36 @@ hipError_t launch_set_step(StepState* st, int pos, int64_t ld, const int32_t* to
     return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm_bf16(const float* h, int64_t ldh, int rows, int dim, const void* w,
-                               float eps, void* out, int64_t ldo, int frag_mt, hipStream_t s) {
+template <int NS>
+void launch_rmsnorm_ns(float* h, int64_t ldh, int rows, int dim, const bf16* wb, float eps, uint16_t* o,
+                       int64_t ldo, int frag_mt, const float* part, hipStream_t s) {
+    switch ((dim + 1023) / 1024) {
+        case 1: launch_kernel((rmsnorm_reg_kernel<1, NS>), dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt, part); break;
+        case 2: launch_kernel((rmsnorm_reg_kernel<2, NS>), dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt, part); break;
+        case 3:
+        case 4: launch_kernel((rmsnorm_reg_kernel<4, NS>), dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt, part); break;
+        case 5:
+        case 6: launch_kernel((rmsnorm_reg_kernel<6, NS>), dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt, part); break;
+        default: launch_kernel((rmsnorm_reg_kernel<8, NS>), dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt, part); break;
+    }
+}
+
+hipError_t launch_rmsnorm_bf16(float* h, int64_t ldh, int rows, int dim, const void* w,
+                               float eps, void* out, int64_t ldo, int frag_mt, hipStream_t s,
+                               const float* part, int nsplit) {
     const bf16* wb = static_cast<const bf16*>(w);
     uint16_t* o = static_cast<uint16_t*>(out);
-    switch ((dim + 1023) / 1024) {
-        case 1: launch_kernel(rmsnorm_reg_kernel<1>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt); break;
-        case 2: launch_kernel(rmsnorm_reg_kernel<2>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt); break;
-        case 3:
-        case 4: launch_kernel(rmsnorm_reg_kernel<4>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt); break;
-        case 5:
-        case 6: launch_kernel(rmsnorm_reg_kernel<6>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt); break;
-        case 7:
-        case 8: launch_kernel(rmsnorm_reg_kernel<8>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt); break;
-        default:
-            launch_kernel(rmsnorm_bf16_kernel<bf16>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt);
-    }
+    if (nsplit > 1 && (!part || nsplit > kMaxNormFold)) return hipErrorInvalidValue;
+    if (dim > 8192)
+        launch_kernel(rmsnorm_bf16_kernel<bf16>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt,
+                      part, nsplit);
+    else if (nsplit == 2)
+        launch_rmsnorm_ns<2>(h, ldh, rows, dim, wb, eps, o, ldo, frag_mt, part, s);
+    else if (nsplit > 1)
+        launch_kernel(rmsnorm_bf16_kernel<bf16>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt,
+                      part, nsplit);
+    else
+        launch_rmsnorm_ns<0>(h, ldh, rows, dim, wb, eps, o, ldo, frag_mt, nullptr, s);
     return hipGetLastError();
 }
 

@@ -103,7 +103,10 @@ __device__ __forceinline__ void sk_epilogue(const SkinnyArgs& a, const f32x4 (&a
             const int n = nb + 4 * g + e;
             if (n >= a.N) continue;
             if (EPI == EPI_RESID) {
-                a.resid[(size_t)m * a.ldr + n] += acc[0][e];
+                if (a.ksplit > 1)   // this K split's share, summed into the residual later
+                    a.part[((size_t)blockIdx.y * a.M + m) * a.N + n] = acc[0][e];
+                else
+                    a.resid[(size_t)m * a.ldr + n] += acc[0][e];
             } else if (EPI == EPI_SWIGLU) {
                 const size_t o = a.out_frag_mt ? frag_index(m, n, a.out_frag_mt) : (size_t)m * a.ldo + n;
                 static_cast<uint16_t*>(a.out16)[o] = f32_to_bf16(silu(acc[0][e]) * acc[NW - 1][e]);
@@ -128,7 +131,10 @@ __global__ __launch_bounds__(64 * NWV) void skinny_kernel(SkinnyArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int fr = lane & 15, g = lane >> 4;
     const int n0 = blockIdx.x * 16 * NT;
-    const int nst = a.K / kSkBK;
+    // K split blockIdx.y of gridDim.y takes stages st0 .. st0 + nst - 1
+    const int nst_all = a.K / kSkBK;
+    const int st0 = (int)((int64_t)blockIdx.y * nst_all / gridDim.y);
+    const int nst = (int)((int64_t)(blockIdx.y + 1) * nst_all / gridDim.y) - st0;
     const int n_my = (nst - wid + NWV - 1) / NWV;     // stages wid, wid + NWV, ... of this wave
 
     // DMA sources of this lane: rows n0 + 16t + 8h + r8 (clamped past N), chunk c8
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(64 * NWV) void skinny_kernel(SkinnyArgs a) {
     const int rot = (int)((blockIdx.x * 37u) % (unsigned)nst);
     auto issue = [&](int i, int u) {
         int kt = min(wid + NWV * i, nst - 1) + rot;     // repeats of the last stage past the end
-        kt = kt >= nst ? kt - nst : kt;
+        kt = (kt >= nst ? kt - nst : kt) + st0;
         const int k = kt * kSkBK;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -237,7 +243,7 @@ __global__ __launch_bounds__(64 * NWV) void skinny_kernel(SkinnyArgs a) {
 
 template <int NW, int NT, int MT, int EPI, int D, int NWV>
 hipError_t launch_waves(const SkinnyArgs& a, hipStream_t s) {
-    const dim3 grid((a.N + 16 * NT - 1) / (16 * NT));
+    const dim3 grid((a.N + 16 * NT - 1) / (16 * NT), EPI == EPI_RESID && a.ksplit > 1 ? a.ksplit : 1);
     launch_kernel((skinny_kernel<NW, NT, MT, EPI, D, NWV>), grid, dim3(64 * NWV), 0, s, a);
     return hipGetLastError();
 }
@@ -249,12 +255,18 @@ hipError_t launch_waves(const SkinnyArgs& a, hipStream_t s) {
 //  - wide products (q/k/v, logits: 640 or more tiles): NT = 4 for up to 16 batch rows; for up
 //    to 32, NT = 3 with 8 waves and a 2-slot ring at up to 1024 tiles (the 7B q/k/v: one
 //    workgroup per CU), else NT = 2 with 4 waves;
-//  - the others (wo, w2): NT = 2 with 8 waves for up to 16 rows, NT = 1 with 4 for more.
+//  - the others (wo, w2): NT = 2 with 8 waves for up to 16 rows, NT = 1 with 4 for more;
+//  - residual products split over K (fewer than 512 tiles: the 7B wo/w2 at 32 rows and the
+//    13B ones at 16 filled half the chip or less): 4 waves, NT = 1 for up to 16 rows, NT = 2
+//    for more (7B w2 at 32 rows 27.8 -> 21.6 us, 13B wo at 16 rows 19.5 -> 15.7 us).
 // The LDS of a workgroup stays at or under 128 KB.
 template <int EPI>
 hipError_t launch_epi(const SkinnyArgs& a, hipStream_t s) {
     const int tiles = (a.N + 15) / 16;
     const bool m16 = a.M <= 16;     // one 16-row batch tile (MT = 1) or two
+    if constexpr (EPI == EPI_RESID) {
+        if (a.ksplit > 1) return m16 ? launch_waves<1, 1, 1, EPI, 4, 4>(a, s) : launch_waves<1, 2, 2, EPI, 4, 4>(a, s);
+    }
     if constexpr (EPI == EPI_SWIGLU) {
         if (tiles >= 512) return m16 ? launch_waves<2, 1, 1, EPI, 4, 4>(a, s) : launch_waves<2, 1, 2, EPI, 4, 4>(a, s);
         return m16 ? launch_waves<2, 1, 1, EPI, 4, 8>(a, s) : launch_waves<2, 1, 2, EPI, 4, 8>(a, s);
@@ -271,8 +283,15 @@ hipError_t launch_epi(const SkinnyArgs& a, hipStream_t s) {
 
 }  // namespace
 
+int skinny_resid_splits(int M, int N, int K) {
+    if (M < 1 || M > 32 || K % kSkBK != 0) return 1;
+    // two splits while the row blocks alone leave CUs idle, each split at least 8 stages
+    return (N + 15) / 16 < 512 && K / kSkBK >= 16 ? 2 : 1;
+}
+
 hipError_t launch_skinny(int epi, const SkinnyArgs& a, hipStream_t s) {
     if (a.M < 1 || a.M > 32 || a.K % kSkBK != 0 || a.K < kSkBK) return hipErrorInvalidValue;
+    if (a.ksplit > 1 && (epi != EPI_RESID || !a.part || a.ksplit > a.K / kSkBK)) return hipErrorInvalidValue;
     switch (epi) {
         case EPI_QKV: return launch_epi<EPI_QKV>(a, s);
         case EPI_RESID: return launch_epi<EPI_RESID>(a, s);
