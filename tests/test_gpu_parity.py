@@ -208,6 +208,13 @@ SMALL_BF16 = {
                                               n_kv_heads=8, dim=1024, hidden_dim=2816, vocab_size=1000,
                                               batch=32, prompt_len=0, prompt_len_range=(12, 40),
                                               gen_steps=12, weight_seed=16, prompt_seed=116, max_seq_len=96),
+    # head_dim 32 with GQA 4:1 (prefill on the row attention kernel, decode on the MFMA GQA
+    # kernel at its narrowest head) and 17 decode rows: the skinny products' second 16-row tile
+    # holds one live row
+    "hd32": synth.WORKLOADS["tiny_fp32"].with_(name="small_bf16_hd32", dtype="bf16", n_heads=8,
+                                               n_kv_heads=2, dim=256, hidden_dim=768, vocab_size=512,
+                                               batch=17, prompt_len=0, prompt_len_range=(10, 50),
+                                               gen_steps=12, weight_seed=18, prompt_seed=118, max_seq_len=96),
     # RoPE base 500000 instead of 10000 (theta is an argument of the ABI, not a constant)
     "theta": synth.WORKLOADS["tiny_fp32"].with_(name="small_bf16_theta", dtype="bf16", n_heads=8,
                                                 n_kv_heads=2, dim=512, hidden_dim=1536, vocab_size=1000,
@@ -258,7 +265,7 @@ def test_small_bf16_prefill_equals_token_by_token_decode():
     model.close()
 
 
-@pytest.mark.parametrize("name", ["gqa8", "mha", "theta"])
+@pytest.mark.parametrize("name", ["gqa8", "mha", "theta", "hd32"])
 def test_small_bf16_chunked_prefill_all_positions(name):
     """Prefill in two chunks (the second at start_pos > 0, ragged against the 64-row tiles)
     against the oracle's full forward, every position."""
