@@ -20,6 +20,8 @@ LLAMA_ERR_WORKSPACE = -3
 LLAMA_ERR_HIP = -4
 LLAMA_BF16 = 0
 LLAMA_FP32 = 1
+LLAMA_FP16 = 2
+DTYPES = {"bf16": LLAMA_BF16, "fp32": LLAMA_FP32, "fp16": LLAMA_FP16}
 
 # Every symbol include/llama_mi355x.h declares.
 EXPORTED = ("llama_check_args", "llama_workspace_bytes", "llama_init", "llama_prefill",

@@ -7,6 +7,8 @@
 // LDS.  With more than one split per row, every workgroup stores its partial (m, l, acc)
 // and a second, small launch combines the splits in split order (deterministic; the kernel
 // boundary makes the partials visible without any cross-workgroup synchronisation).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -41,8 +43,8 @@ struct RawRow {
         } else {
 #pragma unroll
             for (int i = 0; i < N / 2; ++i) {
-                out[2 * i] = bf16lo(w[i]);
-                out[2 * i + 1] = bf16hi(w[i]);
+                out[2 * i] = Elem<KT>::lo(w[i]);
+                out[2 * i + 1] = Elem<KT>::hi(w[i]);
             }
         }
     }
@@ -438,7 +440,7 @@ hipError_t launch4(const AttnArgs& args, hipStream_t s) {
         const int n = min(kMaxZ, args.rows - r0);
         const dim3 grid(a.n_split, a.n_kv_heads, n);
         bool done = false;
-        if constexpr (NREP >= 4 && sizeof(KT) == 2) {
+        if constexpr (NREP >= 4 && std::is_same<KT, bf16>::value) {
             if (a.seqlen == 1) {
                 launch_kernel((attn_gqa_decode_kernel<HD, NREP, OB>), grid, dim3(256), 0, s, a);
                 done = true;
@@ -488,9 +490,14 @@ hipError_t launch2(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_attn_rows(int kv_bf16, const AttnArgs& a, hipStream_t s) {
-    if (kv_bf16) return a.out_bf16 ? launch2<bf16, true>(a, s) : launch2<bf16, false>(a, s);
-    return a.out_bf16 ? launch2<float, true>(a, s) : launch2<float, false>(a, s);
+hipError_t launch_attn_rows(int kv_type, const AttnArgs& a, hipStream_t s) {
+    switch (kv_type) {
+        case kStoreBf16: return a.out_bf16 ? launch2<bf16, true>(a, s) : launch2<bf16, false>(a, s);
+        case kStoreF32: return a.out_bf16 ? launch2<float, true>(a, s) : launch2<float, false>(a, s);
+        // fp16 caches belong to the vector path, whose attention output is fp32
+        case kStoreF16: return a.out_bf16 ? hipErrorInvalidValue : launch2<f16, false>(a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace llk

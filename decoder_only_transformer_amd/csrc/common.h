@@ -1,4 +1,4 @@
-// Device-side helpers shared by the gfx950 kernels: storage types, bf16 conversion,
+// Device-side helpers shared by the gfx950 kernels: storage types, bf16 / fp16 conversion,
 // wave64 reductions, vector loads.
 #pragma once
 
@@ -34,9 +34,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
-// Element access for the two storage types.
+// IEEE binary16 (fp16) is handled as raw 16-bit storage too; conversions go through clang's
+// _Float16 (v_cvt_f16_f32 rounds to nearest even; v_cvt_f32_f16 is exact).
+struct f16 {
+    uint16_t bits;
+};
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return static_cast<float>(__builtin_bit_cast(_Float16, h)); }
+__device__ __forceinline__ uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f)); }
+
+// Element access for the storage types.  k16: a 16-bit type, whose values the method rounds
+// where it stores them (round: the value after storage); lo / hi: the two elements of a
+// packed 32-bit pair.
 template <typename T> struct Elem;
 template <> struct Elem<float> {
+    static constexpr bool k16 = false;
+    __device__ __forceinline__ static float round(float x) { return x; }
     static constexpr int kPer16B = 4;
     __device__ __forceinline__ static float load(const float* p, size_t i) { return p[i]; }
     __device__ __forceinline__ static void store(float* p, size_t i, float v) { p[i] = v; }
@@ -47,6 +59,10 @@ template <> struct Elem<float> {
     }
 };
 template <> struct Elem<bf16> {
+    static constexpr bool k16 = true;
+    __device__ __forceinline__ static float round(float x) { return round_bf16(x); }
+    __device__ __forceinline__ static float lo(uint32_t w) { return bf16lo(w); }
+    __device__ __forceinline__ static float hi(uint32_t w) { return bf16hi(w); }
     static constexpr int kPer16B = 8;
     __device__ __forceinline__ static float load(const bf16* p, size_t i) { return bf16_to_f32(p[i].bits); }
     __device__ __forceinline__ static void store(bf16* p, size_t i, float v) { p[i].bits = f32_to_bf16(v); }
@@ -54,6 +70,20 @@ template <> struct Elem<bf16> {
     __device__ __forceinline__ static void unpack(const uint4& v, float* out) {
         out[0] = bf16lo(v.x); out[1] = bf16hi(v.x); out[2] = bf16lo(v.y); out[3] = bf16hi(v.y);
         out[4] = bf16lo(v.z); out[5] = bf16hi(v.z); out[6] = bf16lo(v.w); out[7] = bf16hi(v.w);
+    }
+};
+template <> struct Elem<f16> {
+    static constexpr bool k16 = true;
+    __device__ __forceinline__ static float round(float x) { return f16_to_f32(f32_to_f16(x)); }
+    __device__ __forceinline__ static float lo(uint32_t w) { return f16_to_f32(static_cast<uint16_t>(w & 0xffffu)); }
+    __device__ __forceinline__ static float hi(uint32_t w) { return f16_to_f32(static_cast<uint16_t>(w >> 16)); }
+    static constexpr int kPer16B = 8;
+    __device__ __forceinline__ static float load(const f16* p, size_t i) { return f16_to_f32(p[i].bits); }
+    __device__ __forceinline__ static void store(f16* p, size_t i, float v) { p[i].bits = f32_to_f16(v); }
+    // 16 bytes -> 8 floats
+    __device__ __forceinline__ static void unpack(const uint4& v, float* out) {
+        out[0] = lo(v.x); out[1] = hi(v.x); out[2] = lo(v.y); out[3] = hi(v.y);
+        out[4] = lo(v.z); out[5] = hi(v.z); out[6] = lo(v.w); out[7] = hi(v.w);
     }
 };
 

@@ -8,9 +8,9 @@
 // once per workgroup in LDS as fp32.  Epilogues fuse what follows each projection in the
 // block: RoPE + KV-cache append for [wq; wk; wv], residual add for wo / w2, the SiLU gate
 // for [w1; w3], and the fp32 logits store for the output projection.
-// With bf16 weights the activations are rounded to bf16 as they are staged, and q is
-// rounded before it is stored: the decode path stores the same bf16 tensors as the MFMA
-// prefill path (normalised operands, q, K/V, attention output, gated FFN activation).
+// With 16-bit weights (bf16 or fp16) the activations are rounded to that type as they are
+// staged, and q is rounded before it is stored: the path stores the same 16-bit tensors as
+// the MFMA prefill path (normalised operands, q, K/V, attention output, gated FFN activation).
 #include "common.h"
 #include "kernels.h"
 
@@ -20,8 +20,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
 
-template <typename WT> constexpr bool kIsBf16 = false;
-template <> constexpr bool kIsBf16<bf16> = true;
 
 template <typename WT>
 __device__ __forceinline__ const WT* qkv_row(const GemvArgs& a, int n) {
@@ -45,9 +43,9 @@ __device__ __forceinline__ void qkv_store(const QkvTarget& t, int m, int n0, flo
         y1 = r1;
     }
     if (n0 < t.nq) {
-        if (kIsBf16<WT>) {
-            y0 = round_bf16(y0);
-            y1 = round_bf16(y1);
+        if (Elem<WT>::k16) {
+            y0 = Elem<WT>::round(y0);
+            y1 = Elem<WT>::round(y1);
         }
         t.q[(size_t)m * t.nq + n0] = y0;
         t.q[(size_t)m * t.nq + n0 + 1] = y1;
@@ -159,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
                     xv[m][i] = *reinterpret_cast<const float4*>(a.x + (size_t)row * a.ldx + k0 + k);
                 }
                 if (NORM) {
-                    if (kIsBf16<WT>)
+                    if (Elem<WT>::k16)
                         nv[i] = *reinterpret_cast<const uint2*>(static_cast<const WT*>(a.norm_w) + k0 + k);
                     else
                         nvf[i] = *reinterpret_cast<const float4*>(static_cast<const WT*>(a.norm_w) + k0 + k);
@@ -180,8 +178,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
 #pragma unroll
             for (int i = 0; i < XPT; ++i) {
                 kin[i] = (tid + i * kThreads) * 4 < klen ? 1.f : 0.f;
-                if (NORM && kIsBf16<WT>)
-                    nvf[i] = make_float4(bf16lo(nv[i].x), bf16hi(nv[i].x), bf16lo(nv[i].y), bf16hi(nv[i].y));
+                if constexpr (NORM && Elem<WT>::k16)
+                    nvf[i] = make_float4(Elem<WT>::lo(nv[i].x), Elem<WT>::hi(nv[i].x), Elem<WT>::lo(nv[i].y),
+                                         Elem<WT>::hi(nv[i].y));
             }
             float scale[MB];
 #pragma unroll
@@ -226,11 +225,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
                         v.z *= scale[m];
                         v.w *= scale[m];
                     }
-                    if (kIsBf16<WT>) {
-                        v.x = round_bf16(v.x);
-                        v.y = round_bf16(v.y);
-                        v.z = round_bf16(v.z);
-                        v.w = round_bf16(v.w);
+                    if (Elem<WT>::k16) {
+                        v.x = Elem<WT>::round(v.x);
+                        v.y = Elem<WT>::round(v.y);
+                        v.z = Elem<WT>::round(v.z);
+                        v.w = Elem<WT>::round(v.w);
                     }
                     *reinterpret_cast<float4*>(&xs[m][k]) = v;
                 }
@@ -320,8 +319,13 @@ hipError_t launch_typed(int epi, const GemvArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_gemv(int wbf16, int epi, const GemvArgs& a, hipStream_t s) {
-    return wbf16 ? launch_typed<bf16>(epi, a, s) : launch_typed<float>(epi, a, s);
+hipError_t launch_gemv(int wtype, int epi, const GemvArgs& a, hipStream_t s) {
+    switch (wtype) {
+        case kStoreF32: return launch_typed<float>(epi, a, s);
+        case kStoreBf16: return launch_typed<bf16>(epi, a, s);
+        case kStoreF16: return launch_typed<f16>(epi, a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace llk

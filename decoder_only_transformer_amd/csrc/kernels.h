@@ -7,6 +7,9 @@
 
 namespace llk {
 
+// Storage type of weights and KV cache, as the launchers take it.
+constexpr int kStoreF32 = 0, kStoreBf16 = 1, kStoreF16 = 2;
+
 // Per-kernel timing for diagnostics.  While a timer is installed on the calling thread,
 // every kernel goes out through hipExtLaunchKernel with an event pair of its own, which HIP
 // ties to that dispatch's begin and end timestamps (so queue gaps between launches are not
@@ -143,7 +146,7 @@ hipError_t launch_flash_prefill(const FlashArgs& a, hipStream_t s);
 hipError_t launch_rope_scatter_parts(const float* y, int splits, int64_t ldy, int T, const QkvTarget& t,
                                      hipStream_t s);
 hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, const void* table,
-                        int wbf16, int vocab, int dim, float* h, const StepState* st, hipStream_t s);
+                        int wtype, int vocab, int dim, float* h, const StepState* st, hipStream_t s);
 hipError_t launch_set_step(StepState* st, int pos, int64_t ld, const int32_t* tokens, float* logits,
                            hipStream_t s);
 // RMSNorm of fp32 rows to bf16; frag_mt > 0 writes the rows fragment-major (frag_index).
@@ -154,12 +157,12 @@ constexpr int kMaxNormFold = 4;
 hipError_t launch_rmsnorm_bf16(float* h, int64_t ldh, int rows, int dim, const void* w,
                                float eps, void* out, int64_t ldo, int frag_mt, hipStream_t s,
                                const float* part = nullptr, int nsplit = 0);
-hipError_t launch_gemv(int wbf16, int epi, const GemvArgs& a, hipStream_t s);
+hipError_t launch_gemv(int wtype, int epi, const GemvArgs& a, hipStream_t s);   // wtype: kStore*
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
 hipError_t launch_skinny(int epi, const SkinnyArgs& a, hipStream_t s);
 // K splits the skinny residual product of M x K by K x N takes (SkinnyArgs::ksplit).
 int skinny_resid_splits(int M, int N, int K);
-hipError_t launch_attn_rows(int kv_bf16, const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_rows(int kv_type, const AttnArgs& a, hipStream_t s);   // kv_type: kStore*
 hipError_t launch_argmax(const float* logits, int bsz, int vocab, int64_t stride, int32_t* out,
                          hipStream_t s);
 hipError_t launch_select(const int32_t* next, int32_t* tokens, int64_t ld, int cur_pos,

@@ -53,7 +53,7 @@ llama_status check_args(const llama_args* a) {
         a->max_seq_len <= 0)
         return LLAMA_ERR_INVALID_ARG;
     if (!(a->norm_eps >= 0.f) || !(a->rope_theta > 0.f)) return LLAMA_ERR_INVALID_ARG;
-    if (a->dtype != LLAMA_BF16 && a->dtype != LLAMA_FP32) return LLAMA_ERR_INVALID_ARG;
+    if (a->dtype != LLAMA_BF16 && a->dtype != LLAMA_FP32 && a->dtype != LLAMA_FP16) return LLAMA_ERR_INVALID_ARG;
     if (a->dim % a->n_heads != 0) return LLAMA_ERR_INVALID_ARG;
     if (a->n_heads % a->n_kv_heads != 0) return LLAMA_ERR_INVALID_ARG;
     const int hd = head_dim_of(*a);
@@ -78,12 +78,14 @@ size_t splitk_cols(const llama_args& a) {
 
 Layout layout_of(const llama_args& a) {
     Layout L{};
-    const size_t esz = a.dtype == LLAMA_BF16 ? 2 : 4;
+    const size_t esz = a.dtype == LLAMA_FP32 ? 4 : 2;
     const size_t hd = head_dim_of(a);
     const size_t nq = (size_t)a.n_heads * hd;
     const size_t maxB = a.max_batch_size, maxS = a.max_seq_len;
     const size_t maxT = maxB * maxS;
-    const bool fp32 = a.dtype == LLAMA_FP32;
+    // the vector path (fp32 and fp16 models) keeps every row's activations in fp32 and needs
+    // none of the MFMA path's bf16 operands or split-K partials
+    const bool fp32 = a.dtype != LLAMA_BF16;
     const size_t rows32 = fp32 ? maxT : maxB;
     L.kv_layer_elems = maxB * maxS * (size_t)a.n_kv_heads * hd;
     size_t off = 0;
@@ -125,7 +127,8 @@ struct llama_ctx {
     Layout L;
     char* ws;
     int hd, nq, nk;
-    bool bf16;
+    bool bf16;      // the MFMA path (bf16 models)
+    int wtype;      // storage type of weights and KV cache (kStoreF32 / kStoreBf16 / kStoreF16)
 
     // decode graphs: one per (bsz, key splits), captured on a private stream
     hipStream_t cap_stream = nullptr;
@@ -156,7 +159,7 @@ struct llama_ctx {
     Timer timer;
 
     template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
-    size_t esz() const { return bf16 ? 2 : 4; }
+    size_t esz() const { return wtype == kStoreF32 ? 4 : 2; }
     void* kcache(int l) const { return ws + L.k_cache + (size_t)l * L.kv_layer_elems * esz(); }
     void* vcache(int l) const { return ws + L.v_cache + (size_t)l * L.kv_layer_elems * esz(); }
 };
@@ -269,7 +272,7 @@ llama_status run_attention(const llama_ctx* c, int l, int rows, int seqlen, int 
         at.n_split = n_split;
         at.chunk = chunk;
     }
-    LAUNCH(c, seqlen == 1 ? LLAMA_KC_ATTN_DECODE : LLAMA_KC_ATTN_PREFILL, s, launch_attn_rows(c->bf16 ? 1 : 0, at, s));
+    LAUNCH(c, seqlen == 1 ? LLAMA_KC_ATTN_DECODE : LLAMA_KC_ATTN_PREFILL, s, launch_attn_rows(c->wtype, at, s));
     return LLAMA_OK;
 }
 
@@ -282,7 +285,7 @@ llama_status block_gemv(const llama_ctx* c, int l, int M, int seqlen, int start_
     float* h = c->at<float>(c->L.h32);
     float* o32 = c->at<float>(c->L.o32);
     float* g32 = c->at<float>(c->L.g32);
-    const int wb = c->bf16 ? 1 : 0;
+    const int wb = c->wtype;
 
     GemvArgs g{};
     g.x = h; g.ldx = D; g.M = M; g.K = D; g.N = c->nq + 2 * c->nk;
@@ -446,7 +449,7 @@ llama_status final_logits(const llama_ctx* c, const float* x, int64_t ldx, int r
     g.x = x; g.ldx = ldx; g.M = rows; g.K = c->a.dim; g.N = c->a.vocab_size;
     g.norm_w = c->w.norm; g.eps = c->a.norm_eps;
     g.w0 = c->w.output; g.out = logits; g.ldo = c->a.vocab_size;
-    LAUNCH(c, LLAMA_KC_GEMV_OUT, s, launch_gemv(c->bf16 ? 1 : 0, EPI_STORE, g, s));
+    LAUNCH(c, LLAMA_KC_GEMV_OUT, s, launch_gemv(c->wtype, EPI_STORE, g, s));
     return LLAMA_OK;
 }
 
@@ -492,6 +495,7 @@ llama_status llama_init(const llama_args* a, const llama_weights* w, void* d_wor
     c->nq = a->n_heads * c->hd;
     c->nk = a->n_kv_heads * c->hd;
     c->bf16 = a->dtype == LLAMA_BF16;
+    c->wtype = a->dtype == LLAMA_BF16 ? kStoreBf16 : (a->dtype == LLAMA_FP16 ? kStoreF16 : kStoreF32);
     {
         // Graph replay of decode steps is opt-in: measured on this stack, replaying the
         // captured step is no faster than launching its kernels back to back.
@@ -530,7 +534,7 @@ llama_status llama_prefill(llama_ctx* c, const int32_t* d_tokens, int64_t ld_tok
     const int D = c->a.dim;
     const int T = bsz * seqlen;
     float* h = c->at<float>(c->L.h32);
-    HIP_TRY(launch_embed(d_tokens, ld_tokens, bsz, seqlen, c->w.tok_embeddings, c->bf16 ? 1 : 0,
+    HIP_TRY(launch_embed(d_tokens, ld_tokens, bsz, seqlen, c->w.tok_embeddings, c->wtype,
                          c->a.vocab_size, D, h, nullptr, s));
     for (int l = 0; l < c->a.n_layers; ++l) {
         const llama_status st = c->bf16 ? block_mfma(c, l, T, seqlen, start_pos, s)
@@ -555,7 +559,7 @@ static llama_status decode_plan(llama_ctx* c, const int32_t* d_tokens, int64_t l
                                 const StepState* st, int graph_splits) {
     const int D = c->a.dim;
     float* h = c->at<float>(c->L.h32);
-    HIP_TRY(launch_embed(d_tokens, ld_tokens, bsz, 1, c->w.tok_embeddings, c->bf16 ? 1 : 0,
+    HIP_TRY(launch_embed(d_tokens, ld_tokens, bsz, 1, c->w.tok_embeddings, c->wtype,
                          c->a.vocab_size, D, h, st, s));
     if (c->bf16 && bsz > kSkinnyMaxRows) {
         // more rows than the skinny kernels take: the prefill GEMMs with the decode attention

@@ -230,14 +230,24 @@ hipError_t launch_rope_scatter_parts(const float* y, int splits, int64_t ldy, in
 
 
 hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, const void* table,
-                        int wbf16, int vocab, int dim, float* h, const StepState* st, hipStream_t s) {
+                        int wtype, int vocab, int dim, float* h, const StepState* st, hipStream_t s) {
     const dim3 grid(bsz * seqlen), block(256);
-    if (wbf16)
-        launch_kernel(embed_kernel<bf16>, grid, block, 0, s, tokens, ld, seqlen,
-                           static_cast<const bf16*>(table), vocab, dim, h, st);
-    else
-        launch_kernel(embed_kernel<float>, grid, block, 0, s, tokens, ld, seqlen,
-                           static_cast<const float*>(table), vocab, dim, h, st);
+    switch (wtype) {
+        case kStoreBf16:
+            launch_kernel(embed_kernel<bf16>, grid, block, 0, s, tokens, ld, seqlen,
+                          static_cast<const bf16*>(table), vocab, dim, h, st);
+            break;
+        case kStoreF16:
+            launch_kernel(embed_kernel<f16>, grid, block, 0, s, tokens, ld, seqlen,
+                          static_cast<const f16*>(table), vocab, dim, h, st);
+            break;
+        case kStoreF32:
+            launch_kernel(embed_kernel<float>, grid, block, 0, s, tokens, ld, seqlen,
+                          static_cast<const float*>(table), vocab, dim, h, st);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

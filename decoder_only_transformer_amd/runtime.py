@@ -27,7 +27,7 @@ def make_args(dim, n_layers, n_heads, n_kv_heads, vocab_size, hidden_dim, norm_e
               max_batch_size, max_seq_len, dtype: str) -> abi.llama_args:
     return abi.llama_args(dim, n_layers, n_heads, n_kv_heads, vocab_size, hidden_dim,
                           float(norm_eps), float(rope_theta), max_batch_size, max_seq_len,
-                          abi.LLAMA_BF16 if dtype == "bf16" else abi.LLAMA_FP32)
+                          abi.DTYPES[dtype])
 
 
 def stream_handle(stream: Optional[torch.cuda.Stream] = None) -> int:

@@ -45,7 +45,12 @@ typedef enum llama_status {
 
 typedef enum llama_dtype {
     LLAMA_BF16 = 0,  /* bf16 weights and KV cache; fp32 residual stream and accumulation */
-    LLAMA_FP32 = 1   /* fp32 weights, KV cache and arithmetic */
+    LLAMA_FP32 = 1,  /* fp32 weights, KV cache and arithmetic */
+    LLAMA_FP16 = 2   /* fp16 weights and KV cache (the reference implementation's dtype): the
+                        fp32 model's vector-ALU kernels, fp32 residual stream and accumulation,
+                        and the tensors the method stores in 16 bits (normalised operands, q,
+                        K/V, attention output, gated FFN activation) rounded to fp16 (nearest
+                        even) where they are produced.  Weights 16-byte aligned, as for bf16 */
 } llama_dtype;
 
 /*

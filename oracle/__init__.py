@@ -10,5 +10,5 @@ from .llama import (  # noqa: F401
     ModelArgs, ffn_hidden_dim, kv_cache_bytes, rms_norm, rope_frequencies, rope_angles,
     apply_rope, causal_mask, softmax, attention, silu, feed_forward, Oracle,
     argmax_lowest, sample_top_p, greedy_generate, teacher_forced_logits, args_from_workload,
-    workload_weights, round_bf16,
+    workload_weights, round_bf16, round_fp16,
 )

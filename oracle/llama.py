@@ -27,7 +27,8 @@ Readings taken where the pages leave a step open:
       produced; every operation still computes in the working precision.  The pages run
       the reference with 16-bit activations throughout (fp16, [AG] 6.4 and the loader
       description in [ST]); the bf16 method keeps the residual stream and all accumulation
-      in fp32 and rounds only at these points.  storage=None is the plain definition.
+      in fp32 and rounds only at these points.  storage="fp16" rounds at the same points to
+      IEEE binary16 (the fp16 model).  storage=None is the plain definition.
 """
 from __future__ import annotations
 
@@ -89,11 +90,26 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return np.ldexp(np.round(m * 256.0) / 256.0, e).astype(x.dtype, copy=False)
 
 
+def round_fp16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest IEEE binary16 value, kept in x's dtype.  Written from the format's
+    definition: 11 significant bits, so with x = m * 2^e (0.5 <= |m| < 1) the spacing is
+    2^(e - 11); below 2^-14 (subnormals) the spacing stays 2^-24; ties go to even; a result
+    above the largest finite value 65504 is infinity."""
+    x64 = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x64)
+    q = np.where(e < -13, 2.0 ** -24, np.ldexp(1.0, e - 11))
+    r = np.round(x64 / q) * q
+    r = np.where(np.abs(r) > 65504.0, np.copysign(np.inf, x64), r)
+    return r.astype(np.asarray(x).dtype, copy=False)
+
+
 def _storage_fn(storage: Optional[str]):
     if storage is None:
         return lambda x: x
     if storage == "bf16":
         return round_bf16
+    if storage == "fp16":
+        return round_fp16
     raise ValueError(storage)
 
 

@@ -156,13 +156,13 @@ def quantile_table(dtype: str, device="cpu") -> torch.Tensor:
         from scipy.special import ndtri
         p = (np.arange(1 << _TABLE_BITS, dtype=np.float64) + 0.5) / float(1 << _TABLE_BITS)
         t32 = torch.from_numpy((0.02 * ndtri(p)).astype(np.float32))
-        t = t32.to(torch.bfloat16) if dtype == "bf16" else t32
+        t = t32.to(torch_dtype(dtype))
         _TABLES[key] = t.to(device)
     return _TABLES[key]
 
 
 def torch_dtype(dtype: str) -> torch.dtype:
-    return torch.bfloat16 if dtype == "bf16" else torch.float32
+    return {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dtype]
 
 
 def gen_tensor(w: Workload, name: str, layer: int = 0, device="cpu",

@@ -48,6 +48,7 @@ def test_status_strings(lib):
 @pytest.mark.parametrize("kw,expect", [
     (dict(), abi.LLAMA_OK),
     (dict(dtype="bf16"), abi.LLAMA_OK),
+    (dict(dtype="fp16"), abi.LLAMA_OK),
     (dict(n_kv_heads=3), abi.LLAMA_ERR_INVALID_ARG),          # n_heads % n_kv_heads
     (dict(dim=250), abi.LLAMA_ERR_INVALID_ARG),               # dim % n_heads
     (dict(n_heads=16, n_kv_heads=1), abi.LLAMA_ERR_UNSUPPORTED),  # head_dim 16, n_rep 16
@@ -63,6 +64,18 @@ def test_check_args(lib, kw, expect):
     a = tiny(**kw)
     assert abi.llama_check_args(a) == expect
     assert (abi.llama_workspace_bytes(a) > 0) == (expect == abi.LLAMA_OK)
+
+
+def test_fp16_models_take_two_byte_caches_on_the_vector_path(lib):
+    """An fp16 model's workspace is the fp32 model's with the KV cache at 2 bytes an element:
+    K and V, 4 layers x 2 rows x 128 positions x 2 kv heads x 32 dims, 2 bytes fewer each."""
+    f32 = abi.llama_workspace_bytes(tiny(dtype="fp32"))
+    f16 = abi.llama_workspace_bytes(tiny(dtype="fp16"))
+    assert f32 - f16 == 2 * 4 * 2 * 128 * 2 * 32 * 2
+    bad = tiny()
+    bad.dtype = 3
+    assert abi.llama_check_args(bad) == abi.LLAMA_ERR_INVALID_ARG
+    assert abi.llama_workspace_bytes(bad) == 0
 
 
 def test_workspace_holds_kv_cache_of_pages_example(lib):

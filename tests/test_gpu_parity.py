@@ -121,7 +121,7 @@ def plain_distance(call_logits, tf_plain, min_len):
         o = tf_plain[:, min_len - 1 + i].astype(np.float64)
         worst = max(worst, np.abs(g - o).max())
         worst_cos = min(worst_cos, ((g * o).sum(-1) / np.linalg.norm(g, axis=-1) / np.linalg.norm(o, axis=-1)).min())
-    say(f"  vs plain fp32 oracle (bf16 storage effect): max|dlogit|={worst:.3e} min cos={worst_cos:.6f}")
+    say(f"  vs plain fp32 oracle (16-bit storage effect): max|dlogit|={worst:.3e} min cos={worst_cos:.6f}")
     return worst, worst_cos
 
 
@@ -228,6 +228,75 @@ SMALL_BF16 = {
                                                batch=4, prompt_len=600, gen_steps=6, weight_seed=14,
                                                prompt_seed=114, max_seq_len=640),
 }
+
+
+# ----------------------------------------------------------------------------- fp16 models
+
+# fp16 (the reference's dtype) runs the vector path with every 16-bit storage point rounded to
+# binary16.  Its 11 significant bits are 3 more than bf16's, so the bar is the stated bf16 bar
+# scaled by the ulp ratio, 2^-3.
+FP16_TOL = BF16_TOL / 8
+
+FP16 = {
+    "gqa": synth.WORKLOADS["tiny_fp32"].with_(name="tiny_fp16_gqa", dtype="fp16", batch=3,
+                                              prompt_len=0, prompt_len_range=(8, 40), gen_steps=16,
+                                              weight_seed=19, prompt_seed=119, max_seq_len=96),
+    # 6 decode rows (bf16 would take the skinny MFMA products; fp16 stays on the vector path),
+    # MHA with head_dim 64
+    "mha_b6": synth.WORKLOADS["tiny_fp32"].with_(name="tiny_fp16_mha_b6", dtype="fp16", n_heads=8,
+                                                 n_kv_heads=8, dim=512, hidden_dim=1536, vocab_size=1000,
+                                                 batch=6, prompt_len=0, prompt_len_range=(12, 50),
+                                                 gen_steps=12, weight_seed=20, prompt_seed=120, max_seq_len=96),
+}
+
+
+@pytest.mark.parametrize("name", list(FP16))
+def test_fp16_generate_matches_oracle(name):
+    wl = FP16[name]
+    say(f"case {wl}")
+    W = synth.gen_weights(wl, device="cuda")
+    assert W["layers"][0]["wq"].dtype == torch.float16
+    prompts = synth.prompts(wl)
+    tokens, logits, _ = gpu_generate(wl, W, prompts)
+    a = oracle.args_from_workload(wl)
+    hw = host_weights(wl, W)
+    tf = oracle.teacher_forced_logits(a, hw, tokens[:, :-1], np.float32, storage="fp16")
+    verify_generate(wl, prompts, tokens, logits, tf, FP16_TOL, COS_MIN)
+    plain = oracle.teacher_forced_logits(a, hw, tokens[:, :-1], np.float32)
+    plain_distance(logits, plain, min(len(p) for p in prompts))
+
+
+def test_fp16_prefill_all_positions_chunked_and_decode():
+    """Prefill of every position (whole, and in two chunks the second at start_pos > 0)
+    against the oracle's fp16-storage forward, and token-by-token decode against prefill."""
+    wl = FP16["gqa"]
+    say("case tiny_fp16_gqa: prefill all positions, chunked, decode")
+    W = synth.gen_weights(wl, device="cuda")
+    P = synth.prompts(wl)
+    S = min(len(p) for p in P)
+    tok = np.array([p[:S] for p in P], dtype=np.int32)
+    B = tok.shape[0]
+    c = S // 2
+    model = runtime.LlamaModel(args_of(wl), W)
+    dtok = torch.from_numpy(tok).cuda()
+    full = torch.empty((B, S, wl.vocab_size), device="cuda")
+    model.prefill(dtok, B, S, 0, full, all_positions=True)
+    a = torch.empty((B, c, wl.vocab_size), device="cuda")
+    b = torch.empty((B, S - c, wl.vocab_size), device="cuda")
+    model.prefill(dtok, B, c, 0, a, all_positions=True)
+    model.prefill(dtok, B, S - c, c, b, all_positions=True, col=c)
+    steps = torch.empty((S, B, wl.vocab_size), device="cuda")
+    for j in range(S):
+        model.decode_step(dtok, B, j, j, steps[j])
+    torch.cuda.synchronize()
+    ref = oracle.Oracle(oracle.args_from_workload(wl), host_weights(wl, W), B, np.float32,
+                        storage="fp16").forward(tok, 0)
+    d_full = np.abs(full.cpu().numpy() - ref).max()
+    d_chunk = np.abs(np.concatenate([a.cpu().numpy(), b.cpu().numpy()], 1) - ref).max()
+    d_dec = (steps.transpose(0, 1) - full).abs().max().item()
+    say(f"  max|dlogit| prefill {d_full:.3e} chunked {d_chunk:.3e} decode-vs-prefill {d_dec:.3e}")
+    assert d_full <= FP16_TOL and d_chunk <= FP16_TOL and d_dec <= FP16_TOL
+    model.close()
 
 
 @pytest.mark.parametrize("name", list(SMALL_BF16))

@@ -397,6 +397,47 @@ def test_round_bf16_matches_torch_rne():
     assert np.all(np.abs(r - y) <= np.ldexp(1.0 / 512, e) * (1 + 1e-12))
 
 
+def test_round_fp16_matches_numpy_binary16():
+    """The binary16 rounding written from the format's definition against numpy's float16
+    conversion (a library routine): normals, subnormals, exact ties of both parities,
+    overflow to infinity, signed zeros."""
+    rng = np.random.default_rng(33)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-22, 12, 200000))).astype(np.float32)
+    # exact ties between two binary16 neighbours: a binary16 value plus half its spacing
+    h = rng.standard_normal(2000).astype(np.float16)
+    h = h[np.isfinite(h) & (h != 0)].astype(np.float64)
+    _, e = np.frexp(h)
+    spacing = np.where(e < -13, 2.0 ** -24, np.ldexp(1.0, e - 11))
+    ties = (h + spacing / 2).astype(np.float32)
+    edge = np.array([0.0, -0.0, 1.0, 65504.0, 65519.0, 65520.0, -65520.0, 2.0 ** -24, 2.0 ** -25,
+                     1.5 * 2.0 ** -24, 2.0 ** -14, 3.0 * 2.0 ** -26], dtype=np.float32)
+    x = np.concatenate([x, ties, edge])
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).astype(np.float32)
+    got = oracle.round_fp16(x)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    # worked values: ties to even at 1 + 2^-11 (down to 1) and 1 + 3 * 2^-11 (up to 1 + 2^-9)
+    w = oracle.round_fp16(np.array([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 65520.0, 0.5 * 2.0 ** -24]))
+    assert w[0] == 1.0 and w[1] == 1 + 2.0 ** -9 and np.isinf(w[2]) and w[3] == 0.0
+
+
+def test_fp16_storage_keeps_prefill_equal_to_decode_and_cache_in_fp16():
+    a = small_args()
+    W = random_weights(a, seed=34)
+    tokens = np.random.default_rng(35).integers(0, a.vocab_size, size=(2, 10))
+    full = oracle.Oracle(a, W, 2, dtype=np.float64, storage="fp16")
+    lf = full.forward(tokens, 0)
+    inc = oracle.Oracle(a, W, 2, dtype=np.float64, storage="fp16")
+    steps = np.stack([inc.forward(tokens[:, j:j + 1], j)[:, 0] for j in range(10)], 1)
+    np.testing.assert_allclose(steps, lf, rtol=1e-9, atol=1e-9)
+    kv = full.cache_k[:, :, :10]
+    assert np.array_equal(kv.astype(np.float16).astype(np.float64), kv)
+    plain = oracle.Oracle(a, W, 2, dtype=np.float64).forward(tokens, 0)
+    bf = oracle.Oracle(a, W, 2, dtype=np.float64, storage="bf16").forward(tokens, 0)
+    # binary16 keeps 3 more significant bits than bf16: its rounding moves the logits less
+    assert 0 < np.abs(plain - lf).max() < np.abs(plain - bf).max()
+
+
 def test_bf16_storage_keeps_prefill_equal_to_decode_and_cache_in_bf16():
     a = small_args()
     W = random_weights(a, seed=31)
