@@ -215,6 +215,12 @@ SMALL_BF16 = {
                                                n_kv_heads=2, dim=256, hidden_dim=768, vocab_size=512,
                                                batch=17, prompt_len=0, prompt_len_range=(10, 50),
                                                gen_steps=12, weight_seed=18, prompt_seed=118, max_seq_len=96),
+    # 20 decode rows at a width where wo and w2 split K in two: the split partials of a second
+    # row tile with 4 live rows, added by the RMSNorm that follows
+    "b20": synth.WORKLOADS["tiny_fp32"].with_(name="small_bf16_b20", dtype="bf16", n_heads=8,
+                                              n_kv_heads=8, dim=1024, hidden_dim=2816, vocab_size=1000,
+                                              batch=20, prompt_len=0, prompt_len_range=(10, 30),
+                                              gen_steps=12, weight_seed=21, prompt_seed=121, max_seq_len=64),
     # RoPE base 500000 instead of 10000 (theta is an argument of the ABI, not a constant)
     "theta": synth.WORKLOADS["tiny_fp32"].with_(name="small_bf16_theta", dtype="bf16", n_heads=8,
                                                 n_kv_heads=2, dim=512, hidden_dim=1536, vocab_size=1000,
