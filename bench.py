@@ -37,7 +37,7 @@ def decode_step_bytes(wl, ctx: int) -> float:
     positions [0, ctx) read, one position written)."""
     D, L, F, V = wl.dim, wl.n_layers, wl.hidden_dim, wl.vocab_size
     hd, H, KVH, B = wl.head_dim, wl.n_heads, wl.n_kv_heads, wl.batch
-    e = 2 if wl.dtype == "bf16" else 4
+    e = 4 if wl.dtype == "fp32" else 2
     per_layer = (H * hd * D + 2 * KVH * hd * D + D * H * hd + 3 * F * D + 2 * D) * e
     weights = L * per_layer + V * D * e + D * e + B * D * e
     kv = B * L * 2 * KVH * hd * e * (ctx + 1)
@@ -56,7 +56,7 @@ def prefill_bytes(wl, B: int, S: int) -> float:
     read), the K/V of the B*S positions written, the last positions' logits written."""
     D, L, F, V = wl.dim, wl.n_layers, wl.hidden_dim, wl.vocab_size
     hd, H, KVH = wl.head_dim, wl.n_heads, wl.n_kv_heads
-    e = 2 if wl.dtype == "bf16" else 4
+    e = 4 if wl.dtype == "fp32" else 2
     per_layer = (H * hd * D + 2 * KVH * hd * D + D * H * hd + 3 * F * D + 2 * D) * e
     return L * per_layer + V * D * e + D * e + B * S * D * e + B * S * L * 2 * KVH * hd * e + B * V * 4
 
@@ -64,7 +64,7 @@ def prefill_bytes(wl, B: int, S: int) -> float:
 def w13_launch_bytes(wl) -> float:
     """Per launch of the decode [w1;w3] GEMV: both weight matrices, the norm weight, the
     residual rows read and the gated rows written."""
-    e = 2 if wl.dtype == "bf16" else 4
+    e = 4 if wl.dtype == "fp32" else 2
     return 2 * wl.hidden_dim * wl.dim * e + wl.dim * e + wl.batch * wl.dim * 4 + wl.batch * wl.hidden_dim * 4
 
 
@@ -205,10 +205,16 @@ def main() -> int:
     pf = prefill_flops(wl, B, S)
     prefill_tflops = pf * args.steps / (pre_ms / 1e3) / 1e12
 
-    # Live per-kernel timing of the dominant decode kernel, same launch configuration.
+    # Live per-kernel timing of the dominant decode kernel, same launch configuration: one
+    # more step, with the class selected after its prefill (the vector path of fp32 / fp16
+    # models runs the prefill on the same kernel class, with many rows per launch)
     kc = abi.KERNEL_CLASSES[args.profile_class]
+    run.reset()
+    run.prefill()
+    torch.cuda.synchronize()
     runtime.check("profile_select", abi.llama_profile_select(model.ctx, kc))
-    one_step()
+    for i in range(1, run.n_calls):
+        run.decode(i)
     torch.cuda.synchronize()
     st, n_launch, k_ms = abi.llama_profile_read(model.ctx)
     runtime.check("profile_read", st)

@@ -58,7 +58,7 @@ class Workload:
     prompt_len: int                      # fixed prompt length (0 when ragged)
     prompt_len_range: Optional[tuple]    # (lo, hi) inclusive, for ragged prompts
     gen_steps: int                       # max_gen_len of the greedy generate schedule
-    dtype: str                           # "bf16" or "fp32"
+    dtype: str                           # "bf16", "fp16" or "fp32"
     weight_seed: int
     prompt_seed: int
 
@@ -76,6 +76,10 @@ WORKLOADS: Dict[str, Workload] = {
                  2, 16, None, 16, "fp32", 1, 1001),
         Workload("llama2_7b_b1", 4096, 32, 32, 32, 11008, 32000, 1e-5, 10000.0, 4096,
                  1, 128, None, 128, "bf16", 2, 1002),
+        # the 7B batch-1 workload with fp16 weights and cache (the reference's dtype; the
+        # vector-ALU path)
+        Workload("llama2_7b_b1_fp16", 4096, 32, 32, 32, 11008, 32000, 1e-5, 10000.0, 4096,
+                 1, 128, None, 128, "fp16", 2, 1002),
         Workload("llama2_7b_b32_ragged", 4096, 32, 32, 32, 11008, 32000, 1e-5, 10000.0, 4096,
                  32, 0, (256, 512), 256, "bf16", 3, 1003),
         Workload("llama2_13b_b16", 5120, 40, 40, 40, 13824, 32000, 1e-5, 10000.0, 4096,
