@@ -407,12 +407,18 @@ def test_llama2_7b_widths_one_layer_chunked_prefill_all_positions():
     assert d <= tol and cos >= COS_MIN
 
 
-@pytest.mark.parametrize("name", ["gqa8", "mha", "b6"])
+@pytest.mark.parametrize("name", ["gqa8", "mha", "b6", "b20", "fp16_mha_b6", "tiny_fp32"])
 def test_decode_graph_replays_match_eager_launches(name):
     """Decode steps replay one captured graph per split count; the generate loop puts eager
     work (argmax, select, step-state writes) between replays.  Every replay's logits must
-    equal the eagerly launched step bit for bit (same kernels, same arithmetic)."""
-    wl = SMALL_BF16[name]
+    equal the eagerly launched step bit for bit (same kernels, same arithmetic).  Cases: bf16
+    on the vector and skinny paths (b20: with the wo/w2 K split), fp16 and fp32 models."""
+    if name in SMALL_BF16:
+        wl = SMALL_BF16[name]
+    elif name.startswith("fp16_"):
+        wl = FP16[name[len("fp16_"):]]
+    else:
+        wl = synth.WORKLOADS[name]
     say(f"case {wl.name}: graph replays vs eager launches")
     W = synth.gen_weights(wl, device="cuda")
     prompts = synth.prompts(wl)
