@@ -321,6 +321,27 @@ def test_small_bf16_generate_matches_oracle(name):
     assert cos > 0.99
 
 
+def test_small_bf16_cache_filled_to_max_seq_len_with_one_token_prompt():
+    """Edge cases of the schedule: one prompt of a single token (the prefill covers one
+    position), the others up to 40, and total_len = max_seq_len (the last decode call writes
+    and attends to the cache's last position and reads the RoPE table's last row), at a batch
+    that takes the skinny decode products."""
+    wl = SMALL_BF16["gqa8"].with_(name="small_bf16_edge", batch=8, max_seq_len=64, gen_steps=30,
+                                  weight_seed=22, prompt_seed=122)
+    rng = np.random.default_rng(122)
+    prompts = [[int(rng.integers(3, wl.vocab_size))]] + \
+              [rng.integers(3, wl.vocab_size, size=int(n)).tolist() for n in rng.integers(2, 41, size=7)]
+    total_len = min(wl.max_seq_len, wl.gen_steps + max(len(p) for p in prompts))
+    assert total_len == wl.max_seq_len
+    say(f"case {wl.name}: prompt lengths {[len(p) for p in prompts]}, total_len {total_len}")
+    W = synth.gen_weights(wl, device="cuda")
+    tokens, logits, _ = gpu_generate(wl, W, prompts)
+    assert tokens.shape[1] == wl.max_seq_len and logits.shape[0] == wl.max_seq_len - 1
+    a = oracle.args_from_workload(wl)
+    tf = oracle.teacher_forced_logits(a, host_weights(wl, W), tokens[:, :-1], np.float32, storage="bf16")
+    verify_generate(wl, prompts, tokens, logits, tf, BF16_TOL, COS_MIN)
+
+
 def test_small_bf16_prefill_equals_token_by_token_decode():
     wl = SMALL_BF16["gqa8"]
     say("case small bf16 gqa8: prefill (MFMA path) vs decode (GEMV path)")
