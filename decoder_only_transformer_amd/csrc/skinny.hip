@@ -19,7 +19,9 @@
 // as many bytes per stage as one weight block, and the bytes a CU takes in per stage, not
 // the weights alone, set the pace.  At the end the waves' partial sums meet in LDS.
 // Epilogues: RoPE + bf16 q / KV append, residual add, SiLU gate (bf16 out, optionally in
-// fragment-major order for the next product), fp32 logits.
+// fragment-major order for the next product), fp32 logits.  A residual product may split K
+// over gridDim.y (SkinnyArgs::ksplit): each split then stores its fp32 sum, and the RMSNorm
+// launched next adds the splits to the residual in split order.
 #include "common.h"
 #include "kernels.h"
 
