@@ -92,10 +92,16 @@ def measured_traffic(kernel_class: str, workload: str):
     return float(fields["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(wl, dev_weights, prompts, decode_steps: int = 48) -> dict:
-    """The oracle as it stands, on this host, over a bounded sample of the same workload:
-    the whole model (every layer and the head) in fp32 NumPy, prefill of the prompt batch
-    and then the first `decode_steps` single-token decode calls.  Nothing is scaled."""
+def cpu_baseline(wl, dev_weights, prompts, decode_steps: int = 48, max_fp32_bytes: float = 32e9,
+                 max_tokens: int = 4096) -> dict:
+    """The oracle as it stands, on this host, over a bounded sample of the same workload.
+
+    Workloads whose fp32 weights fit in `max_fp32_bytes` and whose prompt batch has at most
+    `max_tokens` tokens: the whole model (every layer and the head) in fp32 NumPy, prefill of
+    the prompt batch and then the first `decode_steps` single-token decode calls; nothing is
+    scaled.  Larger ones: the first 2 layers and the head, prefill of at most 1024 prompt
+    tokens (the first rows, or the first 1024 tokens of row 0) and 4 decode calls of those rows,
+    with the times scaled by n_layers / 2 ("scaled" in the sample description)."""
     import dataclasses
     import numpy as np
     import oracle
@@ -115,7 +121,19 @@ def cpu_baseline(wl, dev_weights, prompts, decode_steps: int = 48) -> dict:
         return cache[k]
     tok = np.array([p[:min(len(x) for x in prompts)] for p in prompts])
     B, S = tok.shape
-    a = dataclasses.replace(oracle.args_from_workload(wl), max_seq_len=S + decode_steps + 1)
+    e = 4  # the oracle's fp32 copy of every weight
+    fp32_bytes = e * (wl.n_layers * (2 * wl.dim * wl.dim + 2 * wl.n_kv_heads * wl.head_dim * wl.dim
+                                     + 3 * wl.hidden_dim * wl.dim) + 2 * wl.vocab_size * wl.dim)
+    scaled = fp32_bytes > max_fp32_bytes or B * S > max_tokens
+    n_layers, scale = wl.n_layers, 1.0
+    if scaled:
+        rows = max(1, min(B, 1024 // S))
+        tok = tok[:rows, :min(S, 1024)]
+        B, S = tok.shape
+        decode_steps = 4
+        n_layers, scale = 2, wl.n_layers / 2.0
+    a = dataclasses.replace(oracle.args_from_workload(wl), n_layers=n_layers,
+                            max_seq_len=S + decode_steps + 1)
     m = oracle.Oracle(a, provider, B, np.float32)
     m.forward(tok[:, :1], 0)                # first touch: weights to host fp32, BLAS warm-up
     t0 = time.perf_counter()
@@ -126,9 +144,11 @@ def cpu_baseline(wl, dev_weights, prompts, decode_steps: int = 48) -> dict:
         logits = m.forward(nxt, S + j)
         nxt = oracle.argmax_lowest(logits[:, -1]).reshape(B, 1)
     t2 = time.perf_counter()
-    return {"value": B * decode_steps / (t2 - t1), "unit": "tok/s", "cores": threads, "kind": "oracle",
-            "prefill_tok_per_s": B * S / (t1 - t0),
-            "sample": (f"{wl.name}: oracle fp32 NumPy, all {wl.n_layers} layers and the head, "
+    what = (f"scaled: the first 2 of {wl.n_layers} layers and the head, times x {scale:g}"
+            if scaled else f"all {wl.n_layers} layers and the head")
+    return {"value": B * decode_steps / ((t2 - t1) * scale), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "prefill_tok_per_s": B * S / ((t1 - t0) * scale),
+            "sample": (f"{wl.name}: oracle fp32 NumPy, {what}, "
                        f"{S}-token prefill of {B} row(s) then {decode_steps} greedy decode calls "
                        f"({t2 - t0:.1f} s timed); host cpu_count={os.cpu_count()}")}
 
