@@ -107,9 +107,11 @@ def cpu_baseline(wl, dev_weights, prompts, decode_steps: int = 48, max_fp32_byte
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"] or threadpool_info()
+        threads = max((p.get("num_threads", 1) for p in pools), default=1)
+        blas = ",".join(sorted({str(p.get("internal_api", "?")) for p in pools})) or "?"
     except Exception:
-        threads = os.cpu_count()
+        threads, blas = os.cpu_count(), "?"
 
     cache = {}
 
@@ -150,7 +152,8 @@ def cpu_baseline(wl, dev_weights, prompts, decode_steps: int = 48, max_fp32_byte
             "prefill_tok_per_s": B * S / ((t1 - t0) * scale),
             "sample": (f"{wl.name}: oracle fp32 NumPy, {what}, "
                        f"{S}-token prefill of {B} row(s) then {decode_steps} greedy decode calls "
-                       f"({t2 - t0:.1f} s timed); host cpu_count={os.cpu_count()}")}
+                       f"({t2 - t0:.1f} s timed); host cpu_count={os.cpu_count()}, BLAS {blas} "
+                       f"on {threads} threads")}
 
 
 def main() -> int:
