@@ -17,6 +17,8 @@ the bf16 format, not the kernels.
 import os
 import sys
 
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -520,10 +522,14 @@ def _tf_pair(wl, W, tokens):
             cache[(n, l)] = t.double().cpu().numpy()
         return cache[(n, l)].astype(dt, copy=False)
     hook = lambda l: say(f"    oracle layer {l}") if l % 8 == 0 else None  # noqa: E731
+    t0 = time.perf_counter()
     t32 = oracle.teacher_forced_logits(a, lambda n, l: prov(n, l, np.float32), tokens, np.float32,
                                        layer_hook=hook, storage="bf16")
+    t1 = time.perf_counter()
     t64 = oracle.teacher_forced_logits(a, lambda n, l: prov(n, l, np.float64), tokens, np.float64,
                                        layer_hook=hook, storage="bf16")
+    say(f"  oracle teacher-forced pass over {tokens.size} positions: fp32 {t1 - t0:.1f} s, "
+        f"fp64 {time.perf_counter() - t1:.1f} s")
     return t32, t64
 
 
@@ -633,9 +639,13 @@ def check_rows(wl, W, prompts, tokens, call_logits, rows):
     min_len = min(len(p) for p in prompts)
     for b in rows:
         tb = tokens[b:b + 1, :-1]
+        c0 = time.perf_counter()
         t1 = oracle.teacher_forced_logits(a, base, tb, np.float32, storage="bf16")[0]
+        c1 = time.perf_counter()
         t2 = oracle.teacher_forced_logits(a, permuted_provider(base, wl.dim, wl.hidden_dim), tb,
                                           np.float32, storage="bf16")[0]
+        say(f"  row {b}: oracle teacher-forced pass over {tb.size} positions {c1 - c0:.1f} s "
+            f"(permuted evaluation {time.perf_counter() - c1:.1f} s)")
         sel = np.arange(min_len - 1, min_len - 1 + call_logits.shape[0])
         spread = float(np.abs(t1[sel] - t2[sel]).max())
         tol = max(BF16_TOL, 1.5 * spread)
