@@ -230,7 +230,10 @@ class Oracle:
         self.args = args
         self.dtype = dtype
         self.st = _storage_fn(storage)
-        self.w: WeightFn = weights if callable(weights) else _dense_weights(weights, dtype)
+        # every weight in the working precision: arrays a callable hands over in another dtype
+        # (fp32 copies of the device tensors) would otherwise set the precision of the sums
+        self.w: WeightFn = ((lambda n, l: np.asarray(weights(n, l)).astype(dtype, copy=False))
+                            if callable(weights) else _dense_weights(weights, dtype))
         shape = (args.n_layers, max_batch_size, args.max_seq_len, args.kv_heads, args.head_dim)
         self.cache_k = np.zeros(shape, dtype=dtype)
         self.cache_v = np.zeros(shape, dtype=dtype)

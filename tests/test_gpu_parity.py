@@ -420,7 +420,7 @@ def test_llama2_7b_widths_one_layer_chunked_prefill_all_positions():
     ref = oracle.Oracle(a_, base, B, np.float32, storage="bf16").forward(tok, 0)
     # the bar over this many positions: the oracle's own spread against a second correct
     # fp32 evaluation (consistently permuted model and FFN dimensions), as at depth (R19)
-    ref2 = oracle.Oracle(a_, permuted_provider(base, wl.dim, wl.hidden_dim), B, np.float32,
+    ref2 = oracle.Oracle(a_, permuted_provider(W, wl.dim, wl.hidden_dim), B, np.float32,
                          storage="bf16").forward(tok, 0)
     spread = float(np.abs(ref - ref2).max())
     tol = max(BF16_TOL, 1.5 * spread)
@@ -597,23 +597,33 @@ def test_llama2_7b_b1_generate_matches_oracle():
 # second, equivalent evaluation: permuting the model dimension consistently across all
 # weights leaves the function unchanged but changes every fp32 summation order.
 
-def permuted_provider(base, dim, hidden, seed=7):
+def permuted_provider(W, dim, hidden, seed=7):
+    """The model with its dim and hidden axes permuted consistently: the same function, with
+    every fp32 sum over them in another order.  The weights are gathered from the generator's
+    device tensors with torch's indexing (data movement only) and handed to the oracle as host
+    fp32 arrays, one layer at a time."""
     rng = np.random.default_rng(seed)
     pd, ph = rng.permutation(dim), rng.permutation(hidden)
+    cache = {}
 
     def get(name, layer):
-        w = base(name, layer)
+        if (name, layer) in cache:
+            return cache[(name, layer)]
+        if layer >= 0:
+            for k in [k for k in cache if k[1] >= 0 and k[1] != layer]:
+                del cache[k]
+        w = W[name] if layer < 0 else W["layers"][layer][name]
+        td, th = torch.from_numpy(pd).to(w.device), torch.from_numpy(ph).to(w.device)
         if name in ("tok_embeddings", "output", "wq", "wk", "wv"):
-            return np.ascontiguousarray(w[:, pd])
-        if name in ("norm", "attention_norm", "ffn_norm"):
-            return np.ascontiguousarray(w[pd])
-        if name in ("wo",):
-            return np.ascontiguousarray(w[pd, :])
-        if name in ("w1", "w3"):
-            return np.ascontiguousarray(w[ph][:, pd])
-        if name == "w2":
-            return np.ascontiguousarray(w[pd][:, ph])
-        return w
+            w = w[:, td]
+        elif name in ("norm", "attention_norm", "ffn_norm", "wo"):
+            w = w[td]
+        elif name in ("w1", "w3"):
+            w = w[th][:, td]
+        elif name == "w2":
+            w = w[td][:, th]
+        cache[(name, layer)] = w.float().cpu().numpy()
+        return cache[(name, layer)]
     return get
 
 
@@ -642,7 +652,7 @@ def check_rows(wl, W, prompts, tokens, call_logits, rows):
         c0 = time.perf_counter()
         t1 = oracle.teacher_forced_logits(a, base, tb, np.float32, storage="bf16")[0]
         c1 = time.perf_counter()
-        t2 = oracle.teacher_forced_logits(a, permuted_provider(base, wl.dim, wl.hidden_dim), tb,
+        t2 = oracle.teacher_forced_logits(a, permuted_provider(W, wl.dim, wl.hidden_dim), tb,
                                           np.float32, storage="bf16")[0]
         say(f"  row {b}: oracle teacher-forced pass over {tb.size} positions {c1 - c0:.1f} s "
             f"(permuted evaluation {time.perf_counter() - c1:.1f} s)")

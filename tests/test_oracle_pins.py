@@ -397,6 +397,19 @@ def test_round_bf16_matches_torch_rne():
     assert np.all(np.abs(r - y) <= np.ldexp(1.0 / 512, e) * (1 + 1e-12))
 
 
+def test_working_precision_is_the_dtype_argument_whatever_the_provider_hands_over():
+    """A weight callable that returns fp32 arrays must not lower a float64 oracle's precision:
+    the result equals the one from float64 arrays of the same values, bit for bit."""
+    a = small_args()
+    W = random_weights(a, seed=36)
+    def getter(dt):
+        return lambda n, l: np.asarray(W[n] if l < 0 else W["layers"][l][n], dtype=np.float32).astype(dt)
+    tokens = np.random.default_rng(37).integers(0, a.vocab_size, size=(2, 9))
+    r32 = oracle.Oracle(a, getter(np.float32), 2, dtype=np.float64).forward(tokens, 0)
+    r64 = oracle.Oracle(a, getter(np.float64), 2, dtype=np.float64).forward(tokens, 0)
+    assert r32.dtype == np.float64 and np.array_equal(r32, r64)
+
+
 def test_round_fp16_matches_numpy_binary16():
     """The binary16 rounding written from the format's definition against numpy's float16
     conversion (a library routine): normals, subnormals, exact ties of both parities,
