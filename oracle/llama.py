@@ -358,7 +358,8 @@ def teacher_forced_logits(args: ModelArgs, weights, tokens: np.ndarray,
     computed layer by layer (each layer's weights are touched once).  By the causal mask
     ([AG] 8.4 note), position j's logits equal what an incremental run would emit at the
     call that ends at j.  tokens (B, T) -> logits (B, T, vocab)."""
-    wf: WeightFn = weights if callable(weights) else _dense_weights(weights, dtype)
+    wf: WeightFn = ((lambda n, l: np.asarray(weights(n, l)).astype(dtype, copy=False))
+                    if callable(weights) else _dense_weights(weights, dtype))
     st = _storage_fn(storage)
     tokens = np.asarray(tokens)
     B, T = tokens.shape

@@ -408,6 +408,11 @@ def test_working_precision_is_the_dtype_argument_whatever_the_provider_hands_ove
     r32 = oracle.Oracle(a, getter(np.float32), 2, dtype=np.float64).forward(tokens, 0)
     r64 = oracle.Oracle(a, getter(np.float64), 2, dtype=np.float64).forward(tokens, 0)
     assert r32.dtype == np.float64 and np.array_equal(r32, r64)
+    t32 = oracle.teacher_forced_logits(a, getter(np.float32), tokens, np.float64)
+    t64 = oracle.teacher_forced_logits(a, getter(np.float64), tokens, np.float64)
+    assert np.array_equal(t32, t64)
+    # and the other way round: a float32 oracle computes in float32 from float64 arrays
+    assert oracle.teacher_forced_logits(a, getter(np.float64), tokens, np.float32).dtype == np.float32
 
 
 def test_round_fp16_matches_numpy_binary16():
