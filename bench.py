@@ -168,7 +168,7 @@ def main() -> int:
                     help="cap on generated positions per step (profiler runs only; 0 = the workload's)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         return 2
 
