@@ -1,4 +1,4 @@
-"""Host-side driver around the C ABI: device memory for weights and workspace (torch),
+"""Host-side runtime around the C ABI: device memory for weights and workspace (torch),
 the generate loop's schedule, and status checking.  No model arithmetic happens here:
 every step of the forward pass, the greedy pick and the token select run in the library.
 """
