@@ -28,7 +28,9 @@ Readings taken where the pages leave a step open:
       the reference with 16-bit activations throughout (fp16, [AG] 6.4 and the loader
       description in [ST]); the bf16 method keeps the residual stream and all accumulation
       in fp32 and rounds only at these points.  storage="fp16" rounds at the same points to
-      IEEE binary16 (the fp16 model).  storage=None is the plain definition.
+      IEEE binary16 (the fp16 model).  storage="bf16_kv" rounds only the cached k and v
+      to bf16 (the cache format alone, everything else exact): it measures what the 16-bit
+      cache by itself costs.  storage=None is the plain definition.
 """
 from __future__ import annotations
 
@@ -103,13 +105,18 @@ def round_fp16(x: np.ndarray) -> np.ndarray:
     return r.astype(np.asarray(x).dtype, copy=False)
 
 
-def _storage_fn(storage: Optional[str]):
+def _storage_fns(storage: Optional[str]):
+    """(rounding of the activations the method stores in 16 bits, rounding of the cached k
+    and v) for a storage mode."""
+    keep = lambda x: x  # noqa: E731
     if storage is None:
-        return lambda x: x
+        return keep, keep
     if storage == "bf16":
-        return round_bf16
+        return round_bf16, round_bf16
     if storage == "fp16":
-        return round_fp16
+        return round_fp16, round_fp16
+    if storage == "bf16_kv":
+        return keep, round_bf16
     raise ValueError(storage)
 
 
@@ -229,7 +236,7 @@ class Oracle:
                  storage: Optional[str] = None):
         self.args = args
         self.dtype = dtype
-        self.st = _storage_fn(storage)
+        self.st, self.st_kv = _storage_fns(storage)
         # every weight in the working precision: arrays a callable hands over in another dtype
         # (fp32 copies of the device tensors) would otherwise set the precision of the sums
         self.w: WeightFn = ((lambda n, l: np.asarray(weights(n, l)).astype(dtype, copy=False))
@@ -246,7 +253,7 @@ class Oracle:
         assert start_pos + S <= a.max_seq_len and B <= self.cache_k.shape[1]
         hd, H, KVH = a.head_dim, a.n_heads, a.kv_heads
         positions = list(range(start_pos, start_pos + S))
-        st = self.st
+        st, st_kv = self.st, self.st_kv
         h = self.w("tok_embeddings", -1)[tokens]                       # (B, S, D)
         for l in range(a.n_layers):
             w = lambda n: self.w(n, l)  # noqa: E731
@@ -255,9 +262,9 @@ class Oracle:
             k = (x @ w("wk").T).reshape(B, S, KVH, hd)
             v = (x @ w("wv").T).reshape(B, S, KVH, hd)
             q = st(apply_rope(q, positions, a.rope_theta))
-            k = st(apply_rope(k, positions, a.rope_theta))
+            k = st_kv(apply_rope(k, positions, a.rope_theta))
             self.cache_k[l, :B, start_pos:start_pos + S] = k
-            self.cache_v[l, :B, start_pos:start_pos + S] = st(v)
+            self.cache_v[l, :B, start_pos:start_pos + S] = st_kv(v)
             keys = self.cache_k[l, :B, :start_pos + S]
             vals = self.cache_v[l, :B, :start_pos + S]
             o = st(attention(q, keys, vals, start_pos, a.n_rep).reshape(B, S, H * hd))
@@ -360,7 +367,7 @@ def teacher_forced_logits(args: ModelArgs, weights, tokens: np.ndarray,
     call that ends at j.  tokens (B, T) -> logits (B, T, vocab)."""
     wf: WeightFn = ((lambda n, l: np.asarray(weights(n, l)).astype(dtype, copy=False))
                     if callable(weights) else _dense_weights(weights, dtype))
-    st = _storage_fn(storage)
+    st, st_kv = _storage_fns(storage)
     tokens = np.asarray(tokens)
     B, T = tokens.shape
     hd, H, KVH = args.head_dim, args.n_heads, args.kv_heads
@@ -372,8 +379,8 @@ def teacher_forced_logits(args: ModelArgs, weights, tokens: np.ndarray,
         w = lambda n: wf(n, l)  # noqa: E731
         x = st(rms_norm(h, w("attention_norm"), args.norm_eps))
         q = st(apply_rope((x @ w("wq").T).reshape(B, T, H, hd), positions, args.rope_theta))
-        k = st(apply_rope((x @ w("wk").T).reshape(B, T, KVH, hd), positions, args.rope_theta))
-        v = st((x @ w("wv").T).reshape(B, T, KVH, hd))
+        k = st_kv(apply_rope((x @ w("wk").T).reshape(B, T, KVH, hd), positions, args.rope_theta))
+        v = st_kv((x @ w("wv").T).reshape(B, T, KVH, hd))
         o = st(attention(q, k, v, 0, args.n_rep).reshape(B, T, H * hd))
         h = h + o @ w("wo").T
         x = st(rms_norm(h, w("ffn_norm"), args.norm_eps))

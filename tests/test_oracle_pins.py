@@ -220,11 +220,18 @@ def test_feed_forward_gate_zero_and_linear_orientation():
 
 # ----------------------------------------------------------------------------- whole model
 
-def torch_model_forward(a: ModelArgs, W: dict, tokens: np.ndarray) -> np.ndarray:
+def torch_model_forward(a: ModelArgs, W: dict, tokens: np.ndarray, act=None, kv=None) -> np.ndarray:
     """The pre-norm block of the pages composed from torch library routines (F.embedding,
     F.rms_norm, F.linear, complex RoPE via torch.polar, SDPA with repeat-interleave GQA,
-    F.silu), fp64, one causal pass from position 0."""
+    F.silu), fp64, one causal pass from position 0.
+
+    act / kv: optional storage roundings (numpy functions) applied to the stored activations
+    (normalised operands, q after RoPE, attention output, gated FFN activation) and to the
+    cached k (after RoPE) and v, the points the 16-bit method stores."""
     t = lambda x: torch.from_numpy(np.asarray(x, dtype=np.float64))  # noqa: E731
+    keep = lambda x: x  # noqa: E731
+    ra = (lambda x: torch.from_numpy(act(x.numpy()))) if act else keep  # noqa: E731
+    rk = (lambda x: torch.from_numpy(kv(x.numpy()))) if kv else keep  # noqa: E731
     B, S = tokens.shape
     hd = a.head_dim
     freqs = 1.0 / (a.rope_theta ** (torch.arange(0, hd, 2, dtype=torch.float64) / hd))
@@ -236,16 +243,16 @@ def torch_model_forward(a: ModelArgs, W: dict, tokens: np.ndarray) -> np.ndarray
         return torch.view_as_real(xc * cis).reshape(x.shape)
     h = F.embedding(torch.from_numpy(tokens), t(W["tok_embeddings"]))
     for L in W["layers"]:
-        x = F.rms_norm(h, (a.dim,), t(L["attention_norm"]), eps=a.norm_eps)
-        q = rope(F.linear(x, t(L["wq"])).view(B, S, a.n_heads, hd))
-        k = rope(F.linear(x, t(L["wk"])).view(B, S, a.kv_heads, hd))
-        v = F.linear(x, t(L["wv"])).view(B, S, a.kv_heads, hd)
+        x = ra(F.rms_norm(h, (a.dim,), t(L["attention_norm"]), eps=a.norm_eps))
+        q = ra(rope(F.linear(x, t(L["wq"])).view(B, S, a.n_heads, hd)))
+        k = rk(rope(F.linear(x, t(L["wk"])).view(B, S, a.kv_heads, hd)))
+        v = rk(F.linear(x, t(L["wv"])).view(B, S, a.kv_heads, hd))
         o = F.scaled_dot_product_attention(q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2),
                                            is_causal=True, enable_gqa=True)
-        h = h + F.linear(o.transpose(1, 2).reshape(B, S, -1), t(L["wo"]))
-        x = F.rms_norm(h, (a.dim,), t(L["ffn_norm"]), eps=a.norm_eps)
-        h = h + F.linear(F.silu(F.linear(x, t(L["w1"]))) * F.linear(x, t(L["w3"])), t(L["w2"]))
-    x = F.rms_norm(h, (a.dim,), t(W["norm"]), eps=a.norm_eps)
+        h = h + F.linear(ra(o.transpose(1, 2).reshape(B, S, -1)), t(L["wo"]))
+        x = ra(F.rms_norm(h, (a.dim,), t(L["ffn_norm"]), eps=a.norm_eps))
+        h = h + F.linear(ra(F.silu(F.linear(x, t(L["w1"]))) * F.linear(x, t(L["w3"]))), t(L["w2"]))
+    x = ra(F.rms_norm(h, (a.dim,), t(W["norm"]), eps=a.norm_eps))
     return F.linear(x, t(W["output"])).numpy()
 
 
@@ -259,6 +266,25 @@ def test_model_matches_torch_library_composition(kvh):
     np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-10)
     np.testing.assert_allclose(oracle.teacher_forced_logits(a, W, tokens, np.float64), ref,
                                rtol=1e-10, atol=1e-10)
+
+
+@pytest.mark.parametrize("storage", ["bf16", "bf16_kv", "fp16"])
+def test_storage_modes_round_exactly_at_the_stated_points(storage):
+    """The storage modes against the torch composition with the roundings placed by hand at
+    the points each mode names (bf16 / fp16: every stored activation and the cache; bf16_kv:
+    the cache only).  The rounding functions themselves are pinned against torch's bf16 and
+    numpy's float16 conversions below; this pins where they are applied."""
+    a = small_args()
+    W = random_weights(a, seed=36)
+    tokens = np.random.default_rng(37).integers(0, a.vocab_size, size=(2, 11))
+    r = oracle.round_fp16 if storage == "fp16" else oracle.round_bf16
+    ref = torch_model_forward(a, W, tokens, act=None if storage == "bf16_kv" else r, kv=r)
+    got = oracle.Oracle(a, W, 2, dtype=np.float64, storage=storage).forward(tokens, 0)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(oracle.teacher_forced_logits(a, W, tokens, np.float64, storage=storage),
+                               ref, rtol=1e-10, atol=1e-10)
+    # and the rounding is not a no-op: the plain model differs
+    assert np.abs(ref - torch_model_forward(a, W, tokens)).max() > 1e-7
 
 
 def test_identity_blocks_closed_form():
