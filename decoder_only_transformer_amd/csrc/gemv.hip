@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
     constexpr int SEG = U * kWave * VEC;       // K elements per segment (bf16: 4096, fp32: 2048)
     constexpr int XPT = SEG / 4 / kThreads;    // activation float4s per thread per row per segment
     __shared__ float xs[MB][SEG];
-    __shared__ float red[kWavesPerBlock][MB];
+    __shared__ double red[kWavesPerBlock][MB];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -104,34 +104,39 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
     }
 
     for (int m0 = 0; m0 < a.M; m0 += MB) {
-        float rstd[MB];
+        // RMS denominators sqrt(mean(x^2) + eps): squares summed in fp64 (exact), the mean
+        // rounded once to fp32, correctly rounded square root; the operand is x / den * w with
+        // the correctly rounded division.  A reciprocal times x, or a mean off by one bit,
+        // differs from this in the last bit, which a 16-bit rounding of an embedding row
+        // scaled onto exact ties can turn into hundreds of flipped elements.
+        float den[MB];
 #pragma unroll
-        for (int m = 0; m < MB; ++m) rstd[m] = 1.f;
+        for (int m = 0; m < MB; ++m) den[m] = 1.f;
         if (NORM && !one_seg) {
             // rows longer than one segment: statistics in a pass of their own
-            float ss[MB];
+            double ss[MB];
 #pragma unroll
-            for (int m = 0; m < MB; ++m) ss[m] = 0.f;
+            for (int m = 0; m < MB; ++m) ss[m] = 0.0;
             for (int k = tid * 4; k < a.K; k += kThreads * 4) {
 #pragma unroll
                 for (int m = 0; m < MB; ++m) {
                     const int row = min(m0 + m, a.M - 1);
                     const float4 v = *reinterpret_cast<const float4*>(a.x + (size_t)row * a.ldx + k);
-                    ss[m] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+                    ss[m] += sq64(v.x) + sq64(v.y) + sq64(v.z) + sq64(v.w);
                 }
             }
 #pragma unroll
             for (int m = 0; m < MB; ++m) {
-                const float t = wave_sum(ss[m]);
+                const double t = wave_sum(ss[m]);
                 if (lane == 0) red[wid][m] = t;
             }
             lds_barrier();
 #pragma unroll
             for (int m = 0; m < MB; ++m) {
-                float t = 0.f;
+                double t = 0.0;
 #pragma unroll
                 for (int w = 0; w < kWavesPerBlock; ++w) t += red[w][m];
-                rstd[m] = rsqrtf(t / (float)a.K + a.eps);
+                den[m] = sqrtf((float)(t / (double)a.K) + a.eps);
             }
             lds_barrier();
         }
@@ -182,28 +187,31 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
                     nvf[i] = make_float4(Elem<WT>::lo(nv[i].x), Elem<WT>::hi(nv[i].x), Elem<WT>::lo(nv[i].y),
                                          Elem<WT>::hi(nv[i].y));
             }
+            // NORM: the row's denominator (rows past M: infinity, which normalises them to 0);
+            // otherwise a 1 / 0 factor
             float scale[MB];
 #pragma unroll
-            for (int m = 0; m < MB; ++m) scale[m] = (m0 + m < a.M) ? rstd[m] : 0.f;
+            for (int m = 0; m < MB; ++m)
+                scale[m] = (m0 + m < a.M) ? den[m] : (NORM ? __builtin_inff() : 0.f);
             // 4. RMS statistics when the whole row is this segment
             if (NORM && one_seg) {
 #pragma unroll
                 for (int m = 0; m < MB; ++m) {
-                    float ss = 0.f;
+                    double ss = 0.0;
 #pragma unroll
                     for (int i = 0; i < XPT; ++i)
-                        ss += kin[i] * (xv[m][i].x * xv[m][i].x + xv[m][i].y * xv[m][i].y +
-                                        xv[m][i].z * xv[m][i].z + xv[m][i].w * xv[m][i].w);
+                        ss += (double)kin[i] * (sq64(xv[m][i].x) + sq64(xv[m][i].y) + sq64(xv[m][i].z) +
+                                                sq64(xv[m][i].w));
                     ss = wave_sum(ss);
                     if (lane == 0) red[wid][m] = ss;
                 }
                 lds_barrier();
 #pragma unroll
                 for (int m = 0; m < MB; ++m) {
-                    float t = 0.f;
+                    double t = 0.0;
 #pragma unroll
                     for (int w = 0; w < kWavesPerBlock; ++w) t += red[w][m];
-                    scale[m] = (m0 + m < a.M) ? rsqrtf(t / (float)a.K + a.eps) : 0.f;
+                    scale[m] = (m0 + m < a.M) ? sqrtf((float)(t / (double)a.K) + a.eps) : __builtin_inff();
                 }
             }
             // 5. normalise, round to the stored precision, stage in LDS (positions past the
@@ -215,10 +223,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
                 for (int m = 0; m < MB; ++m) {
                     float4 v = xv[m][i];
                     if (NORM) {
-                        v.x = v.x * scale[m] * nvf[i].x;
-                        v.y = v.y * scale[m] * nvf[i].y;
-                        v.z = v.z * scale[m] * nvf[i].z;
-                        v.w = v.w * scale[m] * nvf[i].w;
+                        v.x = v.x / scale[m] * nvf[i].x;
+                        v.y = v.y / scale[m] * nvf[i].y;
+                        v.z = v.z / scale[m] * nvf[i].z;
+                        v.w = v.w / scale[m] * nvf[i].w;
                     } else {
                         v.x *= scale[m];
                         v.y *= scale[m];

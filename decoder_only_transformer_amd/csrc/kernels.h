@@ -61,7 +61,8 @@ struct QkvTarget {
 };
 
 // y[m][n] = sum_k x[m][k] * W[n][k]  (VALU, fp32 activations, weights streamed once per
-// M-chunk).  With norm_w, x is RMS-normalised on the fly: x * rsqrt(mean(x^2)+eps) * norm_w.
+// M-chunk).  With norm_w, x is RMS-normalised on the fly: x / sqrt(mean(x^2)+eps) * norm_w
+// (correctly rounded square root and division).
 struct GemvArgs {
     const float* x; int64_t ldx;
     int M, K, N;           // N = output columns (SWIGLU: hidden units)

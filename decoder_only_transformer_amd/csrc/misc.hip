@@ -24,7 +24,12 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* tokens, int64
     for (int k = threadIdx.x; k < dim; k += blockDim.x) out[k] = Elem<WT>::load(row, k);
 }
 
-// out[r][:] = bf16( h[r][:] * rsqrt(mean(h[r]^2) + eps) * w ), fp32 reduction.
+// out[r][:] = bf16( h[r][:] / sqrt(mean(h[r]^2) + eps) * w ).  The squares are summed in fp64
+// (each is exact there) and the mean rounded once to fp32, so it is the correctly rounded
+// mean in all but ~1e-7 of rows whatever the summation order; the square root and the
+// division are the correctly rounded fp32 ones.  Where a row of bf16 values (an embedding
+// row) times the scale lands on many exact bf16 ties, one bit of the denominator decides
+// hundreds of roundings, so the denominator is made exact rather than approximate.
 // With nsplit > 1, h[r] first takes the K-split partial sums of the residual product that
 // wrote them, part[0][r] + ... + part[nsplit - 1][r] (part is [nsplit][rows][dim], summed in
 // split order), and is stored back.
@@ -33,9 +38,9 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(float* h, int64_t ldh
                                                            const WT* w, float eps, uint16_t* out,
                                                            int64_t ldo, int frag_mt,
                                                            const float* part, int nsplit) {
-    __shared__ float red[4];
+    __shared__ double red[4];
     float* x = h + (size_t)blockIdx.x * ldh;
-    float ss = 0.f;
+    double ss = 0.0;
     for (int k = threadIdx.x * 4; k < dim; k += 256 * 4) {
         float4 v = *reinterpret_cast<const float4*>(x + k);
         if (nsplit > 1) {
@@ -47,18 +52,18 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(float* h, int64_t ldh
             v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
             *reinterpret_cast<float4*>(x + k) = v;
         }
-        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        ss += sq64(v.x) + sq64(v.y) + sq64(v.z) + sq64(v.w);
     }
     ss = wave_sum(ss);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
-    const float r = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)dim + eps);
+    const float den = sqrtf((float)((red[0] + red[1] + red[2] + red[3]) / (double)dim) + eps);
     // row-major [rows][ldo], or fragment-major (4 consecutive k stay adjacent in both)
     for (int k = threadIdx.x * 4; k < dim; k += 256 * 4) {
         const float4 v = *reinterpret_cast<const float4*>(x + k);
         uint2 p;
-        p.x = pack_bf16x2(v.x * r * Elem<WT>::load(w, k), v.y * r * Elem<WT>::load(w, k + 1));
-        p.y = pack_bf16x2(v.z * r * Elem<WT>::load(w, k + 2), v.w * r * Elem<WT>::load(w, k + 3));
+        p.x = pack_bf16x2(v.x / den * Elem<WT>::load(w, k), v.y / den * Elem<WT>::load(w, k + 1));
+        p.y = pack_bf16x2(v.z / den * Elem<WT>::load(w, k + 2), v.w / den * Elem<WT>::load(w, k + 3));
         const size_t o = frag_mt ? frag_index(blockIdx.x, k, frag_mt) : (size_t)blockIdx.x * ldo + k;
         *reinterpret_cast<uint2*>(out + o) = p;
     }
@@ -71,7 +76,7 @@ template <int NV, int NS>
 __global__ __launch_bounds__(256) void rmsnorm_reg_kernel(float* h, int64_t ldh, int dim, const bf16* w,
                                                           float eps, uint16_t* out, int64_t ldo, int frag_mt,
                                                           const float* part) {
-    __shared__ float red[4];
+    __shared__ double red[4];
     float* x = h + (size_t)blockIdx.x * ldh;
     float4 v[NV];
     uint2 wv[NV];
@@ -99,20 +104,20 @@ __global__ __launch_bounds__(256) void rmsnorm_reg_kernel(float* h, int64_t ldh,
             if (k < dim) *reinterpret_cast<float4*>(x + k) = v[i];
         }
     }
-    float ss = 0.f;
+    double ss = 0.0;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) ss += v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+    for (int i = 0; i < NV; ++i) ss += sq64(v[i].x) + sq64(v[i].y) + sq64(v[i].z) + sq64(v[i].w);
     ss = wave_sum(ss);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
-    const float r = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)dim + eps);
+    const float den = sqrtf((float)((red[0] + red[1] + red[2] + red[3]) / (double)dim) + eps);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int k = (threadIdx.x + 256 * i) * 4;
         if (k >= dim) continue;
         uint2 p;
-        p.x = pack_bf16x2(v[i].x * r * bf16lo(wv[i].x), v[i].y * r * bf16hi(wv[i].x));
-        p.y = pack_bf16x2(v[i].z * r * bf16lo(wv[i].y), v[i].w * r * bf16hi(wv[i].y));
+        p.x = pack_bf16x2(v[i].x / den * bf16lo(wv[i].x), v[i].y / den * bf16hi(wv[i].x));
+        p.y = pack_bf16x2(v[i].z / den * bf16lo(wv[i].y), v[i].w / den * bf16hi(wv[i].y));
         const size_t o = frag_mt ? frag_index(blockIdx.x, k, frag_mt) : (size_t)blockIdx.x * ldo + k;
         *reinterpret_cast<uint2*>(out + o) = p;
     }

@@ -122,8 +122,10 @@ def _storage_fns(storage: Optional[str]):
 
 def rms_norm(x: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
     """RMSNorm ([AG] 8.4 RMSNorm; [ST] RMSNorm): x * rsqrt(mean(x^2) + eps) * weight over
-    the last axis.  No mean subtraction, no bias."""
-    ms = np.mean(x * x, axis=-1, keepdims=True)
+    the last axis.  No mean subtraction, no bias.  The mean of squares is taken in float64
+    (every square of a float32 is exact there) and then held in the working precision: in
+    float32 it is the correctly rounded mean, which any other summation order reproduces."""
+    ms = np.mean(np.square(x, dtype=np.float64), axis=-1, keepdims=True).astype(x.dtype)
     return (x / np.sqrt(ms + x.dtype.type(eps))) * weight
 
 

@@ -93,6 +93,22 @@ def test_rmsnorm_matches_torch_library():
     np.testing.assert_allclose(oracle.rms_norm(x, w, 1e-5), ref, rtol=1e-12, atol=1e-14)
 
 
+def test_rmsnorm_fp32_mean_is_the_correctly_rounded_mean():
+    """In float32 the mean of squares is the correctly rounded one (math.fsum of the exact
+    squares), so the result does not depend on the order of the row's elements."""
+    rng = np.random.default_rng(8)
+    eps = 1e-5
+    for n in (4096, 5120, 768):
+        x = (rng.standard_normal((64, n)) * 0.02).astype(np.float32)
+        got = oracle.rms_norm(x, np.float32(1.0), eps)
+        for r in range(x.shape[0]):
+            sq = [float(v) * float(v) for v in x[r]]          # exact in binary64
+            ms = np.float32(math.fsum(sq) / n)
+            np.testing.assert_array_equal(got[r], x[r] / np.sqrt(ms + np.float32(eps)))
+        perm = rng.permutation(n)
+        np.testing.assert_array_equal(oracle.rms_norm(x[:, perm], np.float32(1.0), eps), got[:, perm])
+
+
 def test_rmsnorm_scale_invariance_and_unit_rms():
     rng = np.random.default_rng(2)
     x = rng.standard_normal((4, 64))
