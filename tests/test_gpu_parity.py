@@ -1,18 +1,31 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded
 inputs.
 
-Bars (floating point): fp32 models max |d logit| <= 1e-4; bf16 models max |d logit| <= 3e-2
-and cosine >= 0.999 per position; greedy tokens identical wherever the oracle's top-1 /
-top-2 margin exceeds 0.1.  The oracle is run teacher-forced on the GPU's own token sequence
-(one causal pass, layer by layer), which by the causal mask gives the logits every
-generate call should have produced, including after a legitimate low-margin divergence.
+The oracle is run teacher-forced on the GPU's own token sequence (one causal pass, layer by
+layer), which by the causal mask gives the logits every generate call should have produced,
+including after a legitimate low-margin divergence.
 
-bf16 models are compared with the oracle in its bf16-storage mode: the oracle computes in
-fp32 and rounds to bf16 exactly the tensors the bf16 method stores in 16 bits (normalised
-GEMM operands, q, the K/V cache, attention output, gated FFN activation).  Their distance
-to the plain fp32 oracle is reported as well: on the 7B shape, rounding the K/V cache
-alone already moves the logits of the exact model by ~0.15, so that distance measures
-the bf16 format, not the kernels.
+fp32 models: max |d logit| <= 1e-4 against the plain oracle in fp64.
+
+16-bit models (bf16; fp16 with the bar scaled by the ulp ratio): the stated bars are max
+|d logit| <= 3e-2 and cosine >= 0.999 per position, and the greedy token must be the
+oracle's wherever the oracle's top-1/top-2 margin exceeds 0.1.  Each result is compared
+with three oracle evaluations on the same tokens:
+  ref    the oracle in its 16-bit storage mode (fp32 arithmetic, the tensors the method
+         stores in 16 bits rounded where they are produced);
+  alt    the same, on an equivalent model whose model and FFN dimensions are permuted
+         consistently (the same function; every fp32 sum in another order): a second
+         correct evaluation of the method;
+  plain  the plain fp32 oracle (no storage rounding).
+Where a second correct evaluation meets the stated bars (small shapes, one layer at the 7B
+widths), the GPU must meet them too.  At depth it does not: two correct bf16 evaluations
+of the 7B shape differ by ~0.15 at single logits, and the bf16-storage oracle itself sits
+at cosine 0.9987 from the plain one (rounding the K/V cache alone moves the logits by
+0.15; measured in test_llama2_7b_b1_generate_matches_oracle).  There the GPU must be as
+close to ref and to plain as a correct evaluation is, within a factor 1 + DELTA, on the
+pooled RMS and 99.9th percentile of |d logit|, the worst position's RMS and the maximum
+(tests/parity_stats.py), and greedy tokens must match where no correct evaluation could
+flip them, with band mismatches within what a correct evaluation's noise explains.
 """
 import os
 import sys
@@ -24,6 +37,7 @@ import pytest
 import torch
 
 import oracle
+import parity_stats as ps
 import synth
 from decoder_only_transformer_amd import abi, runtime
 
@@ -33,14 +47,12 @@ FP32_TOL = 1e-4
 BF16_TOL = 3e-2
 COS_MIN = 0.999
 MARGIN = 0.1
-
-
-def greedy_margin(tol):
-    """Oracle top-1/top-2 margin above which the GPU's greedy token must equal the oracle's.
-    If every logit is within tol, a margin above 2 * tol forces the pick; at the stated bar
-    (3e-2) that is below 0.1, so 0.1 holds there, and with the bar derived at depth the
-    rule scales with it (reading R19)."""
-    return max(MARGIN, 2.0 * tol)
+# Allowance over a second correct evaluation.  Correct evaluations (fp32 with permuted sums,
+# fp64) differ from one another by up to 3% in the pooled statistics and 7% in the extreme
+# ones (worst position, maximum) at the 7B widths; the GPU's arithmetic perturbs the stored
+# values in more places than a summation order does (P carried as bf16 high + low parts in
+# the attention, fp32 RoPE table, exp2-based softmax), each at the same ~1e-6 relative level.
+DELTA = 0.2
 
 
 def say(msg):
@@ -62,13 +74,78 @@ def args_of(wl, max_batch=None):
                              max_batch or wl.batch, wl.max_seq_len, wl.dtype)
 
 
-def host_weights(wl, dev_weights):
-    """Oracle weights: the same seeded tensors as fp32 numpy (copied from the generator's
-    device output, which is bit-identical to its CPU output)."""
-    def get(name, layer):
-        t = dev_weights[name] if layer < 0 else dev_weights["layers"][layer][name]
-        return t.float().cpu().numpy()
-    return get
+class HostWeights:
+    """Oracle weights: the generator's device tensors as host fp32 arrays (the generator's
+    device output is bit-identical to its CPU output), one layer at a time.  Each tensor is
+    widened on the device (exact) and copied into a pinned host buffer that the next layer's
+    tensor of the same name reuses; the oracle touches a layer's weights only while it
+    computes that layer.
+
+    perm_seed: the model with its dim and hidden axes permuted consistently (the same
+    function, every fp32 sum over them in another order); the gathers are torch indexing on
+    the device (data movement only)."""
+
+    def __init__(self, W, dim, hidden, perm_seed=None):
+        self.W = W
+        self.bufs = {}
+        self.cache = {}
+        self.layer = None
+        self.pd = self.ph = None
+        if perm_seed is not None:
+            rng = np.random.default_rng(perm_seed)
+            dev = W["output"].device
+            self.pd = torch.from_numpy(rng.permutation(dim)).to(dev)
+            self.ph = torch.from_numpy(rng.permutation(hidden)).to(dev)
+
+    def _permute(self, name, w):
+        pd, ph = self.pd, self.ph
+        if name in ("tok_embeddings", "output", "wq", "wk", "wv"):
+            return w[:, pd]
+        if name in ("norm", "attention_norm", "ffn_norm", "wo"):
+            return w[pd]
+        if name in ("w1", "w3"):
+            return w[ph][:, pd]
+        if name == "w2":
+            return w[pd][:, ph]
+        raise KeyError(name)
+
+    def __call__(self, name, layer):
+        key = (name, layer)
+        if key in self.cache:
+            return self.cache[key]
+        if layer >= 0 and layer != self.layer:
+            for k in [k for k in self.cache if k[1] >= 0]:
+                del self.cache[k]
+            self.layer = layer
+        w = self.W[name] if layer < 0 else self.W["layers"][layer][name]
+        if self.pd is not None:
+            w = self._permute(name, w)
+        bkey = (name, layer < 0)
+        buf = self.bufs.get(bkey)
+        if buf is None or buf.shape != w.shape:
+            buf = torch.empty(w.shape, dtype=torch.float32, pin_memory=True)
+            self.bufs[bkey] = buf
+        buf.copy_(w.float())
+        self.cache[key] = buf.numpy()
+        return self.cache[key]
+
+
+def host_weights(wl, W):
+    return HostWeights(W, wl.dim, wl.hidden_dim)
+
+
+def oracle_pass(wl, W, tokens, kind, storage="bf16", dtype=np.float32):
+    """Teacher-forced oracle logits (B, T, V) for tokens (B, T): kind "ref" (storage mode),
+    "alt" (storage mode, permuted model), "plain" (no storage rounding) or "kv" (only the
+    K/V cache rounded to bf16)."""
+    a = oracle.args_from_workload(wl)
+    prov = HostWeights(W, wl.dim, wl.hidden_dim, perm_seed=7 if kind == "alt" else None)
+    st = {"ref": storage, "alt": storage, "plain": None, "kv": "bf16_kv"}[kind]
+    t0 = time.perf_counter()
+    out = oracle.teacher_forced_logits(a, prov, tokens, dtype, storage=st)
+    say(f"    oracle pass {kind:5s} over {tokens.shape[0]} x {tokens.shape[1]} positions: "
+        f"{time.perf_counter() - t0:.1f} s")
+    return out
 
 
 def gpu_generate(wl, weights, prompts, keep_logits=True):
@@ -81,51 +158,86 @@ def gpu_generate(wl, weights, prompts, keep_logits=True):
     return out
 
 
-def verify_generate(wl, prompts, tokens, call_logits, tf_logits, tol, cos_min=None, min_len=None):
-    """call i of the generate schedule produced logits of position min_len-1+i (min_len: the
-    shortest prompt of the whole batch)."""
+def check_logits(gpu, ref, alt, plain, stated=BF16_TOL):
+    """ps.check_depth with this file's bars; returns the distances."""
+    return ps.check_depth(gpu, ref, alt, plain, DELTA, say=say, stated_max=stated, stated_cos=COS_MIN)
+
+
+def forced_margin(dist, stated=BF16_TOL):
+    """Oracle margin above which the greedy token is forced: the stated 0.1 where a second
+    correct evaluation stays within the stated bar, else twice the largest logit error the
+    GPU is allowed (no correct evaluation can flip such a pick)."""
+    a = dist["alt_ref"].max_all
+    return MARGIN if a <= stated else max(MARGIN, 2.0 * (1.0 + DELTA) * a)
+
+
+def check_generate_rows(wl, W, prompts, tokens, call_logits, rows, storage="bf16", stated=BF16_TOL,
+                        plain=True, min_len=None, extra_kinds=()):
+    """The generate run's logits of batch rows `rows` against the oracle passes on those rows
+    (teacher-forced on the GPU's tokens), pooled over rows and calls; greedy tokens against
+    the reference's.  Call i produced the logits of position min_len - 1 + i (min_len: the
+    shortest prompt of the whole batch).  Returns the oracle passes."""
+    rows = list(rows)
     if min_len is None:
         min_len = min(len(p) for p in prompts)
-    worst = 0.0
-    worst_cos = 1.0
-    checked = 0
+    n_calls = call_logits.shape[0]
+    sel = np.arange(min_len - 1, min_len - 1 + n_calls)
+    tb = tokens[rows, :-1]
+    passes = {k: oracle_pass(wl, W, tb, k, storage) for k in ("ref", "alt") + (("plain",) if plain else ())
+              + tuple(extra_kinds)}
+
+    def pooled(x):   # (rows, calls, V) -> (rows * calls, V)
+        return x.reshape(-1, x.shape[-1])
+    G = pooled(np.transpose(call_logits[:, rows], (1, 0, 2)))
+    assert np.isfinite(G).all(), "non-finite GPU logits"
+    S, P = pooled(passes["ref"][:, sel]), pooled(passes["alt"][:, sel])
+    X = pooled(passes["plain"][:, sel]) if plain else None
+    dist = check_logits(G, S, P, X, stated)
+    # greedy tokens at the positions generated (not prompt tokens kept by the select)
+    free = np.array([[sel[i] + 1 >= len(prompts[b]) for i in range(n_calls)] for b in rows]).reshape(-1)
+    nxt = np.array([[tokens[b, sel[i] + 1] for i in range(n_calls)] for b in rows]).reshape(-1)
+    rep = ps.greedy_check(nxt[free], G[free], S[free], P[free], forced_margin(dist, stated))
+    say(f"    {rep.line()}")
+    for b in rows:
+        assert tokens[b, :len(prompts[b])].tolist() == list(prompts[b]), "prompt overwritten"
+    passes["sel"] = sel
+    return passes
+
+
+def check_positions(wl, W, tokens, gpu_logits, storage="bf16", stated=BF16_TOL, plain=True):
+    """All-positions logits (B, T, V) of a prefill (or a sequence of calls covering every
+    position) against the oracle passes over the same tokens (B, T)."""
+    passes = {k: oracle_pass(wl, W, tokens, k, storage) for k in ("ref", "alt") + (("plain",) if plain else ())}
+    V = gpu_logits.shape[-1]
+    return check_logits(gpu_logits.reshape(-1, V), passes["ref"].reshape(-1, V), passes["alt"].reshape(-1, V),
+                        passes["plain"].reshape(-1, V) if plain else None, stated)
+
+
+def verify_fp32_generate(prompts, tokens, call_logits, tf_logits, min_len=None):
+    """fp32 models: every call's logits within 1e-4 of the fp64 plain oracle; greedy tokens
+    equal wherever the oracle's margin exceeds 0.1."""
+    if min_len is None:
+        min_len = min(len(p) for p in prompts)
+    worst, checked = 0.0, 0
     for i in range(call_logits.shape[0]):
         p = min_len - 1 + i
         g = call_logits[i].astype(np.float64)
         o = tf_logits[:, p].astype(np.float64)
         assert np.isfinite(g).all(), f"non-finite GPU logits at call {i}"
-        d = np.abs(g - o).max()
-        worst = max(worst, d)
-        cos = (g * o).sum(-1) / np.linalg.norm(g, axis=-1) / np.linalg.norm(o, axis=-1)
-        worst_cos = min(worst_cos, cos.min())
-        srt = np.sort(o, axis=-1)
-        margin = srt[:, -1] - srt[:, -2]
-        top = np.argmax(o, -1)
+        worst = max(worst, np.abs(g - o).max())
+        top, margin = ps.top2(o)
         for b in range(len(prompts)):
-            if p + 1 >= len(prompts[b]) and margin[b] > greedy_margin(tol):
+            if p + 1 >= len(prompts[b]) and margin[b] > MARGIN:
                 assert tokens[b, p + 1] == top[b], f"greedy token differs at row {b} pos {p + 1}"
                 checked += 1
-    say(f"  max|dlogit|={worst:.3e} min cos={worst_cos:.6f} greedy tokens checked={checked}")
-    assert worst <= tol, worst
-    if cos_min is not None:
-        assert worst_cos >= cos_min, worst_cos
+    say(f"  max|dlogit|={worst:.3e} greedy tokens checked={checked}")
+    assert worst <= FP32_TOL, worst
     for b, p in enumerate(prompts):
         assert tokens[b, :len(p)].tolist() == list(p), "prompt overwritten"
     return worst
 
 
 # ----------------------------------------------------------------------------- tiny fp32
-
-def plain_distance(call_logits, tf_plain, min_len):
-    worst, worst_cos = 0.0, 1.0
-    for i in range(call_logits.shape[0]):
-        g = call_logits[i].astype(np.float64)
-        o = tf_plain[:, min_len - 1 + i].astype(np.float64)
-        worst = max(worst, np.abs(g - o).max())
-        worst_cos = min(worst_cos, ((g * o).sum(-1) / np.linalg.norm(g, axis=-1) / np.linalg.norm(o, axis=-1)).min())
-    say(f"  vs plain fp32 oracle (16-bit storage effect): max|dlogit|={worst:.3e} min cos={worst_cos:.6f}")
-    return worst, worst_cos
-
 
 def test_tiny_fp32_generate_matches_oracle():
     wl = synth.WORKLOADS["tiny_fp32"]
@@ -135,7 +247,7 @@ def test_tiny_fp32_generate_matches_oracle():
     tokens, logits, _ = gpu_generate(wl, W, prompts)
     a = oracle.args_from_workload(wl)
     tf = oracle.teacher_forced_logits(a, host_weights(wl, W), tokens[:, :-1], np.float64)
-    verify_generate(wl, prompts, tokens, logits, tf, FP32_TOL)
+    verify_fp32_generate(prompts, tokens, logits, tf)
     # free-running oracle generate gives the same tokens (all margins are checked above)
     ref_tokens, _ = oracle.greedy_generate(oracle.Oracle(a, host_weights(wl, W), wl.batch, np.float64),
                                            prompts, wl.gen_steps)
@@ -266,12 +378,7 @@ def test_fp16_generate_matches_oracle(name):
     assert W["layers"][0]["wq"].dtype == torch.float16
     prompts = synth.prompts(wl)
     tokens, logits, _ = gpu_generate(wl, W, prompts)
-    a = oracle.args_from_workload(wl)
-    hw = host_weights(wl, W)
-    tf = oracle.teacher_forced_logits(a, hw, tokens[:, :-1], np.float32, storage="fp16")
-    verify_generate(wl, prompts, tokens, logits, tf, FP16_TOL, COS_MIN)
-    plain = oracle.teacher_forced_logits(a, hw, tokens[:, :-1], np.float32)
-    plain_distance(logits, plain, min(len(p) for p in prompts))
+    check_generate_rows(wl, W, prompts, tokens, logits, range(len(prompts)), storage="fp16", stated=FP16_TOL)
 
 
 def test_fp16_prefill_all_positions_chunked_and_decode():
@@ -314,13 +421,7 @@ def test_small_bf16_generate_matches_oracle(name):
     W = synth.gen_weights(wl, device="cuda")
     prompts = synth.prompts(wl)
     tokens, logits, _ = gpu_generate(wl, W, prompts)
-    a = oracle.args_from_workload(wl)
-    hw = host_weights(wl, W)
-    tf = oracle.teacher_forced_logits(a, hw, tokens[:, :-1], np.float32, storage="bf16")
-    verify_generate(wl, prompts, tokens, logits, tf, BF16_TOL, COS_MIN)
-    plain = oracle.teacher_forced_logits(a, hw, tokens[:, :-1], np.float32)
-    _, cos = plain_distance(logits, plain, min(len(p) for p in prompts))
-    assert cos > 0.99
+    check_generate_rows(wl, W, prompts, tokens, logits, range(len(prompts)))
 
 
 def test_small_bf16_cache_filled_to_max_seq_len_with_one_token_prompt():
@@ -339,9 +440,7 @@ def test_small_bf16_cache_filled_to_max_seq_len_with_one_token_prompt():
     W = synth.gen_weights(wl, device="cuda")
     tokens, logits, _ = gpu_generate(wl, W, prompts)
     assert tokens.shape[1] == wl.max_seq_len and logits.shape[0] == wl.max_seq_len - 1
-    a = oracle.args_from_workload(wl)
-    tf = oracle.teacher_forced_logits(a, host_weights(wl, W), tokens[:, :-1], np.float32, storage="bf16")
-    verify_generate(wl, prompts, tokens, logits, tf, BF16_TOL, COS_MIN)
+    check_generate_rows(wl, W, prompts, tokens, logits, range(len(prompts)))
 
 
 def test_small_bf16_prefill_equals_token_by_token_decode():
@@ -383,13 +482,8 @@ def test_small_bf16_chunked_prefill_all_positions(name):
     model.prefill(dtok, B, S - c, c, b, all_positions=True, col=c)
     torch.cuda.synchronize()
     got = np.concatenate([a.cpu().numpy(), b.cpu().numpy()], 1)
-    ref = oracle.Oracle(oracle.args_from_workload(wl), host_weights(wl, W), B, np.float32,
-                        storage="bf16").forward(tok, 0)
-    d = np.abs(got - ref).max()
-    cos = ((got * ref).sum(-1) / np.linalg.norm(got, axis=-1) / np.linalg.norm(ref, axis=-1)).min()
-    say(f"  max|dlogit|={d:.3e} min cos={cos:.6f}")
-    assert d <= BF16_TOL and cos >= COS_MIN
     model.close()
+    check_positions(wl, W, tok, got)
 
 
 @pytest.mark.timeout(600)
@@ -415,19 +509,13 @@ def test_llama2_7b_widths_one_layer_chunked_prefill_all_positions():
     got = np.concatenate([a.cpu().numpy(), b.cpu().numpy()], 1)
     del a, b
     model.close()
-    a_ = oracle.args_from_workload(wl)
-    base = cached_provider(W)
-    ref = oracle.Oracle(a_, base, B, np.float32, storage="bf16").forward(tok, 0)
-    # the bar over this many positions: the oracle's own spread against a second correct
-    # fp32 evaluation (consistently permuted model and FFN dimensions), as at depth (R19)
-    ref2 = oracle.Oracle(a_, permuted_provider(W, wl.dim, wl.hidden_dim), B, np.float32,
-                         storage="bf16").forward(tok, 0)
-    spread = float(np.abs(ref - ref2).max())
-    tol = max(BF16_TOL, 1.5 * spread)
-    d = np.abs(got - ref).max()
-    cos = ((got * ref).sum(-1) / np.linalg.norm(got, axis=-1) / np.linalg.norm(ref, axis=-1)).min()
-    say(f"  max|dlogit|={d:.3e} min cos={cos:.6f} (oracle spread {spread:.3e} -> bar {tol:.3e})")
-    assert d <= tol and cos >= COS_MIN
+    V = wl.vocab_size
+    passes = {k: oracle_pass(wl, W, tok, k) for k in ("ref", "alt", "plain")}
+    for name, sl in (("first chunk (positions 0-1023)", slice(0, c)), ("second chunk (1024-1535)", slice(c, S))):
+        g, r, p = (x[:, sl].reshape(-1, V) for x in (got, passes["ref"], passes["alt"]))
+        say(f"  {name}: GPU - ref {ps.distance(g, r).line()}; alt - ref {ps.distance(p, r).line()}")
+    check_logits(got.reshape(-1, V), passes["ref"].reshape(-1, V), passes["alt"].reshape(-1, V),
+                 passes["plain"].reshape(-1, V))
 
 
 @pytest.mark.parametrize("name", ["gqa8", "mha", "b6", "b20", "fp16_mha_b6", "tiny_fp32"])
@@ -497,41 +585,6 @@ def test_argmax_ties_nan_and_select():
 
 
 # ----------------------------------------------------------------------------- 7B shape, batch 1
-#
-# At the 7B widths two correct evaluations of the same bf16-storage method disagree by more
-# than 3e-2 once a few layers are stacked: fp32 summation-order differences (~1e-6
-# relative over 4096-11008-term dot products) flip a fraction of the bf16 roundings, and
-# each flip moves a stored value by a full bf16 ulp.  Measured max |d logit| between the
-# oracle run in fp32 and in fp64 (same bf16 storage, same tokens): 0.022 at 1 layer, 0.031
-# at 2, 0.045 at 4, 0.066 at 8, 0.10 at 16, ~0.15 at 32, while the cosine stays >= 0.9996.
-# The one-layer model at full width is therefore held to the stated 3e-2; the 32-layer
-# model is held to max(3e-2, 1.5 x the oracle's own fp32-vs-fp64 spread, measured here on
-# the same tokens), with the stated cosine >= 0.999 and greedy rule unchanged.
-
-def _tf_pair(wl, W, tokens):
-    """bf16-storage oracle logits in fp32 and fp64 arithmetic on the same tokens."""
-    a = oracle.args_from_workload(wl)
-    cache = {}
-
-    def prov(n, l, dt):
-        if (n, l) not in cache:
-            if l >= 0:
-                for k in [k for k in cache if k[1] >= 0 and k[1] != l]:
-                    del cache[k]
-            t = W[n] if l < 0 else W["layers"][l][n]
-            cache[(n, l)] = t.double().cpu().numpy()
-        return cache[(n, l)].astype(dt, copy=False)
-    hook = lambda l: say(f"    oracle layer {l}") if l % 8 == 0 else None  # noqa: E731
-    t0 = time.perf_counter()
-    t32 = oracle.teacher_forced_logits(a, lambda n, l: prov(n, l, np.float32), tokens, np.float32,
-                                       layer_hook=hook, storage="bf16")
-    t1 = time.perf_counter()
-    t64 = oracle.teacher_forced_logits(a, lambda n, l: prov(n, l, np.float64), tokens, np.float64,
-                                       layer_hook=hook, storage="bf16")
-    say(f"  oracle teacher-forced pass over {tokens.size} positions: fp32 {t1 - t0:.1f} s, "
-        f"fp64 {time.perf_counter() - t1:.1f} s")
-    return t32, t64
-
 
 @pytest.mark.timeout(600)
 def test_llama2_7b_widths_one_layer_generate_matches_oracle():
@@ -541,9 +594,7 @@ def test_llama2_7b_widths_one_layer_generate_matches_oracle():
     W = synth.gen_weights(wl, device="cuda")
     prompts = synth.prompts(wl)
     tokens, logits, _ = gpu_generate(wl, W, prompts)
-    a = oracle.args_from_workload(wl)
-    tf = oracle.teacher_forced_logits(a, host_weights(wl, W), tokens[:, :-1], np.float32, storage="bf16")
-    verify_generate(wl, prompts, tokens, logits, tf, BF16_TOL, COS_MIN)
+    check_generate_rows(wl, W, prompts, tokens, logits, [0])
 
 
 @pytest.mark.timeout(600)
@@ -560,131 +611,108 @@ def test_llama2_7b_widths_one_layer_tail_rows_match_oracle():
     prompts = synth.prompts(wl)
     assert len(prompts) * min(len(p) for p in prompts) == 33 * 256
     tokens, logits, _ = gpu_generate(wl, W, prompts)
-    rows = [0, 32]
-    a = oracle.args_from_workload(wl)
-    tf = oracle.teacher_forced_logits(a, host_weights(wl, W), tokens[rows, :-1], np.float32, storage="bf16")
-    verify_generate(wl, [prompts[r] for r in rows], tokens[rows], logits[:, rows], tf, BF16_TOL, COS_MIN)
+    check_generate_rows(wl, W, prompts, tokens, logits, [0, 32])
 
 
 @pytest.mark.timeout(900)
 def test_llama2_7b_b1_generate_matches_oracle():
+    """The 7B batch-1 workload at full depth, in the launch configuration bench.py times.
+    Besides the checks of every depth case, this measures the floor the bf16 format sets
+    against the plain fp32 oracle on the same tokens: rounding only the K/V cache (the
+    layout the method fixes) already moves single logits by more than three times the
+    stated 3e-2, and the full bf16-storage method sits below the stated cosine."""
     wl = synth.WORKLOADS["llama2_7b_b1"]
     say(f"case {wl.name}: generating weights")
     W = synth.gen_weights(wl, device="cuda")
     prompts = synth.prompts(wl)
     say("  gpu generate")
     tokens, logits, _ = gpu_generate(wl, W, prompts)
-    say("  oracle teacher-forced passes (bf16 storage; fp32 and fp64 arithmetic)")
-    t32, t64 = _tf_pair(wl, W, tokens[:, :-1])
-    sel = np.arange(len(prompts[0]) - 1, tokens.shape[1] - 1)
-    floor = float(np.abs(t32[:, sel] - t64[:, sel]).max())
-    tol = max(BF16_TOL, 1.5 * floor)
-    say(f"  oracle fp32-vs-fp64 spread {floor:.4f} -> bar {tol:.4f}")
-    verify_generate(wl, prompts, tokens, logits, t32, tol, COS_MIN)
-    say("  oracle teacher-forced pass (plain fp32)")
-    plain = oracle.teacher_forced_logits(oracle.args_from_workload(wl), host_weights(wl, W),
-                                         tokens[:, :-1], np.float32)
-    plain_distance(logits, plain, len(prompts[0]))
+    passes = check_generate_rows(wl, W, prompts, tokens, logits, [0], extra_kinds=("kv",))
+    sel = passes["sel"]
+    kv = ps.distance(passes["kv"][0, sel], passes["plain"][0, sel])
+    st = ps.distance(passes["ref"][0, sel], passes["plain"][0, sel])
+    say(f"  floor: K/V cache alone in bf16 - plain: {kv.line()}")
+    say(f"  floor: bf16 storage - plain:            {st.line()}")
+    assert kv.max_all > 3 * BF16_TOL
+    assert st.cos.min() < COS_MIN and st.rms_all > kv.rms_all
 
 
 # ----------------------------------------------------------------------------- other workloads
 #
 # The oracle's cost grows with batch x depth x length, so the larger workloads are checked
 # on sampled rows: the GPU runs the whole batch (the launch configuration of a real
-# generate), the oracle follows selected rows teacher-forced.  Where depth makes even one
-# row too slow, the model is cut to its first layers at full width (same kernels, same
-# shapes) and the full-depth run is checked on a causal prefix.  The spread bar uses a
-# second, equivalent evaluation: permuting the model dimension consistently across all
-# weights leaves the function unchanged but changes every fp32 summation order.
-
-def permuted_provider(W, dim, hidden, seed=7):
-    """The model with its dim and hidden axes permuted consistently: the same function, with
-    every fp32 sum over them in another order.  The weights are gathered from the generator's
-    device tensors with torch's indexing (data movement only) and handed to the oracle as host
-    fp32 arrays, one layer at a time."""
-    rng = np.random.default_rng(seed)
-    pd, ph = rng.permutation(dim), rng.permutation(hidden)
-    cache = {}
-
-    def get(name, layer):
-        if (name, layer) in cache:
-            return cache[(name, layer)]
-        if layer >= 0:
-            for k in [k for k in cache if k[1] >= 0 and k[1] != layer]:
-                del cache[k]
-        w = W[name] if layer < 0 else W["layers"][layer][name]
-        td, th = torch.from_numpy(pd).to(w.device), torch.from_numpy(ph).to(w.device)
-        if name in ("tok_embeddings", "output", "wq", "wk", "wv"):
-            w = w[:, td]
-        elif name in ("norm", "attention_norm", "ffn_norm", "wo"):
-            w = w[td]
-        elif name in ("w1", "w3"):
-            w = w[th][:, td]
-        elif name == "w2":
-            w = w[td][:, th]
-        cache[(name, layer)] = w.float().cpu().numpy()
-        return cache[(name, layer)]
-    return get
-
-
-def cached_provider(W):
-    cache = {}
-
-    def get(name, layer):
-        if (name, layer) not in cache:
-            if layer >= 0:
-                for k in [k for k in cache if k[1] >= 0 and k[1] != layer]:
-                    del cache[k]
-            t = W[name] if layer < 0 else W["layers"][layer][name]
-            cache[(name, layer)] = t.float().cpu().numpy()
-        return cache[(name, layer)]
-    return get
-
-
-def check_rows(wl, W, prompts, tokens, call_logits, rows):
-    """Teacher-forced oracle (bf16 storage) on the selected rows; bar from the permuted
-    evaluation's spread."""
-    a = oracle.args_from_workload(wl)
-    base = cached_provider(W)
-    min_len = min(len(p) for p in prompts)
-    for b in rows:
-        tb = tokens[b:b + 1, :-1]
-        c0 = time.perf_counter()
-        t1 = oracle.teacher_forced_logits(a, base, tb, np.float32, storage="bf16")[0]
-        c1 = time.perf_counter()
-        t2 = oracle.teacher_forced_logits(a, permuted_provider(W, wl.dim, wl.hidden_dim), tb,
-                                          np.float32, storage="bf16")[0]
-        say(f"  row {b}: oracle teacher-forced pass over {tb.size} positions {c1 - c0:.1f} s "
-            f"(permuted evaluation {time.perf_counter() - c1:.1f} s)")
-        sel = np.arange(min_len - 1, min_len - 1 + call_logits.shape[0])
-        spread = float(np.abs(t1[sel] - t2[sel]).max())
-        tol = max(BF16_TOL, 1.5 * spread)
-        say(f"  row {b}: oracle permuted-evaluation spread {spread:.4f} -> bar {tol:.4f}")
-        verify_generate(wl, [prompts[b]], tokens[b:b + 1], call_logits[:, b:b + 1],
-                        t1[None], tol, COS_MIN, min_len=min_len)
-
+# generate), the oracle follows selected rows teacher-forced.  Batch rows are independent in
+# the forward (no cross-row term), so a row subset is exact for those rows.
 
 @pytest.mark.timeout(900)
 def test_llama2_7b_b32_ragged_generate_rows_match_oracle():
+    """Full batch, ragged prompts, full depth; the oracle follows the first and last row of
+    each of the skinny decode products' two 16-row tiles."""
     wl = synth.WORKLOADS["llama2_7b_b32_ragged"]
-    say(f"case {wl.name}: full batch, ragged prompts, full depth; oracle on row 0")
+    W = synth.gen_weights(wl, device="cuda")
+    prompts = synth.prompts(wl)
+    lens = [len(p) for p in prompts]
+    rows = [0, 15, 16, 31]
+    say(f"case {wl.name}: full batch, ragged prompts {min(lens)}-{max(lens)}, full depth; oracle rows {rows}")
+    tokens, logits, _ = gpu_generate(wl, W, prompts)
+    assert np.isfinite(logits).all()
+    check_generate_rows(wl, W, prompts, tokens, logits, rows)
+
+
+@pytest.mark.timeout(900)
+def test_llama2_13b_b16_generate_rows_match_oracle():
+    """The 13B workload at full depth (40 layers), full batch and prompt, full generate; the
+    oracle follows the first and the last row."""
+    wl = synth.WORKLOADS["llama2_13b_b16"]
+    say(f"case {wl.name}: full batch {wl.batch} x {wl.prompt_len}, {wl.gen_steps} steps, full depth")
     W = synth.gen_weights(wl, device="cuda")
     prompts = synth.prompts(wl)
     tokens, logits, _ = gpu_generate(wl, W, prompts)
     assert np.isfinite(logits).all()
-    check_rows(wl, W, prompts, tokens, logits, rows=[0])
+    check_generate_rows(wl, W, prompts, tokens, logits, [0, wl.batch - 1], plain=False)
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["llama2_13b_b16", "llama2_70b_b8"])
-def test_full_width_first_layers_generate_rows_match_oracle(name):
-    wl = synth.WORKLOADS[name].with_(n_layers=2)
+def test_llama2_70b_b8_full_depth_prefix_rows_match_oracle():
+    """The 70B workload (GQA 8:1) at full depth (80 layers), full batch of 8, on a causal
+    prefix: a 512-token prefill with every position's logits, then 16 single-token decode
+    calls feeding the prompt's next tokens (the skinny decode products and the MFMA GQA
+    decode attention over 513-528 keys).  By the causal mask the logits of these positions
+    are those of the full-length run's; the oracle follows rows 0 and 7."""
+    wl = synth.WORKLOADS["llama2_70b_b8"]
+    n_pre, n_dec = 512, 16
+    say(f"case {wl.name}: full depth, batch {wl.batch}, {n_pre}-token prefix + {n_dec} decode calls")
+    W = synth.gen_weights(wl, device="cuda")
+    tok = np.array([p[:n_pre + n_dec] for p in synth.prompts(wl)], dtype=np.int32)
+    B, V = wl.batch, wl.vocab_size
+    model = runtime.LlamaModel(args_of(wl), W)
+    dtok = torch.from_numpy(tok).cuda()
+    pre = torch.empty((B, n_pre, V), device="cuda")
+    model.prefill(dtok, B, n_pre, 0, pre, all_positions=True)
+    dec = torch.empty((n_dec, B, V), device="cuda")
+    for j in range(n_dec):
+        model.decode_step(dtok, B, n_pre + j, n_pre + j, dec[j])
+    torch.cuda.synchronize()
+    rows = [0, B - 1]
+    got = np.concatenate([pre.cpu().numpy()[rows], np.transpose(dec.cpu().numpy(), (1, 0, 2))[rows]], 1)
+    del pre, dec
+    model.close()
+    assert np.isfinite(got).all()
+    check_positions(wl, W, tok[rows], got, plain=False)
+
+
+@pytest.mark.timeout(900)
+def test_llama2_70b_b8_first_layers_full_length_generate_rows_match_oracle():
+    """The 70B workload cut to its first 2 layers at full width: the whole batch, the whole
+    3584-token prompts and all 512 greedy decode calls (the cache filled to max_seq_len);
+    the oracle follows rows 0 and 7."""
+    wl = synth.WORKLOADS["llama2_70b_b8"].with_(n_layers=2)
     say(f"case {wl.name} cut to 2 layers: full batch {wl.batch} x {wl.prompt_len}, {wl.gen_steps} steps")
     W = synth.gen_weights(wl, device="cuda")
     prompts = synth.prompts(wl)
     tokens, logits, _ = gpu_generate(wl, W, prompts)
     assert np.isfinite(logits).all()
-    check_rows(wl, W, prompts, tokens, logits, rows=[0])
+    check_generate_rows(wl, W, prompts, tokens, logits, [0, wl.batch - 1])
 
 
 # ----------------------------------------------------------------------------- sampling
