@@ -25,7 +25,7 @@ DTYPES = {"bf16": LLAMA_BF16, "fp32": LLAMA_FP32, "fp16": LLAMA_FP16}
 
 # Every symbol include/llama_mi355x.h declares.
 EXPORTED = ("llama_check_args", "llama_workspace_bytes", "llama_init", "llama_prefill",
-            "llama_decode_step", "llama_argmax", "llama_sample_top_p", "llama_select_next", "llama_destroy",
+            "llama_decode_step", "llama_decode_step_noalloc", "llama_argmax", "llama_sample_top_p", "llama_select_next", "llama_destroy",
             "llama_status_str", "llama_profile_select", "llama_profile_read")
 
 # Kernel classes for llama_profile_select (llama_kernel_class in the header).
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.llama_prefill.restype = ctypes.c_int
         L.llama_decode_step.argtypes = [P, P, I64, I32, I32, P, P]
         L.llama_decode_step.restype = ctypes.c_int
+        L.llama_decode_step_noalloc.argtypes = [P, P, I64, I32, I32, P, P]
+        L.llama_decode_step_noalloc.restype = ctypes.c_int
         L.llama_argmax.argtypes = [P, I32, I32, I64, P, P]
         L.llama_argmax.restype = ctypes.c_int
         L.llama_sample_top_p.argtypes = [P, I32, I32, I64, ctypes.c_float, ctypes.c_float, P, P, P, P]
@@ -119,6 +121,11 @@ def llama_prefill(ctx: int, d_tokens: int, ld_tokens: int, bsz: int, seqlen: int
 def llama_decode_step(ctx: int, d_tokens: int, ld_tokens: int, bsz: int, start_pos: int,
                       d_logits: int, stream: int) -> int:
     return lib().llama_decode_step(ctx, d_tokens, ld_tokens, bsz, start_pos, d_logits, stream)
+
+
+def llama_decode_step_noalloc(ctx: int, d_tokens: int, ld_tokens: int, bsz: int, start_pos: int,
+                              d_logits: int, stream: int) -> int:
+    return lib().llama_decode_step_noalloc(ctx, d_tokens, ld_tokens, bsz, start_pos, d_logits, stream)
 
 
 def llama_argmax(d_logits: int, bsz: int, vocab: int, row_stride: int, d_out: int,

@@ -17,6 +17,7 @@
 #include <cstring>
 #include <cstdlib>
 #include <map>
+#include <mutex>
 #include <new>
 #include <utility>
 #include <vector>
@@ -26,7 +27,17 @@
 
 using namespace llk;
 
+// Scratch of the allocation-free decode step (llama_decode_step_noalloc): one array per GPU,
+// held until the process ends.  In host code this name is not a device address; the address
+// comes from hipGetSymbolAddress, taken once per device in llama_init (g_noalloc below).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+void* g_noalloc[kMaxDevices];   // device address of `scratch` on each device, once taken
 
 constexpr int kMaxSplit = 32;
 constexpr int kMaxSplitK = 8;      // K splits of a residual GEMM at small prefill sizes
@@ -45,6 +56,16 @@ struct Layout {
 };
 
 int head_dim_of(const llama_args& a) { return a.dim / a.n_heads; }
+
+// Device addresses of the per-call scratch of a forward call (everything but the KV cache and
+// the RoPE table): carved from the ctx's workspace, or, for the allocation-free decode step,
+// from the library's static device array.
+struct Bufs {
+    float *h32, *q32, *o32, *g32, *part, *splitk;
+    void *act16, *g16;
+    StepState* step;
+    size_t splitk_floats;
+};
 
 llama_status check_args(const llama_args* a) {
     if (!a) return LLAMA_ERR_INVALID_ARG;
@@ -158,6 +179,9 @@ struct llama_ctx {
     int prof_class = 0;
     Timer timer;
 
+    Bufs buf;       // scratch of the call in progress (see Bufs)
+    void* noalloc_scratch = nullptr;   // this device's static scratch array (allocation-free decode)
+
     template <typename T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
     size_t esz() const { return wtype == kStoreF32 ? 4 : 2; }
     void* kcache(int l) const { return ws + L.k_cache + (size_t)l * L.kv_layer_elems * esz(); }
@@ -208,7 +232,7 @@ namespace {
 QkvTarget qkv_target(const llama_ctx* c, int l, int start_pos, int seqlen, const StepState* st = nullptr) {
     QkvTarget t{};
     t.st = st;
-    t.q = c->at<float>(c->L.q32);
+    t.q = c->buf.q32;
     t.cache_k = c->kcache(l);
     t.cache_v = c->vcache(l);
     t.rope = c->at<const float2>(c->L.rope);
@@ -241,13 +265,13 @@ llama_status run_attention(const llama_ctx* c, int l, int rows, int seqlen, int 
                            void* out, bool out_bf16, bool allow_split, hipStream_t s,
                            const StepState* st = nullptr, int graph_splits = 0, int out_frag_mt = 0) {
     AttnArgs at{};
-    at.q = c->at<const float>(c->L.q32);
+    at.q = c->buf.q32;
     at.cache_k = c->kcache(l);
     at.cache_v = c->vcache(l);
     at.out = out;
     at.out_bf16 = out_bf16 ? 1 : 0;
     at.out_frag_mt = out_frag_mt;
-    at.part = c->at<float>(c->L.part);
+    at.part = c->buf.part;
     at.rows = rows;
     at.n_heads = c->a.n_heads;
     at.n_kv_heads = c->a.n_kv_heads;
@@ -282,9 +306,9 @@ llama_status block_gemv(const llama_ctx* c, int l, int M, int seqlen, int start_
                         int graph_splits = 0) {
     const llama_layer_weights& W = c->layers[l];
     const int D = c->a.dim, F = c->a.hidden_dim;
-    float* h = c->at<float>(c->L.h32);
-    float* o32 = c->at<float>(c->L.o32);
-    float* g32 = c->at<float>(c->L.g32);
+    float* h = c->buf.h32;
+    float* o32 = c->buf.o32;
+    float* g32 = c->buf.g32;
     const int wb = c->wtype;
 
     GemvArgs g{};
@@ -333,6 +357,36 @@ int residual_splits(const llama_ctx* c, int T, int K) {
 int wo_splits(const llama_ctx* c, int M) { return skinny_resid_splits(M, c->a.dim, c->nq); }
 int w2_splits(const llama_ctx* c, int M) { return skinny_resid_splits(M, c->a.dim, c->a.hidden_dim); }
 
+// Scratch of one decode step of bsz <= kSkinnyMaxRows rows whose longest row attends over ctx
+// keys, carved from `base` in the order of layout_of: the residual rows, q, the vector path's
+// fp32 operands, the MFMA path's bf16 operands (fragment-major, 32 rows with padding), the
+// attention split partials at the split count this step takes, and the skinny residual
+// products' K-split partials.  Returns the bytes needed; fills *out when base is not null.
+size_t decode_scratch(const llama_ctx* c, int bsz, int ctx, char* base, Bufs* out) {
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    const size_t D = c->a.dim, F = c->a.hidden_dim, nq = c->nq, B = bsz;
+    const size_t h32 = take(B * D * 4), q32 = take(B * nq * 4), o32 = take(B * nq * 4), g32 = take(B * F * 4);
+    const size_t rows16 = kSkinnyMaxRows;
+    const size_t act16 = c->bf16 ? take(rows16 * std::max(D, nq) * 2) : off;
+    const size_t g16 = c->bf16 ? take(rows16 * F * 2) : off;
+    const size_t part = take(B * (size_t)c->a.n_heads * decode_splits(c, bsz, ctx) * (c->hd + 2) * 4);
+    const bool skinny = c->bf16 && bsz > kSkinnyRows;
+    const size_t splitk_floats = skinny ? (size_t)std::max(wo_splits(c, bsz), w2_splits(c, bsz)) * B * D : 0;
+    const size_t splitk = take(splitk_floats * 4);
+    if (base && out) {
+        *out = Bufs{reinterpret_cast<float*>(base + h32), reinterpret_cast<float*>(base + q32),
+                    reinterpret_cast<float*>(base + o32), reinterpret_cast<float*>(base + g32),
+                    reinterpret_cast<float*>(base + part), reinterpret_cast<float*>(base + splitk),
+                    base + act16, base + g16, nullptr, splitk_floats};
+    }
+    return off;
+}
+
 // One decode block for a bf16 model at batch > kSkinnyRows: projections on the skinny MFMA
 // kernel, whose activation operands (RMSNorm output, attention output, SiLU gate) are written
 // bf16 in fragment-major order for MT = ceil(M / 16) row tiles.  The attention norm takes in
@@ -342,12 +396,12 @@ llama_status block_skinny(const llama_ctx* c, int l, int M, int start_pos, hipSt
     const llama_layer_weights& W = c->layers[l];
     const int D = c->a.dim, F = c->a.hidden_dim;
     const int mt = (M + 15) / 16;
-    float* h = c->at<float>(c->L.h32);
-    void* act = c->at<void>(c->L.act16);
-    void* g16 = c->at<void>(c->L.g16);
-    float* part = c->at<float>(c->L.splitk);
+    float* h = c->buf.h32;
+    void* act = c->buf.act16;
+    void* g16 = c->buf.g16;
+    float* part = c->buf.splitk;
     const int s_wo = wo_splits(c, M), s_w2 = w2_splits(c, M);
-    if ((size_t)std::max(s_wo, s_w2) * M * D > c->L.splitk_floats) return LLAMA_ERR_WORKSPACE;
+    if ((size_t)std::max(s_wo, s_w2) * M * D > c->buf.splitk_floats) return LLAMA_ERR_WORKSPACE;
 
     LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, M, D, W.attention_norm, c->a.norm_eps, act, 0, mt, s,
                                                        part, l > 0 ? s_w2 : 0));
@@ -384,16 +438,16 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
                         bool decode = false) {
     const llama_layer_weights& W = c->layers[l];
     const int D = c->a.dim, F = c->a.hidden_dim;
-    float* h = c->at<float>(c->L.h32);
-    void* act = c->at<void>(c->L.act16);
-    void* g16 = c->at<void>(c->L.g16);
+    float* h = c->buf.h32;
+    void* act = c->buf.act16;
+    void* g16 = c->buf.g16;
 
     LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.attention_norm, c->a.norm_eps, act, D, 0, s));
     GemmArgs g{};
     g.a = act; g.lda = D; g.M = T; g.K = D; g.N = c->nq + 2 * c->nk;
     g.w0 = W.wq; g.w1 = W.wk; g.w2 = W.wv;
     g.qkv = qkv_target(c, l, start_pos, seqlen);
-    g.part = c->at<float>(c->L.splitk); g.part_cap = c->L.splitk_floats;
+    g.part = c->buf.splitk; g.part_cap = c->buf.splitk_floats;
     LAUNCH(c, LLAMA_KC_GEMM_QKV, s, launch_gemm(EPI_QKV, g, s));
 
     if (decode) {
@@ -402,7 +456,7 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
         if (st != LLAMA_OK) return st;
     } else if (c->hd == 64 || c->hd == 128) {
         FlashArgs fa{};
-        fa.q = c->at<const float>(c->L.q32);
+        fa.q = c->buf.q32;
         fa.cache_k = c->kcache(l);
         fa.cache_v = c->vcache(l);
         fa.out = act;
@@ -423,20 +477,20 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
     g = GemmArgs{};
     g.a = act; g.lda = c->nq; g.M = T; g.K = c->nq; g.N = D;
     g.w0 = W.wo; g.resid = h; g.ldr = D;
-    g.splits = residual_splits(c, T, c->nq); g.part = c->at<float>(c->L.splitk); g.part_cap = c->L.splitk_floats;
+    g.splits = residual_splits(c, T, c->nq); g.part = c->buf.splitk; g.part_cap = c->buf.splitk_floats;
     LAUNCH(c, LLAMA_KC_GEMM_WO, s, launch_gemm(EPI_RESID, g, s));
 
     LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.ffn_norm, c->a.norm_eps, act, D, 0, s));
     g = GemmArgs{};
     g.a = act; g.lda = D; g.M = T; g.K = D; g.N = F;
     g.w0 = W.w1; g.w1 = W.w3; g.out16 = g16; g.ldo16 = F;
-    g.part = c->at<float>(c->L.splitk); g.part_cap = c->L.splitk_floats;
+    g.part = c->buf.splitk; g.part_cap = c->buf.splitk_floats;
     LAUNCH(c, LLAMA_KC_GEMM_W13, s, launch_gemm(EPI_SWIGLU, g, s));
 
     g = GemmArgs{};
     g.a = g16; g.lda = F; g.M = T; g.K = F; g.N = D;
     g.w0 = W.w2; g.resid = h; g.ldr = D;
-    g.splits = residual_splits(c, T, F); g.part = c->at<float>(c->L.splitk); g.part_cap = c->L.splitk_floats;
+    g.splits = residual_splits(c, T, F); g.part = c->buf.splitk; g.part_cap = c->buf.splitk_floats;
     LAUNCH(c, LLAMA_KC_GEMM_W2, s, launch_gemm(EPI_RESID, g, s));
     return LLAMA_OK;
 }
@@ -495,6 +549,9 @@ llama_status llama_init(const llama_args* a, const llama_weights* w, void* d_wor
     c->nq = a->n_heads * c->hd;
     c->nk = a->n_kv_heads * c->hd;
     c->bf16 = a->dtype == LLAMA_BF16;
+    c->buf = Bufs{c->at<float>(L.h32), c->at<float>(L.q32), c->at<float>(L.o32), c->at<float>(L.g32),
+                  c->at<float>(L.part), c->at<float>(L.splitk), c->at<void>(L.act16), c->at<void>(L.g16),
+                  c->at<StepState>(L.step), L.splitk_floats};
     c->wtype = a->dtype == LLAMA_BF16 ? kStoreBf16 : (a->dtype == LLAMA_FP16 ? kStoreF16 : kStoreF32);
     {
         // Graph replay of decode steps is opt-in: measured on this stack, replaying the
@@ -519,6 +576,19 @@ llama_status llama_init(const llama_args* a, const llama_weights* w, void* d_wor
         delete c;
         return LLAMA_ERR_HIP;
     }
+    // this device's copy of the static scratch of the allocation-free decode step
+    int dev = -1;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+        std::lock_guard<std::mutex> lock(g_noalloc_mu);
+        if (!g_noalloc[dev]) {
+            void* p = nullptr;
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess)
+                g_noalloc[dev] = p;
+            else
+                (void)hipGetLastError();   // leave no error for the next call to report
+        }
+        c->noalloc_scratch = g_noalloc[dev];
+    }
     *out = c;
     return LLAMA_OK;
 }
@@ -533,7 +603,7 @@ llama_status llama_prefill(llama_ctx* c, const int32_t* d_tokens, int64_t ld_tok
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int D = c->a.dim;
     const int T = bsz * seqlen;
-    float* h = c->at<float>(c->L.h32);
+    float* h = c->buf.h32;
     HIP_TRY(launch_embed(d_tokens, ld_tokens, bsz, seqlen, c->w.tok_embeddings, c->wtype,
                          c->a.vocab_size, D, h, nullptr, s));
     for (int l = 0; l < c->a.n_layers; ++l) {
@@ -543,7 +613,7 @@ llama_status llama_prefill(llama_ctx* c, const int32_t* d_tokens, int64_t ld_tok
     }
     if (!all_positions) return final_logits(c, h + (size_t)(seqlen - 1) * D, (int64_t)seqlen * D, bsz, d_logits, s);
     if (!c->bf16) return final_logits(c, h, D, T, d_logits, s);
-    void* act = c->at<void>(c->L.act16);
+    void* act = c->buf.act16;
     HIP_TRY(launch_rmsnorm_bf16(h, D, T, D, c->w.norm, c->a.norm_eps, act, D, 0, s));
     GemmArgs g{};
     g.a = act; g.lda = D; g.M = T; g.K = D; g.N = c->a.vocab_size;
@@ -558,7 +628,7 @@ static llama_status decode_plan(llama_ctx* c, const int32_t* d_tokens, int64_t l
                                 int32_t start_pos, float* d_logits, hipStream_t s,
                                 const StepState* st, int graph_splits) {
     const int D = c->a.dim;
-    float* h = c->at<float>(c->L.h32);
+    float* h = c->buf.h32;
     HIP_TRY(launch_embed(d_tokens, ld_tokens, bsz, 1, c->w.tok_embeddings, c->wtype,
                          c->a.vocab_size, D, h, st, s));
     if (c->bf16 && bsz > kSkinnyMaxRows) {
@@ -578,10 +648,10 @@ static llama_status decode_plan(llama_ctx* c, const int32_t* d_tokens, int64_t l
         if (r != LLAMA_OK) return r;
     }
     if (!skinny) return final_logits(c, h, D, bsz, d_logits, s, st);
-    void* act = c->at<void>(c->L.act16);
+    void* act = c->buf.act16;
     // the final norm takes in the last block's w2 partials
     LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, bsz, D, c->w.norm, c->a.norm_eps, act, 0, (bsz + 15) / 16, s,
-                                                       c->at<float>(c->L.splitk), w2_splits(c, bsz)));
+                                                       c->buf.splitk, w2_splits(c, bsz)));
     SkinnyArgs k{};
     k.x = act; k.M = bsz; k.K = D; k.N = c->a.vocab_size;
     k.w0 = c->w.output; k.out = d_logits; k.ldo = c->a.vocab_size; k.st = st;
@@ -599,7 +669,7 @@ static llama_status decode_graph(llama_ctx* c, int bsz, int splits, hipGraphExec
     }
     if (!c->cap_stream && hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking) != hipSuccess)
         return LLAMA_ERR_HIP;
-    const StepState* st = c->at<const StepState>(c->L.step);
+    const StepState* st = c->buf.step;
     if (hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal) != hipSuccess)
         return LLAMA_ERR_HIP;
     const llama_status r = decode_plan(c, nullptr, 0, bsz, 0, nullptr, c->cap_stream, st, splits);
@@ -632,9 +702,33 @@ llama_status llama_decode_step(llama_ctx* c, const int32_t* d_tokens, int64_t ld
     hipGraphExec_t exec;
     const llama_status r = decode_graph(c, bsz, splits, &exec);
     if (r != LLAMA_OK) return r;
-    HIP_TRY(launch_set_step(c->at<StepState>(c->L.step), start_pos, ld_tokens, d_tokens, d_logits, s));
+    HIP_TRY(launch_set_step(c->buf.step, start_pos, ld_tokens, d_tokens, d_logits, s));
     HIP_TRY(hipGraphLaunch(exec, s));
     return LLAMA_OK;
+}
+
+llama_status llama_decode_step_noalloc(llama_ctx* c, const int32_t* d_tokens, int64_t ld_tokens,
+                                       int32_t bsz, int32_t start_pos, float* d_logits, void* stream) {
+    if (!c || !d_tokens || !d_logits) return LLAMA_ERR_INVALID_ARG;
+    if (bsz < 1 || bsz > c->a.max_batch_size || start_pos < 0 || start_pos >= c->a.max_seq_len ||
+        ld_tokens < 1)
+        return LLAMA_ERR_INVALID_ARG;
+    if (bsz > kSkinnyMaxRows) return LLAMA_ERR_UNSUPPORTED;
+    if (!c->noalloc_scratch) return LLAMA_ERR_HIP;
+    Bufs b{};
+    if (decode_scratch(c, bsz, start_pos + 1, static_cast<char*>(c->noalloc_scratch), &b) > kNoAllocScratchBytes)
+        return LLAMA_ERR_WORKSPACE;
+    // eager launches only (a graph or a timing event would be created on first use), with the
+    // step's scratch in the static array; the ctx's own scratch is untouched
+    const Bufs saved = c->buf;
+    const int saved_prof = c->prof_class;
+    c->buf = b;
+    c->prof_class = 0;
+    const llama_status r = decode_plan(c, d_tokens, ld_tokens, bsz, start_pos, d_logits,
+                                       static_cast<hipStream_t>(stream), nullptr, 0);
+    c->buf = saved;
+    c->prof_class = saved_prof;
+    return r;
 }
 
 llama_status llama_argmax(const float* d_logits, int32_t bsz, int32_t vocab, int64_t row_stride,

@@ -86,6 +86,14 @@ class LlamaModel:
             self.ctx, tokens.data_ptr() + 4 * col, tokens.shape[1], bsz, start_pos,
             logits.data_ptr(), stream_handle()))
 
+    def decode_step_noalloc(self, tokens: torch.Tensor, bsz: int, col: int, start_pos: int,
+                            logits: torch.Tensor) -> int:
+        """decode_step with the step's scratch in the library's static array (no allocation);
+        returns the status code."""
+        assert tokens.dtype == torch.int32 and tokens.is_contiguous()
+        return abi.llama_decode_step_noalloc(self.ctx, tokens.data_ptr() + 4 * col, tokens.shape[1], bsz,
+                                             start_pos, logits.data_ptr(), stream_handle())
+
 
 def argmax(logits: torch.Tensor, out: torch.Tensor) -> None:
     bsz, vocab = logits.shape[0], logits.shape[-1]

@@ -154,6 +154,25 @@ llama_status llama_prefill(llama_ctx *c, const int32_t *d_tokens, int64_t ld_tok
 llama_status llama_decode_step(llama_ctx *c, const int32_t *d_tokens, int64_t ld_tokens,
                                int32_t bsz, int32_t start_pos, float *d_logits, void *stream);
 
+/* llama_decode_step for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation, the
+ * same kernels and the same results, but the step's scratch (residual rows, q, the
+ * projections' operands, attention split partials, K-split partials) lives in a static device
+ * array of the library, 32 MiB, one per GPU, held until the process ends; the KV cache stays
+ * in the ctx's workspace.  The call allocates nothing (no hipMalloc / hipFree, no graph, no
+ * event; the HIP runtime loads the library's kernels at their first launch, so run one
+ * ordinary call first where even that must not happen).  Every element of the array that a
+ * call reads was written earlier in that call, so nothing in it needs clearing; the array
+ * keeps the last call's contents.  All calls on one GPU share the array: calls that overlap
+ * in time on one GPU (other streams, other threads, other ctxs) race and must be ordered by
+ * the caller.
+ * Errors: as llama_decode_step; UNSUPPORTED if bsz > 32; WORKSPACE if the step's scratch
+ * exceeds the 32 MiB array (it needs about bsz * (3 * n_heads * head_dim + dim + hidden_dim)
+ * * 4 bytes plus 64 * (dim + hidden_dim) bytes for bf16 models and the attention partials);
+ * HIP if the array's device address could not be taken at llama_init. */
+llama_status llama_decode_step_noalloc(llama_ctx *c, const int32_t *d_tokens, int64_t ld_tokens,
+                                       int32_t bsz, int32_t start_pos, float *d_logits, void *stream);
+
 /* Greedy pick (section 8.5, temperature 0): d_out[b] = argmax_v d_logits[b*row_stride + v]
  * over v in [0, vocab); ties go to the lowest index; NaN entries are never picked (a row of
  * only NaN yields -1).  Independent of any ctx.
