@@ -381,6 +381,33 @@ def test_fp16_generate_matches_oracle(name):
     check_generate_rows(wl, W, prompts, tokens, logits, range(len(prompts)), storage="fp16", stated=FP16_TOL)
 
 
+@pytest.mark.timeout(600)
+def test_llama2_7b_b1_fp16_generate_matches_oracle():
+    """The 7B fp16 workload at full depth in the launch configuration bench.py times: batch 1
+    on the vector path (the one-row fp16 GEMV, w2 over three K segments), prefill four rows
+    at a time, 128 greedy decode calls."""
+    wl = synth.WORKLOADS["llama2_7b_b1_fp16"]
+    say(f"case {wl.name}")
+    W = synth.gen_weights(wl, device="cuda")
+    assert W["layers"][0]["wq"].dtype == torch.float16
+    prompts = synth.prompts(wl)
+    tokens, logits, _ = gpu_generate(wl, W, prompts)
+    check_generate_rows(wl, W, prompts, tokens, logits, [0], storage="fp16", stated=FP16_TOL)
+
+
+@pytest.mark.parametrize("widths,batch", [("llama2_7b_b1_fp16", 2), ("llama2_13b_b16", 1)])
+def test_fp16_full_width_one_layer_generate_matches_oracle(widths, batch):
+    """One fp16 layer at full width: 7B at two rows (the two-row GEMV), 13B at one row (dim
+    5120 > one 4096-element segment: the fused norm's statistics take a pass of their own)."""
+    wl = synth.WORKLOADS[widths].with_(name=f"{widths}_fp16_one_layer_b{batch}", dtype="fp16", n_layers=1,
+                                       batch=batch, prompt_len=96, gen_steps=24, prompt_seed=140 + batch)
+    say(f"case {wl.name}")
+    W = synth.gen_weights(wl, device="cuda")
+    prompts = synth.prompts(wl)
+    tokens, logits, _ = gpu_generate(wl, W, prompts)
+    check_generate_rows(wl, W, prompts, tokens, logits, range(batch), storage="fp16", stated=FP16_TOL)
+
+
 def test_fp16_prefill_all_positions_chunked_and_decode():
     """Prefill of every position (whole, and in two chunks the second at start_pos > 0)
     against the oracle's fp16-storage forward, and token-by-token decode against prefill."""
