@@ -14,6 +14,8 @@ duration, timed live with HIP events bound to each of its dispatches; `traffic` 
 bytes per launch that rocprofv3 counters measured for the same kernel and workload (kept
 under profiles/, reported only while the kernel's sources are unchanged).  `cpu_baseline` is the NumPy
 oracle on this host's cores over a bounded sample (the whole model, the first decode calls).
+`mfma_prefill` times, beside the main line, the MFMA-bound 7B prefill: the 32 ragged prompts of
+the batch-32 workload (about 8.4k rows), reported against the dense bf16 MFMA peak.
 """
 from __future__ import annotations
 
@@ -61,11 +63,62 @@ def prefill_bytes(wl, B: int, S: int) -> float:
     return L * per_layer + V * D * e + D * e + B * S * D * e + B * S * L * 2 * KVH * hd * e + B * V * 4
 
 
-def w13_launch_bytes(wl) -> float:
-    """Per launch of the decode [w1;w3] GEMV: both weight matrices, the norm weight, the
-    residual rows read and the gated rows written."""
+def launch_bytes(kernel_class: str, wl) -> float:
+    """Algorithmic HBM bytes of one launch of a decode projection class at the workload's
+    batch B: the weight matrices once, plus the activation rows it reads and writes (fp32
+    rows on the vector path; the residual products read and write the fp32 residual rows)."""
     e = 4 if wl.dtype == "fp32" else 2
-    return 2 * wl.hidden_dim * wl.dim * e + wl.dim * e + wl.batch * wl.dim * 4 + wl.batch * wl.hidden_dim * 4
+    D, F, V, B = wl.dim, wl.hidden_dim, wl.vocab_size, wl.batch
+    nq, nk = wl.n_heads * wl.head_dim, wl.n_kv_heads * wl.head_dim
+    if kernel_class == "gemv_qkv":     # fused norm + [wq; wk; wv] + RoPE + q store + K/V append
+        return (nq + 2 * nk) * D * e + D * e + B * D * 4 + B * nq * 4 + B * 2 * nk * e
+    if kernel_class == "gemv_wo":      # wo + residual add
+        return D * nq * e + B * nq * 4 + 2 * B * D * 4
+    if kernel_class == "gemv_w13":     # fused norm + [w1; w3] + SiLU gate
+        return 2 * F * D * e + D * e + B * D * 4 + B * F * 4
+    if kernel_class == "gemv_w2":      # w2 + residual add
+        return D * F * e + B * F * 4 + 2 * B * D * 4
+    if kernel_class == "gemv_out":     # fused final norm + vocab projection
+        return V * D * e + D * e + B * D * 4 + B * V * 4
+    raise ValueError(f"no per-launch byte count for kernel class {kernel_class!r}: "
+                     "the roofline line takes the decode projection classes gemv_qkv, gemv_wo, "
+                     "gemv_w13, gemv_w2, gemv_out")
+
+
+def mfma_prefill(workload: str, runs: int = 3) -> dict:
+    """The MFMA-bound 7B prefill: the prompt batch of `workload` (32 ragged prompts, the
+    prefill call covers the shortest prompt of every row, about 8.4k rows), its own seeded
+    weights, timed over `runs` calls after one warm-up, with the on-device argmax and select
+    as in a generate's first call."""
+    import torch
+    import synth
+    from decoder_only_transformer_amd import runtime
+    wl = synth.WORKLOADS[workload]
+    W = synth.gen_weights(wl, device="cuda")
+    model = runtime.LlamaModel(runtime.make_args(
+        wl.dim, wl.n_layers, wl.n_heads, wl.n_kv_heads, wl.vocab_size, wl.hidden_dim,
+        wl.norm_eps, wl.rope_theta, wl.batch, wl.max_seq_len, wl.dtype), W)
+    run = runtime.GreedyRun(model, synth.prompts(wl), wl.gen_steps, keep_logits=False)
+    run.reset()
+    run.prefill()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(runs):
+        run.reset()
+        run.prefill()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / runs
+    B, S = run.bsz, run.min_len
+    flops = prefill_flops(wl, B, S)
+    model.close()
+    del W, run
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "batch": B, "prompt_len": S, "rows": B * S, "ms": round(ms, 3),
+            "tok_per_s": round(B * S / (ms / 1e3), 1), "tflops": round(flops / (ms / 1e3) / 1e12, 1),
+            "mfma_frac": round(flops / (ms / 1e3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+            "flops": flops, "runs": runs}
 
 
 def measured_traffic(kernel_class: str, workload: str):
@@ -163,7 +216,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="llama2_7b_b1")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-class", default="gemv_w13")
+    ap.add_argument("--profile-class", default="gemv_w13",
+                    choices=["gemv_qkv", "gemv_wo", "gemv_w13", "gemv_w2", "gemv_out"])
+    ap.add_argument("--mfma-prefill", default="llama2_7b_b32_ragged",
+                    help="workload whose (MFMA-bound) prefill is timed beside the main line; '' skips it")
     ap.add_argument("--gen-steps", type=int, default=0,
                     help="cap on generated positions per step (profiler runs only; 0 = the workload's)")
     args = ap.parse_args()
@@ -243,7 +299,7 @@ def main() -> int:
     runtime.check("profile_read", st)
     abi.llama_profile_select(model.ctx, 0)
     avg_us = k_ms / max(n_launch, 1) * 1e3
-    per_launch = w13_launch_bytes(wl)
+    per_launch = launch_bytes(args.profile_class, wl)
     achieved = per_launch / (avg_us * 1e-6) / 1e9
     log(f"[bench] {args.profile_class}: {n_launch} launches, avg {avg_us:.2f} us, "
         f"{per_launch / 1e6:.1f} MB/launch -> {achieved:.0f} GB/s")
@@ -260,6 +316,12 @@ def main() -> int:
     torch.cuda.synchronize()
     copy_gbs = 5 * 2 * buf.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
     del buf, dst
+
+    mfma = None
+    if args.mfma_prefill and args.mfma_prefill != wl.name:
+        log(f"[bench] MFMA-bound prefill of {args.mfma_prefill} ...")
+        mfma = mfma_prefill(args.mfma_prefill)
+        log(f"[bench] {mfma}")
 
     cpu = None
     if not args.skip_cpu_baseline:
@@ -298,6 +360,7 @@ def main() -> int:
                      "kernel": args.profile_class, "launches": n_launch, "avg_us": round(avg_us, 3),
                      "bytes_per_launch": per_launch},
         "copy_kernel_gbs": round(copy_gbs, 1),
+        "mfma_prefill": mfma,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

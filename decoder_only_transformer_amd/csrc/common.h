@@ -107,6 +107,17 @@ __device__ __forceinline__ double wave_sum(double v) {
 }
 // x^2 exactly (a product of two fp32 values fits fp64's 53-bit significand)
 __device__ __forceinline__ double sq64(float x) { return (double)x * (double)x; }
+// x / d correctly rounded, given r = 1 / d from an IEEE division (correctly rounded) and a
+// finite x and d with the quotient in the normal range: q0 = x r is within one ulp of x / d,
+// the residual x - d q0 is exact in one FMA, and q0 + residual * r rounded once is the
+// correctly rounded quotient (Markstein's correction step) -- three instructions per element
+// where a row shares d, instead of the general division sequence.  With d = 1, r = 0 it
+// returns 0 for any finite x.
+__device__ __forceinline__ float div_rn(float x, float d, float r) {
+    const float q0 = x * r;
+    const float e = __builtin_fmaf(-q0, d, x);
+    return __builtin_fmaf(e, r, q0);
+}
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
     for (int m0 = 0; m0 < a.M; m0 += MB) {
         // RMS denominators sqrt(mean(x^2) + eps): squares summed in fp64 (exact), the mean
         // rounded once to fp32, correctly rounded square root; the operand is x / den * w with
-        // the correctly rounded division.  A reciprocal times x, or a mean off by one bit,
+        // the correctly rounded division (div_rn, the row's reciprocal computed once).  A reciprocal times x, or a mean off by one bit,
         // differs from this in the last bit, which a 16-bit rounding of an embedding row
         // scaled onto exact ties can turn into hundreds of flipped elements.
         float den[MB];
@@ -187,12 +187,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
                     nvf[i] = make_float4(Elem<WT>::lo(nv[i].x), Elem<WT>::hi(nv[i].x), Elem<WT>::lo(nv[i].y),
                                          Elem<WT>::hi(nv[i].y));
             }
-            // NORM: the row's denominator (rows past M: infinity, which normalises them to 0);
-            // otherwise a 1 / 0 factor
-            float scale[MB];
+            // NORM: the row's denominator and its correctly rounded reciprocal (rows past M:
+            // 1 and 0, which normalise them to 0); otherwise a 1 / 0 factor
+            float scale[MB], rcp[MB];
 #pragma unroll
-            for (int m = 0; m < MB; ++m)
-                scale[m] = (m0 + m < a.M) ? den[m] : (NORM ? __builtin_inff() : 0.f);
+            for (int m = 0; m < MB; ++m) {
+                const bool live = m0 + m < a.M;
+                scale[m] = live ? den[m] : (NORM ? 1.f : 0.f);
+                rcp[m] = live ? 1.f / scale[m] : 0.f;
+            }
             // 4. RMS statistics when the whole row is this segment
             if (NORM && one_seg) {
 #pragma unroll
@@ -211,7 +214,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
                     double t = 0.0;
 #pragma unroll
                     for (int w = 0; w < kWavesPerBlock; ++w) t += red[w][m];
-                    scale[m] = (m0 + m < a.M) ? sqrtf((float)(t / (double)a.K) + a.eps) : __builtin_inff();
+                    const bool live = m0 + m < a.M;
+                    scale[m] = live ? sqrtf((float)(t / (double)a.K) + a.eps) : 1.f;
+                    rcp[m] = live ? 1.f / scale[m] : 0.f;
                 }
             }
             // 5. normalise, round to the stored precision, stage in LDS (positions past the
@@ -223,10 +228,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
                 for (int m = 0; m < MB; ++m) {
                     float4 v = xv[m][i];
                     if (NORM) {
-                        v.x = v.x / scale[m] * nvf[i].x;
-                        v.y = v.y / scale[m] * nvf[i].y;
-                        v.z = v.z / scale[m] * nvf[i].z;
-                        v.w = v.w / scale[m] * nvf[i].w;
+                        v.x = div_rn(v.x, scale[m], rcp[m]) * nvf[i].x;
+                        v.y = div_rn(v.y, scale[m], rcp[m]) * nvf[i].y;
+                        v.z = div_rn(v.z, scale[m], rcp[m]) * nvf[i].z;
+                        v.w = div_rn(v.w, scale[m], rcp[m]) * nvf[i].w;
                     } else {
                         v.x *= scale[m];
                         v.y *= scale[m];

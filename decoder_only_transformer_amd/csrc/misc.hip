@@ -6,11 +6,13 @@
 namespace llk {
 namespace {
 
-// h[b*seqlen + s][:] = E[tokens[b*ld + s]][:] as fp32 (the residual stream is fp32).
+// h[b*seqlen + s][:] = E[tokens[b*ld + s]][:] as fp32 (the residual stream is fp32).  The row
+// is read as 16-byte chunks (dim is a multiple of 64 and the table 16-byte aligned), every
+// load of a round issued before its stores, so a row costs one memory round trip.
 template <typename WT>
-__global__ __launch_bounds__(256) void embed_kernel(const int32_t* tokens, int64_t ld, int seqlen,
-                                                    const WT* table, int vocab, int dim, float* h,
-                                                    const StepState* st) {
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens, int64_t ld, int seqlen,
+                                                    const WT* __restrict__ table, int vocab, int dim,
+                                                    float* __restrict__ h, const StepState* st) {
     if (st) {
         tokens = st->tokens;
         ld = st->ld;
@@ -19,15 +21,36 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* tokens, int64
     const int b = t / seqlen, s = t - b * seqlen;
     int tok = tokens[(size_t)b * ld + s];
     tok = min(max(tok, 0), vocab - 1);   // out-of-range ids are a caller error; never read outside E
-    const WT* row = table + (size_t)tok * dim;
+    constexpr int kPer = Elem<WT>::kPer16B;
+    constexpr int kRound = 4;            // chunks per thread per round
+    const uint4* src = reinterpret_cast<const uint4*>(table + (size_t)tok * dim);
     float* out = h + (size_t)t * dim;
-    for (int k = threadIdx.x; k < dim; k += blockDim.x) out[k] = Elem<WT>::load(row, k);
+    const int n = dim / kPer;
+    for (int c0 = threadIdx.x; c0 < n; c0 += 256 * kRound) {
+        uint4 v[kRound];
+#pragma unroll
+        for (int u = 0; u < kRound; ++u) {
+            const int c = c0 + u * 256;
+            v[u] = c < n ? src[c] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kRound; ++u) {
+            const int c = c0 + u * 256;
+            if (c >= n) continue;
+            float f[kPer];
+            Elem<WT>::unpack(v[u], f);
+#pragma unroll
+            for (int j = 0; j < kPer; j += 4)
+                *reinterpret_cast<float4*>(out + (size_t)c * kPer + j) = make_float4(f[j], f[j + 1], f[j + 2], f[j + 3]);
+        }
+    }
 }
 
 // out[r][:] = bf16( h[r][:] / sqrt(mean(h[r]^2) + eps) * w ).  The squares are summed in fp64
 // (each is exact there) and the mean rounded once to fp32, so it is the correctly rounded
 // mean in all but ~1e-7 of rows whatever the summation order; the square root and the
-// division are the correctly rounded fp32 ones.  Where a row of bf16 values (an embedding
+// division are the correctly rounded fp32 ones (the division as div_rn with the row's
+// correctly rounded reciprocal).  Where a row of bf16 values (an embedding
 // row) times the scale lands on many exact bf16 ties, one bit of the denominator decides
 // hundreds of roundings, so the denominator is made exact rather than approximate.
 // With nsplit > 1, h[r] first takes the K-split partial sums of the residual product that
@@ -58,12 +81,13 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(float* h, int64_t ldh
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
     const float den = sqrtf((float)((red[0] + red[1] + red[2] + red[3]) / (double)dim) + eps);
+    const float rcp = 1.0f / den;
     // row-major [rows][ldo], or fragment-major (4 consecutive k stay adjacent in both)
     for (int k = threadIdx.x * 4; k < dim; k += 256 * 4) {
         const float4 v = *reinterpret_cast<const float4*>(x + k);
         uint2 p;
-        p.x = pack_bf16x2(v.x / den * Elem<WT>::load(w, k), v.y / den * Elem<WT>::load(w, k + 1));
-        p.y = pack_bf16x2(v.z / den * Elem<WT>::load(w, k + 2), v.w / den * Elem<WT>::load(w, k + 3));
+        p.x = pack_bf16x2(div_rn(v.x, den, rcp) * Elem<WT>::load(w, k), div_rn(v.y, den, rcp) * Elem<WT>::load(w, k + 1));
+        p.y = pack_bf16x2(div_rn(v.z, den, rcp) * Elem<WT>::load(w, k + 2), div_rn(v.w, den, rcp) * Elem<WT>::load(w, k + 3));
         const size_t o = frag_mt ? frag_index(blockIdx.x, k, frag_mt) : (size_t)blockIdx.x * ldo + k;
         *reinterpret_cast<uint2*>(out + o) = p;
     }
@@ -111,13 +135,14 @@ __global__ __launch_bounds__(256) void rmsnorm_reg_kernel(float* h, int64_t ldh,
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
     const float den = sqrtf((float)((red[0] + red[1] + red[2] + red[3]) / (double)dim) + eps);
+    const float rcp = 1.0f / den;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int k = (threadIdx.x + 256 * i) * 4;
         if (k >= dim) continue;
         uint2 p;
-        p.x = pack_bf16x2(v[i].x / den * bf16lo(wv[i].x), v[i].y / den * bf16hi(wv[i].x));
-        p.y = pack_bf16x2(v[i].z / den * bf16lo(wv[i].y), v[i].w / den * bf16hi(wv[i].y));
+        p.x = pack_bf16x2(div_rn(v[i].x, den, rcp) * bf16lo(wv[i].x), div_rn(v[i].y, den, rcp) * bf16hi(wv[i].x));
+        p.y = pack_bf16x2(div_rn(v[i].z, den, rcp) * bf16lo(wv[i].y), div_rn(v[i].w, den, rcp) * bf16hi(wv[i].y));
         const size_t o = frag_mt ? frag_index(blockIdx.x, k, frag_mt) : (size_t)blockIdx.x * ldo + k;
         *reinterpret_cast<uint2*>(out + o) = p;
     }
