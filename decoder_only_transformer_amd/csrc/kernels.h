@@ -146,8 +146,13 @@ hipError_t launch_flash_prefill(const FlashArgs& a, hipStream_t s);
 // bsz x seqlen rectangle.
 hipError_t launch_rope_scatter_parts(const float* y, int splits, int64_t ldy, int T, const QkvTarget& t,
                                      hipStream_t s);
+// err: if not null, set to 1 when a token id is outside [0, vocab) (the ids are clamped into
+// range either way, so nothing outside the table is read).
 hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, const void* table,
-                        int wtype, int vocab, int dim, float* h, const StepState* st, hipStream_t s);
+                        int wtype, int vocab, int dim, float* h, const StepState* st, hipStream_t s,
+                        int32_t* err = nullptr);
+// *flag = 0 (a one-thread kernel: no memset node if the stream is being captured).
+hipError_t launch_clear_flag(int32_t* flag, hipStream_t s);
 hipError_t launch_set_step(StepState* st, int pos, int64_t ld, const int32_t* tokens, float* logits,
                            hipStream_t s);
 // RMSNorm of fp32 rows to bf16; frag_mt > 0 writes the rows fragment-major (frag_index).

@@ -50,7 +50,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t k_cache, v_cache, rope, h32, q32, o32, g32, act16, g16, part, splitk, step, total;
+    size_t k_cache, v_cache, rope, h32, q32, o32, g32, act16, g16, part, splitk, step, err, total;
     size_t splitk_floats;
     size_t kv_layer_elems;   // elements of one layer's K (or V) cache
 };
@@ -135,6 +135,7 @@ Layout layout_of(const llama_args& a) {
                                           kSplitKRowsCap * splitk_cols(a));
     L.splitk = fp32 ? off : take(L.splitk_floats * sizeof(float));
     L.step = take(sizeof(StepState));
+    L.err = take(sizeof(int32_t));      // checked mode: out-of-range token flag
     L.total = off;
     return L;
 }
@@ -155,6 +156,10 @@ struct llama_ctx {
     hipStream_t cap_stream = nullptr;
     std::map<std::pair<int, int>, hipGraphExec_t> graphs;
     bool use_graphs = false;
+    // checked mode (LLAMA_MI355X_CHECK_TOKENS=1 at llama_init): the embedding gather flags
+    // token ids outside [0, vocab) in err, and the call returns INVALID_ARG after a sync
+    bool check_tokens = false;
+    int32_t* err = nullptr;
 
     // diagnostics: per-kernel begin/end events of the launches of one kernel class
     struct Timer : llk::KernelTimer {
@@ -507,6 +512,17 @@ llama_status final_logits(const llama_ctx* c, const float* x, int64_t ldx, int r
     return LLAMA_OK;
 }
 
+// Checked mode: the flag the embedding gather set during the call, read after the stream has
+// drained; INVALID_ARG if a token id was outside [0, vocab).
+llama_status finish_token_check(const llama_ctx* c, llama_status r, hipStream_t s) {
+    if (!c->check_tokens || r != LLAMA_OK) return r;
+    int32_t flag = 0;
+    if (hipMemcpyAsync(&flag, c->err, sizeof flag, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return LLAMA_ERR_HIP;
+    return flag ? LLAMA_ERR_INVALID_ARG : LLAMA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -558,6 +574,9 @@ llama_status llama_init(const llama_args* a, const llama_weights* w, void* d_wor
         // captured step is no faster than launching its kernels back to back.
         const char* g = std::getenv("LLAMA_MI355X_GRAPHS");
         c->use_graphs = g && g[0] == '1';
+        const char* ck = std::getenv("LLAMA_MI355X_CHECK_TOKENS");
+        c->check_tokens = ck && ck[0] == '1';
+        c->err = c->at<int32_t>(L.err);
     }
 
     // RoPE table: entry (t, i) = (cos, sin) of t * theta^(-2i/hd), computed in float64.
@@ -593,6 +612,10 @@ llama_status llama_init(const llama_args* a, const llama_weights* w, void* d_wor
     return LLAMA_OK;
 }
 
+static llama_status prefill_plan(llama_ctx* c, const int32_t* d_tokens, int64_t ld_tokens, int32_t bsz,
+                                 int32_t seqlen, int32_t start_pos, float* d_logits, int32_t all_positions,
+                                 hipStream_t s);
+
 llama_status llama_prefill(llama_ctx* c, const int32_t* d_tokens, int64_t ld_tokens, int32_t bsz,
                            int32_t seqlen, int32_t start_pos, float* d_logits,
                            int32_t all_positions, void* stream) {
@@ -601,11 +624,20 @@ llama_status llama_prefill(llama_ctx* c, const int32_t* d_tokens, int64_t ld_tok
         (int64_t)start_pos + seqlen > c->a.max_seq_len || ld_tokens < seqlen)
         return LLAMA_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (c->check_tokens) HIP_TRY(launch_clear_flag(c->err, s));
+    return finish_token_check(c, prefill_plan(c, d_tokens, ld_tokens, bsz, seqlen, start_pos, d_logits,
+                                              all_positions, s), s);
+}
+
+// The launch sequence of one prefill call (arguments checked by llama_prefill).
+static llama_status prefill_plan(llama_ctx* c, const int32_t* d_tokens, int64_t ld_tokens, int32_t bsz,
+                                 int32_t seqlen, int32_t start_pos, float* d_logits, int32_t all_positions,
+                                 hipStream_t s) {
     const int D = c->a.dim;
     const int T = bsz * seqlen;
     float* h = c->buf.h32;
     HIP_TRY(launch_embed(d_tokens, ld_tokens, bsz, seqlen, c->w.tok_embeddings, c->wtype,
-                         c->a.vocab_size, D, h, nullptr, s));
+                         c->a.vocab_size, D, h, nullptr, s, c->check_tokens ? c->err : nullptr));
     for (int l = 0; l < c->a.n_layers; ++l) {
         const llama_status st = c->bf16 ? block_mfma(c, l, T, seqlen, start_pos, s)
                                         : block_gemv(c, l, T, seqlen, start_pos, false, s);
@@ -630,7 +662,7 @@ static llama_status decode_plan(llama_ctx* c, const int32_t* d_tokens, int64_t l
     const int D = c->a.dim;
     float* h = c->buf.h32;
     HIP_TRY(launch_embed(d_tokens, ld_tokens, bsz, 1, c->w.tok_embeddings, c->wtype,
-                         c->a.vocab_size, D, h, st, s));
+                         c->a.vocab_size, D, h, st, s, c->check_tokens ? c->err : nullptr));
     if (c->bf16 && bsz > kSkinnyMaxRows) {
         // more rows than the skinny kernels take: the prefill GEMMs with the decode attention
         // (launch arguments only, so not under graph capture)
@@ -695,6 +727,10 @@ llama_status llama_decode_step(llama_ctx* c, const int32_t* d_tokens, int64_t ld
         ld_tokens < 1)
         return LLAMA_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (c->check_tokens) {
+        HIP_TRY(launch_clear_flag(c->err, s));
+        return finish_token_check(c, decode_plan(c, d_tokens, ld_tokens, bsz, start_pos, d_logits, s, nullptr, 0), s);
+    }
     if (!c->use_graphs || c->prof_class != 0 || (c->bf16 && bsz > kSkinnyMaxRows))
         return decode_plan(c, d_tokens, ld_tokens, bsz, start_pos, d_logits, s, nullptr, 0);
     // graph replay: per-step values go to the device step state, then one graph launch
@@ -724,8 +760,9 @@ llama_status llama_decode_step_noalloc(llama_ctx* c, const int32_t* d_tokens, in
     const int saved_prof = c->prof_class;
     c->buf = b;
     c->prof_class = 0;
-    const llama_status r = decode_plan(c, d_tokens, ld_tokens, bsz, start_pos, d_logits,
-                                       static_cast<hipStream_t>(stream), nullptr, 0);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    llama_status r = c->check_tokens && launch_clear_flag(c->err, s) != hipSuccess ? LLAMA_ERR_HIP : LLAMA_OK;
+    if (r == LLAMA_OK) r = finish_token_check(c, decode_plan(c, d_tokens, ld_tokens, bsz, start_pos, d_logits, s, nullptr, 0), s);
     c->buf = saved;
     c->prof_class = saved_prof;
     return r;
@@ -803,6 +840,7 @@ const char* llama_status_str(llama_status st) {
         case LLAMA_ERR_UNSUPPORTED: return "LLAMA_ERR_UNSUPPORTED";
         case LLAMA_ERR_WORKSPACE: return "LLAMA_ERR_WORKSPACE";
         case LLAMA_ERR_HIP: return "LLAMA_ERR_HIP";
+        case LLAMA_STATUS_MAX_ENUM: break;
     }
     return "LLAMA_STATUS_UNKNOWN";
 }

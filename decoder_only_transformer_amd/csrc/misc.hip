@@ -12,7 +12,8 @@ namespace {
 template <typename WT>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens, int64_t ld, int seqlen,
                                                     const WT* __restrict__ table, int vocab, int dim,
-                                                    float* __restrict__ h, const StepState* st) {
+                                                    float* __restrict__ h, const StepState* st,
+                                                    int32_t* err) {
     if (st) {
         tokens = st->tokens;
         ld = st->ld;
@@ -20,6 +21,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
     const int t = blockIdx.x;
     const int b = t / seqlen, s = t - b * seqlen;
     int tok = tokens[(size_t)b * ld + s];
+    if (err && (tok < 0 || tok >= vocab) && threadIdx.x == 0) *err = 1;   // checked mode
     tok = min(max(tok, 0), vocab - 1);   // out-of-range ids are a caller error; never read outside E
     constexpr int kPer = Elem<WT>::kPer16B;
     constexpr int kRound = 4;            // chunks per thread per round
@@ -199,6 +201,8 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* logits, int v
     }
 }
 
+__global__ void clear_flag_kernel(int32_t* flag) { *flag = 0; }
+
 __global__ void set_step_kernel(StepState* st, int pos, int64_t ld, const int32_t* tokens,
                                 float* logits) {
     st->pos = pos;
@@ -260,24 +264,30 @@ hipError_t launch_rope_scatter_parts(const float* y, int splits, int64_t ldy, in
 
 
 hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, const void* table,
-                        int wtype, int vocab, int dim, float* h, const StepState* st, hipStream_t s) {
+                        int wtype, int vocab, int dim, float* h, const StepState* st, hipStream_t s,
+                        int32_t* err) {
     const dim3 grid(bsz * seqlen), block(256);
     switch (wtype) {
         case kStoreBf16:
             launch_kernel(embed_kernel<bf16>, grid, block, 0, s, tokens, ld, seqlen,
-                          static_cast<const bf16*>(table), vocab, dim, h, st);
+                          static_cast<const bf16*>(table), vocab, dim, h, st, err);
             break;
         case kStoreF16:
             launch_kernel(embed_kernel<f16>, grid, block, 0, s, tokens, ld, seqlen,
-                          static_cast<const f16*>(table), vocab, dim, h, st);
+                          static_cast<const f16*>(table), vocab, dim, h, st, err);
             break;
         case kStoreF32:
             launch_kernel(embed_kernel<float>, grid, block, 0, s, tokens, ld, seqlen,
-                          static_cast<const float*>(table), vocab, dim, h, st);
+                          static_cast<const float*>(table), vocab, dim, h, st, err);
             break;
         default:
             return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_clear_flag(int32_t* flag, hipStream_t s) {
+    launch_kernel(clear_flag_kernel, dim3(1), dim3(1), 0, s, flag);
     return hipGetLastError();
 }
 

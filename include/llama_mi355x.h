@@ -21,7 +21,12 @@
  *  - A llama_ctx is not thread-safe; calls on one ctx must be ordered on one stream (or
  *    ordered by the caller across streams).
  *  - Token ids outside [0, vocab_size) are a precondition violation of the caller; the
- *    kernels clamp them into range rather than read out of bounds.
+ *    kernels clamp them into range rather than read out of bounds.  Checked mode (the
+ *    environment variable LLAMA_MI355X_CHECK_TOKENS=1 when llama_init runs) checks them on
+ *    the device: llama_prefill, llama_decode_step and llama_decode_step_noalloc then wait
+ *    for the stream at the end of the call and return LLAMA_ERR_INVALID_ARG if any id of the
+ *    call was out of range (the outputs are those of the clamped ids).  Meant for debugging:
+ *    every call synchronises, and decode steps launch eagerly.
  */
 #ifndef LLAMA_MI355X_H
 #define LLAMA_MI355X_H
@@ -40,7 +45,9 @@ typedef enum llama_status {
     LLAMA_ERR_INVALID_ARG = -1,  /* a precondition of the call does not hold */
     LLAMA_ERR_UNSUPPORTED = -2,  /* valid model, but a shape this library does not implement */
     LLAMA_ERR_WORKSPACE = -3,    /* workspace missing, too small or misaligned */
-    LLAMA_ERR_HIP = -4           /* the HIP runtime reported an error */
+    LLAMA_ERR_HIP = -4,          /* the HIP runtime reported an error */
+    LLAMA_STATUS_MAX_ENUM = 0x7FFFFFFF  /* not a status: makes every int32 a value of the type,
+                                           so llama_status_str may be handed any code */
 } llama_status;
 
 typedef enum llama_dtype {
