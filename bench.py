@@ -46,11 +46,15 @@ def decode_step_bytes(wl, ctx: int) -> float:
     return weights + kv
 
 
-def prefill_flops(wl, B: int, S: int) -> float:
+def prefill_flops(wl, B: int, S: int, start_pos: int = 0) -> float:
+    """Algorithmic flops of a prefill of S tokens per row at start_pos: the projections of
+    every row, causal attention (query i sees start_pos + i + 1 keys), the last positions'
+    logits."""
     D, L, F, V = wl.dim, wl.n_layers, wl.hidden_dim, wl.vocab_size
     hd, H, KVH = wl.head_dim, wl.n_heads, wl.n_kv_heads
     per_layer = H * hd * D + 2 * KVH * hd * D + D * H * hd + 3 * F * D
-    return 2.0 * B * S * per_layer * L + 4.0 * hd * H * L * B * S * (S + 1) / 2 + 2.0 * B * V * D
+    keys = S * start_pos + S * (S + 1) / 2
+    return 2.0 * B * S * per_layer * L + 4.0 * hd * H * L * B * keys + 2.0 * B * V * D
 
 
 def prefill_bytes(wl, B: int, S: int) -> float:
@@ -112,13 +116,37 @@ def mfma_prefill(workload: str, runs: int = 3) -> dict:
     ms = ev[0].elapsed_time(ev[1]) / runs
     B, S = run.bsz, run.min_len
     flops = prefill_flops(wl, B, S)
+    out = {"workload": wl.name, "batch": B, "prompt_len": S, "rows": B * S, "ms": round(ms, 3),
+           "tok_per_s": round(B * S / (ms / 1e3), 1), "tflops": round(flops / (ms / 1e3) / 1e12, 1),
+           "mfma_frac": round(flops / (ms / 1e3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+           "flops": flops, "runs": runs}
+    # Prefill over a cached prefix (the mask's (seqlen, start_pos + seqlen) form): 4 rows of
+    # 2048 tokens at start_pos 2048, after a first 2048-token chunk filled the cache, with the
+    # same weights; the timed calls rewrite positions [2048, 4096) and read [0, 4096).
+    import numpy as np
+    cb, cs = 4, 2048
+    tok = torch.from_numpy(np.random.Generator(np.random.PCG64(7)).integers(
+        3, wl.vocab_size, size=(cb, 2 * cs)).astype(np.int32)).cuda()
+    lg = torch.empty((cb, wl.vocab_size), device="cuda")
+    model.prefill(tok, cb, cs, 0, lg)
+    model.prefill(tok, cb, cs, cs, lg, col=cs)
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(runs):
+        model.prefill(tok, cb, cs, cs, lg, col=cs)
+    ev[1].record()
+    torch.cuda.synchronize()
+    cms = ev[0].elapsed_time(ev[1]) / runs
+    cfl = prefill_flops(wl, cb, cs, cs)
+    out["cached_prefix"] = {"batch": cb, "start_pos": cs, "prompt_len": cs, "ms": round(cms, 3),
+                            "tok_per_s": round(cb * cs / (cms / 1e3), 1),
+                            "tflops": round(cfl / (cms / 1e3) / 1e12, 1),
+                            "mfma_frac": round(cfl / (cms / 1e3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+                            "flops": cfl}
     model.close()
     del W, run
     torch.cuda.empty_cache()
-    return {"workload": wl.name, "batch": B, "prompt_len": S, "rows": B * S, "ms": round(ms, 3),
-            "tok_per_s": round(B * S / (ms / 1e3), 1), "tflops": round(flops / (ms / 1e3) / 1e12, 1),
-            "mfma_frac": round(flops / (ms / 1e3) / (BF16_PEAK_TFLOPS * 1e12), 4),
-            "flops": flops, "runs": runs}
+    return out
 
 
 def measured_traffic(kernel_class: str, workload: str):
