@@ -87,6 +87,33 @@ template <> struct Elem<f16> {
     }
 };
 
+// The 16-bit storage types on the MFMA path: the 16x16x32 product of that type with fp32
+// accumulation, and the conversions the method's storage points use (round to nearest even).
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+template <typename T16> struct Mma;
+template <> struct Mma<bf16> {
+    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+    __device__ __forceinline__ static f32x4_t mma(v8 a, v8 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static uint16_t bits(float x) { return f32_to_bf16(x); }
+    __device__ __forceinline__ static float value(uint16_t b) { return bf16_to_f32(b); }
+    __device__ __forceinline__ static float round(float x) { return round_bf16(x); }
+    __device__ __forceinline__ static uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+};
+template <> struct Mma<f16> {
+    typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+    __device__ __forceinline__ static f32x4_t mma(v8 a, v8 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static uint16_t bits(float x) { return f32_to_f16(x); }
+    __device__ __forceinline__ static float value(uint16_t b) { return f16_to_f32(b); }
+    __device__ __forceinline__ static float round(float x) { return f16_to_f32(f32_to_f16(x)); }
+    __device__ __forceinline__ static uint32_t pack2(float lo, float hi) {
+        return static_cast<uint32_t>(f32_to_f16(lo)) | (static_cast<uint32_t>(f32_to_f16(hi)) << 16);
+    }
+};
+
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 // Streaming (read-once) 16-byte load: non-temporal hint so weights do not evict reused data.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));

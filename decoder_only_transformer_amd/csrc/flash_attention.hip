@@ -1,4 +1,6 @@
-// Causal grouped-query attention for prefill on bf16 MFMA (gfx950 v_mfma_f32_16x16x32_bf16).
+// Causal grouped-query attention for prefill on 16-bit MFMA (gfx950 v_mfma_f32_16x16x32_bf16,
+// or _f16 for fp16 models: every kernel takes the storage type T16 of q, the cache and the
+// output).
 //
 // A workgroup owns one batch row, one kv head and 128 query rows, a query row being a
 // (position, head) pair of the n_rep heads that read this kv head (GQA is never
@@ -14,16 +16,19 @@
 //                 g feeds keys {4g..4g+3} of the first 16-key half and {16+4g..16+4g+3} of
 //                 the second, exactly the 8 scores the lane already holds, so P never moves
 //                 between lanes.  V is staged transposed in LDS to match.
-//  P is split into a bf16 high part and a bf16 remainder (two MFMAs), so the weights keep
-//  ~16 significant bits and the attention is computed with fp32-softmax semantics; Q and K
-//  are bf16 tensors already (they are stored in bf16 by the projection).
+//  P is split into a 16-bit high part and a 16-bit remainder (two MFMAs), so the weights keep
+//  ~16 (bf16) or ~22 (fp16) significant bits and the attention is computed with fp32-softmax
+//  semantics; Q, K and V are 16-bit tensors already (stored so by the projection).  With fp16,
+//  p <= 2^8 (see the running max below) stays far inside the format's range; a p below 2^-24 of
+//  the row maximum flushes to zero, below fp32's resolution of the row sum.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace llk {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
 
@@ -43,15 +48,19 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(u16x8_t v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-// Two floats to two round-to-nearest-even bf16 in one word (low half = a).
+// Two floats to two round-to-nearest-even 16-bit values in one word (low half = a); bf16 with
+// gfx950's paired conversion.
+template <typename T16>
 __device__ __forceinline__ uint32_t cvt_pk(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_t));
+    if constexpr (std::is_same<T16, bf16>::value)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_t));
+    else
+        return Mma<T16>::pack2(a, b);
 }
 
-template <int HD>
+template <typename T16, int HD>
 __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
+    typedef typename Mma<T16>::v8 v8_t;
     constexpr int KS = HD / 32;            // MFMA k-steps over head_dim
     constexpr int DT = HD / 16;            // 16-row tiles of head_dim in O^T
     constexpr int KLD = HD + 8;            // padded K row (elements)
@@ -83,7 +92,7 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
     // prompt compute with the last position's keys and are not stored.
     int s_idx[kQT], head[kQT], qpos[kQT];
     bool row_ok[kQT];
-    bf16x8_t qf[kQT][KS];
+    v8_t qf[kQT][KS];
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
         const int r_local = qtile * kRows + wid * 16 * kQT + qt * 16 + fr;
@@ -91,14 +100,14 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
         head[qt] = kvh * n_rep + r_local % n_rep;
         row_ok[qt] = s_idx[qt] < a.seqlen;
         qpos[qt] = a.start_pos + (row_ok[qt] ? s_idx[qt] : a.seqlen - 1);   // absolute position
-        // Q fragments (bf16-valued fp32 in the q buffer -> exact bf16)
+        // Q fragments (fp32 holding 16-bit values in the q buffer -> exact conversion)
         const float* qp = a.q + ((size_t)b * a.seqlen + (row_ok[qt] ? s_idx[qt] : 0)) * qstride + head[qt] * HD;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u16x8_t v;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = f32_to_bf16(qp[ks * 32 + g * 8 + e]);
-            qf[qt][ks] = as_bf16x8(v);
+            for (int e = 0; e < 8; ++e) v[e] = Mma<T16>::bits(qp[ks * 32 + g * 8 + e]);
+            qf[qt][ks] = __builtin_bit_cast(v8_t, v);
         }
     }
 
@@ -168,10 +177,10 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
             for (int qt = 0; qt < kQT; ++qt) st[qt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&Ks[buf][16 * j + fr][ks * 32 + g * 8]);
+                const v8_t kf = *reinterpret_cast<const v8_t*>(&Ks[buf][16 * j + fr][ks * 32 + g * 8]);
 #pragma unroll
                 for (int qt = 0; qt < kQT; ++qt)
-                    st[qt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qt][ks], st[qt][j], 0, 0, 0);
+                    st[qt][j] = Mma<T16>::mma(kf, qf[qt][ks], st[qt][j]);
             }
         }
         // ---- scale, causal mask (tiles reaching past the first row's position only), online
@@ -219,10 +228,11 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
                     const float p0 = __builtin_amdgcn_exp2f(st[qt][j][e] - m[qt]);
                     const float p1 = __builtin_amdgcn_exp2f(st[qt][j][e + 1] - m[qt]);
                     psum += p0 + p1;
-                    // P = hi + lo, both bf16; k-slot of key (j, e) in the permuted PV order:
+                    // P = hi + lo, both 16-bit; k-slot of key (j, e) in the permuted PV order:
                     // half kk = j / 2, slot (j % 2) * 4 + e of the lane group's 8
-                    const uint32_t hi = cvt_pk(p0, p1);
-                    const uint32_t lo = cvt_pk(p0 - __uint_as_float(hi << 16), p1 - __uint_as_float(hi & 0xffff0000u));
+                    const uint32_t hi = cvt_pk<T16>(p0, p1);
+                    const uint32_t lo = cvt_pk<T16>(p0 - Mma<T16>::value(static_cast<uint16_t>(hi & 0xffffu)),
+                                                    p1 - Mma<T16>::value(static_cast<uint16_t>(hi >> 16)));
                     phi[qt][j >> 1][(j & 1) * 2 + e / 2] = hi;
                     plo[qt][j >> 1][(j & 1) * 2 + e / 2] = lo;
                 }
@@ -237,17 +247,17 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
 #pragma unroll
             for (int t = 0; t < DT; ++t) {
                 // the 8 keys of lane group g in this half, already in k-slot order
-                const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(&Vt[buf][16 * t + fr][32 * kk + 8 * g]);
+                const v8_t vf = *reinterpret_cast<const v8_t*>(&Vt[buf][16 * t + fr][32 * kk + 8 * g]);
 #pragma unroll
                 for (int qt = 0; qt < kQT; ++qt) {
-                    o[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(bf16x8_t, phi[qt][kk]), o[qt][t], 0, 0, 0);
-                    o[qt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(bf16x8_t, plo[qt][kk]), o[qt][t], 0, 0, 0);
+                    o[qt][t] = Mma<T16>::mma(vf, __builtin_bit_cast(v8_t, phi[qt][kk]), o[qt][t]);
+                    o[qt][t] = Mma<T16>::mma(vf, __builtin_bit_cast(v8_t, plo[qt][kk]), o[qt][t]);
                 }
             }
         }
     }
 
-    // ---- O = O^T / l, stored bf16 at [b*seqlen + s][head*hd + d]: 4 consecutive d per store
+    // ---- O = O^T / l, stored 16-bit at [b*seqlen + s][head*hd + d]: 4 consecutive d per store
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
         if (!row_ok[qt]) continue;
@@ -256,8 +266,8 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
             uint2 w;
-            w.x = cvt_pk(o[qt][t][0] * inv, o[qt][t][1] * inv);
-            w.y = cvt_pk(o[qt][t][2] * inv, o[qt][t][3] * inv);
+            w.x = cvt_pk<T16>(o[qt][t][0] * inv, o[qt][t][1] * inv);
+            w.y = cvt_pk<T16>(o[qt][t][2] * inv, o[qt][t][3] * inv);
             *reinterpret_cast<uint2*>(out + 16 * t + 4 * g) = w;
         }
     }
@@ -270,10 +280,12 @@ hipError_t launch_flash_prefill(const FlashArgs& a, hipStream_t s) {
     const int n_qt = (a.seqlen * n_rep + kRows - 1) / kRows;
     const int total = n_qt * a.n_kv_heads * a.bsz;
     const dim3 grid((unsigned)((total + 7) / 8 * 8));     // padded: bijective XCD mapping
+    const bool f16 = a.wtype == kStoreF16;
+    if (!f16 && a.wtype != kStoreBf16) return hipErrorInvalidValue;
     if (a.head_dim == 128)
-        launch_kernel(flash_prefill_kernel<128>, grid, dim3(256), 0, s, a);
+        launch_kernel(f16 ? flash_prefill_kernel<llk::f16, 128> : flash_prefill_kernel<bf16, 128>, grid, dim3(256), 0, s, a);
     else if (a.head_dim == 64)
-        launch_kernel(flash_prefill_kernel<64>, grid, dim3(256), 0, s, a);
+        launch_kernel(f16 ? flash_prefill_kernel<llk::f16, 64> : flash_prefill_kernel<bf16, 64>, grid, dim3(256), 0, s, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -1,7 +1,9 @@
-// bf16 MFMA GEMM for the prefill projections (gfx950 v_mfma_f32_16x16x32_bf16).
+// 16-bit MFMA GEMM for the prefill projections (gfx950 v_mfma_f32_16x16x32_bf16 for bf16
+// models, v_mfma_f32_16x16x32_f16 for fp16 ones; every kernel takes the storage type T16).
 //
-// C[m][n] = sum_k A[m][k] * W[n][k], A = bf16 activations [M][lda], W = nn.Linear weight
-// [N][K] bf16 (row-major, so both operands are K-contiguous and load as 16-byte chunks).
+// C[m][n] = sum_k A[m][k] * W[n][k], A = 16-bit activations [M][lda], W = nn.Linear weight
+// [N][K] of the same type (row-major, so both operands are K-contiguous and load as 16-byte
+// chunks).
 // A workgroup of WGM x WGN waves owns a BM x BN tile, each wave (BM/WGM) x (BN/WGN) as a grid
 // of 16x16 MFMA accumulators.  K advances 64 at a time through double-buffered LDS tiles
 // (rows padded by 16 bytes so the 16-lane fragment reads hit distinct banks); the next
@@ -13,6 +15,7 @@
 // SiLU gate (w1 and w3 interleaved in one B tile so each wave holds matching gate/up
 // accumulators), fp32 store (logits).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -20,7 +23,6 @@
 namespace llk {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -76,7 +78,7 @@ __device__ __forceinline__ bool tile_of(int id, int n_tm, int n_tn, int& tm, int
 }
 
 // Epilogue.  Lane holds C[row0 + e][col] for e = 0..3 of each 16x16 accumulator tile.
-template <int BN, int WGN, int TM, int TN, int EPI>
+template <typename T16, int BN, int WGN, int TM, int TN, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[TM][TN], int m0, int tile_n,
                                          int wm, int wn, int lane) {
     constexpr int WM = TM * 16, WN = TN * 16;
@@ -94,7 +96,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[TM][TN]
                 for (int e = 0; e < 4; ++e) {
                     const int m = m0 + wm * WM + i * 16 + rq + e;
                     if (m < a.M && unit < a.N)
-                        out[(size_t)m * a.ldo16 + unit] = f32_to_bf16(silu(acc[i][j][e]) * acc[i][j + TN / 2][e]);
+                        out[(size_t)m * a.ldo16 + unit] = Mma<T16>::bits(silu(acc[i][j][e]) * acc[i][j + TN / 2][e]);
                 }
             }
         return;
@@ -133,12 +135,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[TM][TN]
                         v = (n & 1) ? partner * cs.y + v * cs.x : v * cs.x - partner * cs.y;
                     }
                     if (n < t.nq) {
-                        t.q[(size_t)mm * t.nq + n] = round_bf16(v);
+                        t.q[(size_t)mm * t.nq + n] = Mma<T16>::round(v);
                     } else {
                         const bool is_k = n < t.nq + t.nk;
                         const int c = is_k ? n - t.nq : n - t.nq - t.nk;
                         uint16_t* cache = static_cast<uint16_t*>(is_k ? t.cache_k : t.cache_v);
-                        cache[cache_row + c] = f32_to_bf16(v);
+                        cache[cache_row + c] = Mma<T16>::bits(v);
                     }
                 }
             }
@@ -167,8 +169,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, f32x4 (&acc)[TM][TN]
         }
 }
 
-template <int BM, int BN, int WGM, int WGN, int EPI>
+template <typename T16, int BM, int BN, int WGM, int WGN, int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs a, int n_tm, int n_tn) {
+    typedef typename Mma<T16>::v8 v8_t;
     constexpr int NT = 64 * WGM * WGN;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int TM = WM / 16, TN = WN / 16;
@@ -241,24 +244,24 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(GemmArgs a, int n_
         if (kt + 1 < kt1) gload(kt + 1);
 #pragma unroll
         for (int ks = 0; ks < BK; ks += 32) {
-            bf16x8_t af[TM], bfr[TN];
+            v8_t af[TM], bfr[TN];
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8_t*>(&As[buf][wm * WM + i * 16 + fr][ks + fk]);
+                af[i] = *reinterpret_cast<const v8_t*>(&As[buf][wm * WM + i * 16 + fr][ks + fk]);
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][wn * WN + j * 16 + fr][ks + fk]);
+                bfr[j] = *reinterpret_cast<const v8_t*>(&Bs[buf][wn * WN + j * 16 + fr][ks + fk]);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = Mma<T16>::mma(af[i], bfr[j], acc[i][j]);
         }
         if (kt + 1 < kt1) lstore(buf ^ 1);
         __syncthreads();
     }
 
-    epilogue<BN, WGN, TM, TN, EPI>(a, acc, m0, tile_n, wm, wn, lane);
+    epilogue<T16, BN, WGN, TM, TN, EPI>(a, acc, m0, tile_n, wm, wn, lane);
 }
 
 // resid[m][n] += sum over splits of part[z][m][n] (rows ldp apart), in split order.
@@ -275,6 +278,7 @@ __global__ void splitk_reduce_kernel(const float* part, int splits, int M, int N
 // SiLU gate from split partials of the [w1; w3] product: unit u of row m has its gate in
 // B row p and its up projection in B row p + half, where (tile, wave column, offset) of u
 // give p (the interleaving the MFMA kernels load w1 and w3 rows in).
+template <typename T16>
 __global__ void swiglu_reduce_kernel(const float* part, int splits, int M, int N, int64_t ldp,
                                      int bn, int wn_cols, uint16_t* out, int64_t ldo) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -289,17 +293,17 @@ __global__ void swiglu_reduce_kernel(const float* part, int splits, int M, int N
         g += row[p];
         v += row[p + half];
     }
-    out[(size_t)m * ldo + u] = f32_to_bf16(silu(g) * v);
+    out[(size_t)m * ldo + u] = Mma<T16>::bits(silu(g) * v);
 }
 
-template <int BM, int BN, int WGM, int WGN, int EPI>
+template <typename T16, int BM, int BN, int WGM, int WGN, int EPI>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     const int ncols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
     const int splits = (EPI == EPI_RESID && a.part) ? std::max(1, a.splits) : 1;
     const int n_tn = (a.N + ncols - 1) / ncols, n_tm = (a.M + BM - 1) / BM;
     const int per_xcd = (n_tn * n_tm + kXcds - 1) / kXcds;
     const dim3 grid(per_xcd * kXcds, 1, splits);
-    launch_kernel((gemm_kernel<BM, BN, WGM, WGN, EPI>), grid, dim3(64 * WGM * WGN), 0, s, a, n_tm, n_tn);
+    launch_kernel((gemm_kernel<T16, BM, BN, WGM, WGN, EPI>), grid, dim3(64 * WGM * WGN), 0, s, a, n_tm, n_tn);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     const size_t n = (size_t)a.M * a.N;
@@ -340,27 +344,47 @@ __device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
 // block: the reads are in flight while the MFMAs run, and no asm output is left pending.
 // The accumulators chain MFMA to MFMA on the same registers (no wait states needed); the
 // new fragments go to registers no MFMA of this block reads (early clobber).
+template <typename T16>
 __device__ __forceinline__ void mfma8_read2(f32x4& c00, f32x4& c10, f32x4& c20, f32x4& c30,
                                             f32x4& c01, f32x4& c11, f32x4& c21, f32x4& c31,
                                             const u32x4_t& a0, const u32x4_t& a1, const u32x4_t& a2,
                                             const u32x4_t& a3, const u32x4_t& b0, const u32x4_t& b1,
                                             u32x4_t& n0, u32x4_t& n1, uint32_t addr0, uint32_t addr1) {
-    asm volatile(
-        "ds_read_b128 %8, %10\n\t"
-        "ds_read_b128 %9, %11\n\t"
-        "v_mfma_f32_16x16x32_bf16 %0, %12, %16, %0\n\t"
-        "v_mfma_f32_16x16x32_bf16 %1, %13, %16, %1\n\t"
-        "v_mfma_f32_16x16x32_bf16 %2, %14, %16, %2\n\t"
-        "v_mfma_f32_16x16x32_bf16 %3, %15, %16, %3\n\t"
-        "v_mfma_f32_16x16x32_bf16 %4, %12, %17, %4\n\t"
-        "v_mfma_f32_16x16x32_bf16 %5, %13, %17, %5\n\t"
-        "v_mfma_f32_16x16x32_bf16 %6, %14, %17, %6\n\t"
-        "v_mfma_f32_16x16x32_bf16 %7, %15, %17, %7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "+v"(c00), "+v"(c10), "+v"(c20), "+v"(c30), "+v"(c01), "+v"(c11), "+v"(c21), "+v"(c31),
-          "=&v"(n0), "=&v"(n1)
-        : "v"(addr0), "v"(addr1), "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b0), "v"(b1)
-        : "memory");
+    if constexpr (std::is_same<T16, f16>::value) {
+        asm volatile(
+            "ds_read_b128 %8, %10\n\t"
+            "ds_read_b128 %9, %11\n\t"
+            "v_mfma_f32_16x16x32_f16 %0, %12, %16, %0\n\t"
+            "v_mfma_f32_16x16x32_f16 %1, %13, %16, %1\n\t"
+            "v_mfma_f32_16x16x32_f16 %2, %14, %16, %2\n\t"
+            "v_mfma_f32_16x16x32_f16 %3, %15, %16, %3\n\t"
+            "v_mfma_f32_16x16x32_f16 %4, %12, %17, %4\n\t"
+            "v_mfma_f32_16x16x32_f16 %5, %13, %17, %5\n\t"
+            "v_mfma_f32_16x16x32_f16 %6, %14, %17, %6\n\t"
+            "v_mfma_f32_16x16x32_f16 %7, %15, %17, %7\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "+v"(c00), "+v"(c10), "+v"(c20), "+v"(c30), "+v"(c01), "+v"(c11), "+v"(c21), "+v"(c31),
+              "=&v"(n0), "=&v"(n1)
+            : "v"(addr0), "v"(addr1), "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b0), "v"(b1)
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_b128 %8, %10\n\t"
+            "ds_read_b128 %9, %11\n\t"
+            "v_mfma_f32_16x16x32_bf16 %0, %12, %16, %0\n\t"
+            "v_mfma_f32_16x16x32_bf16 %1, %13, %16, %1\n\t"
+            "v_mfma_f32_16x16x32_bf16 %2, %14, %16, %2\n\t"
+            "v_mfma_f32_16x16x32_bf16 %3, %15, %16, %3\n\t"
+            "v_mfma_f32_16x16x32_bf16 %4, %12, %17, %4\n\t"
+            "v_mfma_f32_16x16x32_bf16 %5, %13, %17, %5\n\t"
+            "v_mfma_f32_16x16x32_bf16 %6, %14, %17, %6\n\t"
+            "v_mfma_f32_16x16x32_bf16 %7, %15, %17, %7\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "+v"(c00), "+v"(c10), "+v"(c20), "+v"(c30), "+v"(c01), "+v"(c11), "+v"(c21), "+v"(c31),
+              "=&v"(n0), "=&v"(n1)
+            : "v"(addr0), "v"(addr1), "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b0), "v"(b1)
+            : "memory");
+    }
 }
 
 // Epilogue of the 256 x 256 kernel through LDS.  A wave's accumulators (64 rows x 128
@@ -370,7 +394,7 @@ __device__ __forceinline__ void mfma8_read2(f32x4& c00, f32x4& c10, f32x4& c20, 
 // in whole 256-byte segments rather than 4-byte pieces.  Chunks (4 floats) are XOR-swizzled
 // by row so that both the column-wise writes and the row-wise reads spread over the banks.
 // RoPE is applied on the row chunks: a lane holds two whole (even, odd) pairs.
-template <int EPI>
+template <typename T16, int EPI>
 __device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[4][8], int m0, int tile_n,
                                                 int wm, int wn, int lane, float* stage) {
     constexpr int TM = 4, WM = 64, WN = 128;
@@ -418,8 +442,8 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[
                 const int n = tile_n * 128 + wn * 64 + c * 4;
                 if (n >= a.N) continue;
                 uint2 p;
-                p.x = pack_bf16x2(v.x, v.y);
-                p.y = pack_bf16x2(v.z, v.w);
+                p.x = Mma<T16>::pack2(v.x, v.y);
+                p.y = Mma<T16>::pack2(v.z, v.w);
                 *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out16) + (size_t)m * a.ldo16 + n) = p;
             } else {
                 const QkvTarget& t = a.qkv;
@@ -440,14 +464,14 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[
                 }
                 if (n < t.nq) {
                     *reinterpret_cast<float4*>(t.q + (size_t)mm * t.nq + n) =
-                        float4{round_bf16(y.x), round_bf16(y.y), round_bf16(y.z), round_bf16(y.w)};
+                        float4{Mma<T16>::round(y.x), Mma<T16>::round(y.y), Mma<T16>::round(y.z), Mma<T16>::round(y.w)};
                 } else {
                     const bool is_k = n < t.nq + t.nk;
                     const int cc = is_k ? n - t.nq : n - t.nq - t.nk;
                     uint16_t* cache = static_cast<uint16_t*>(is_k ? t.cache_k : t.cache_v);
                     uint2 p;
-                    p.x = pack_bf16x2(y.x, y.y);
-                    p.y = pack_bf16x2(y.z, y.w);
+                    p.x = Mma<T16>::pack2(y.x, y.y);
+                    p.y = Mma<T16>::pack2(y.z, y.w);
                     *reinterpret_cast<uint2*>(cache + ((size_t)b * t.max_seq + pos) * (size_t)t.nk + cc) = p;
                 }
             }
@@ -459,8 +483,9 @@ template <int BM> struct BigShape;
 template <> struct BigShape<256> { static constexpr int WGN = 2, TN = 8, NS = 4; };   // 4 x 2 waves of 64 x 128; 128 KB
 template <> struct BigShape<128> { static constexpr int WGN = 4, TN = 4, NS = 6; };   // 2 x 4 waves of 64 x 64; 144 KB
 
-template <int BM, int EPI>
+template <typename T16, int BM, int EPI>
 __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int n_tn) {
+    typedef typename Mma<T16>::v8 v8_t;
     constexpr int BN = kBigBN, BKS = kBigBK;
     constexpr int WGN = BigShape<BM>::WGN, TM = 4, TN = BigShape<BM>::TN, WM = 64, WN = BN / WGN;
     constexpr int A_INS = BM / 128, B_INS = BN / 128;    // 16-row load instructions per wave
@@ -552,7 +577,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
         // groups 0 .. TN/2 - 2: MFMAs of group jg with group jg + 1's B reads in flight
 #pragma unroll
         for (int jg = 0; jg + 1 < TN / 2; ++jg)
-            mfma8_read2(acc[0][2 * jg], acc[1][2 * jg], acc[2][2 * jg], acc[3][2 * jg],
+            mfma8_read2<T16>(acc[0][2 * jg], acc[1][2 * jg], acc[2][2 * jg], acc[3][2 * jg],
                         acc[0][2 * jg + 1], acc[1][2 * jg + 1], acc[2][2 * jg + 1], acc[3][2 * jg + 1],
                         ra[0], ra[1], ra[2], ra[3], rb[2 * jg], rb[2 * jg + 1], rb[2 * jg + 2], rb[2 * jg + 3],
                         bb + 2 * b_off[2 * jg + 2], bb + 2 * b_off[2 * jg + 3]);
@@ -560,11 +585,10 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
         constexpr int jl = TN / 2 - 1;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-            const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, rb[2 * jl + jj]);
+            const v8_t bf = __builtin_bit_cast(v8_t, rb[2 * jl + jj]);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                acc[i][2 * jl + jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, ra[i]), bf, acc[i][2 * jl + jj], 0, 0, 0);
+                acc[i][2 * jl + jj] = Mma<T16>::mma(__builtin_bit_cast(v8_t, ra[i]), bf, acc[i][2 * jl + jj]);
         }
     };
 
@@ -610,9 +634,9 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
     }
     if constexpr (BM == 256 && EPI != EPI_STORE) {
         static_assert(TN == 8 && WN == 128 && NS * kSlot >= 8 * 64 * 64 * 2, "16 KB of ring per wave");
-        epilogue_staged<EPI>(a, acc, m0, tile_n, wm, wn, lane, reinterpret_cast<float*>(ring) + wid * 64 * 64);
+        epilogue_staged<T16, EPI>(a, acc, m0, tile_n, wm, wn, lane, reinterpret_cast<float*>(ring) + wid * 64 * 64);
     } else {
-        epilogue<BN, WGN, TM, TN, EPI>(a, acc, m0, tile_n, wm, wn, lane);
+        epilogue<T16, BN, WGN, TM, TN, EPI>(a, acc, m0, tile_n, wm, wn, lane);
     }
 }
 
@@ -620,7 +644,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
 // workgroup per CU, at least 8 k-stages per split, partials within the workspace.
 constexpr int kShortRows = 512;
 
-template <int BM, int EPI>
+template <typename T16, int BM, int EPI>
 hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
     const int ncols = (EPI == EPI_SWIGLU) ? kBigBN / 2 : kBigBN;
     const int n_tn = (a.N + ncols - 1) / ncols, n_tm = (a.M + BM - 1) / BM;
@@ -635,7 +659,7 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
         splits = std::min(splits, kMaxBigSplit);
         while (splits > 1 && (size_t)splits * a.M * ldp > a.part_cap) --splits;
     }
-    launch_kernel((gemm_big_kernel<BM, EPI>), dim3(per_xcd * kXcds, 1, splits), dim3(512), 0, s, a,
+    launch_kernel((gemm_big_kernel<T16, BM, EPI>), dim3(per_xcd * kXcds, 1, splits), dim3(512), 0, s, a,
                   n_tm, n_tn);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
@@ -645,29 +669,29 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
         launch_kernel(splitk_reduce_kernel, rgrid, dim3(256), 0, s, a.part, splits, a.M, a.N,
                       (int64_t)ldp, a.resid, a.ldr);
     } else if constexpr (EPI == EPI_SWIGLU) {
-        launch_kernel(swiglu_reduce_kernel, rgrid, dim3(256), 0, s, a.part, splits, a.M, a.N,
+        launch_kernel(swiglu_reduce_kernel<T16>, rgrid, dim3(256), 0, s, a.part, splits, a.M, a.N,
                       (int64_t)ldp, kBigBN, kBigBN / BigShape<BM>::WGN, static_cast<uint16_t*>(a.out16),
                       a.ldo16);
     } else {
-        return launch_rope_scatter_parts(a.part, splits, (int64_t)ldp, a.M, a.qkv, s);
+        return launch_rope_scatter_parts(a.part, splits, (int64_t)ldp, a.M, a.qkv, s, a.wtype);
     }
     return hipGetLastError();
 }
 
-template <int EPI>
+template <typename T16, int EPI>
 hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
     // Small M: narrow register-staged tiles.
-    if (a.M <= 64) return launch_tile<64, 64, 2, 2, EPI>(a, s);
+    if (a.M <= 64) return launch_tile<T16, 64, 64, 2, 2, EPI>(a, s);
     // Short prefills: the weights are the traffic; the LDS-ring kernel with K split so about
     // one workgroup per CU streams them, the epilogue applied by a reduce pass.
     if constexpr (EPI == EPI_QKV || EPI == EPI_RESID || EPI == EPI_SWIGLU) {
         if (a.M <= kShortRows && a.part) {
-            if (a.M <= 128) return launch_big<128, EPI>(a, s);
-            return launch_big<256, EPI>(a, s);
+            if (a.M <= 128) return launch_big<T16, 128, EPI>(a, s);
+            return launch_big<T16, 256, EPI>(a, s);
         }
     }
-    if (a.M <= 256) return launch_tile<128, 64, 2, 2, EPI>(a, s);
-    if (a.M <= 2048) return launch_tile<128, 128, 2, 2, EPI>(a, s);
+    if (a.M <= 256) return launch_tile<T16, 128, 64, 2, 2, EPI>(a, s);
+    if (a.M <= 2048) return launch_tile<T16, 128, 128, 2, 2, EPI>(a, s);
     if constexpr (EPI == EPI_QKV || EPI == EPI_RESID || EPI == EPI_SWIGLU) {
         // 256 x 256 tiles run one per CU, in rounds of kCUs.  When the last round would be
         // nearly empty, the last one or two tile rows (at most kShortRows rows) go to the
@@ -693,7 +717,7 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
                 const int M1 = (n_tm - best_t) * 256, M2 = a.M - M1;
                 GemmArgs a1 = a;
                 a1.M = M1;
-                const hipError_t e = launch_big<256, EPI>(a1, s);
+                const hipError_t e = launch_big<T16, 256, EPI>(a1, s);
                 if (e != hipSuccess) return e;
                 GemmArgs a2 = a;
                 a2.M = M2;
@@ -701,21 +725,30 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
                 if constexpr (EPI == EPI_RESID) a2.resid = a.resid + (size_t)M1 * a.ldr;
                 if constexpr (EPI == EPI_SWIGLU) a2.out16 = static_cast<uint16_t*>(a.out16) + (size_t)M1 * a.ldo16;
                 if constexpr (EPI == EPI_QKV) a2.qkv.row0 = a.qkv.row0 + M1;
-                return M2 <= 128 ? launch_big<128, EPI>(a2, s) : launch_big<256, EPI>(a2, s);
+                return M2 <= 128 ? launch_big<T16, 128, EPI>(a2, s) : launch_big<T16, 256, EPI>(a2, s);
             }
         }
     }
-    return launch_big<256, EPI>(a, s);
+    return launch_big<T16, 256, EPI>(a, s);
+}
+
+template <typename T16>
+hipError_t launch_typed(int epi, const GemmArgs& a, hipStream_t s) {
+    switch (epi) {
+        case EPI_QKV: return launch_epi<T16, EPI_QKV>(a, s);
+        case EPI_RESID: return launch_epi<T16, EPI_RESID>(a, s);
+        case EPI_SWIGLU: return launch_epi<T16, EPI_SWIGLU>(a, s);
+        default: return launch_epi<T16, EPI_STORE>(a, s);
+    }
 }
 
 }  // namespace
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
-    switch (epi) {
-        case EPI_QKV: return launch_epi<EPI_QKV>(a, s);
-        case EPI_RESID: return launch_epi<EPI_RESID>(a, s);
-        case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(a, s);
-        default: return launch_epi<EPI_STORE>(a, s);
+    switch (a.wtype) {
+        case kStoreBf16: return launch_typed<bf16>(epi, a, s);
+        case kStoreF16: return launch_typed<f16>(epi, a, s);
+        default: return hipErrorInvalidValue;
     }
 }
 

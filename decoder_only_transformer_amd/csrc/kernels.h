@@ -76,7 +76,8 @@ struct GemvArgs {
     const StepState* st;   // if set, the STORE epilogue writes st->logits
 };
 
-// C[m][n] = sum_k A[m][k] * W[n][k] on bf16 MFMA, fp32 accumulate.  A bf16 [M][lda].
+// C[m][n] = sum_k A[m][k] * W[n][k] on 16-bit MFMA, fp32 accumulate.  A [M][lda] and W in
+// the storage type wtype (kStoreBf16 or kStoreF16), as are the 16-bit outputs.
 struct GemmArgs {
     const void* a; int64_t lda;
     int M, K, N;           // N = output columns (SWIGLU: hidden units)
@@ -88,6 +89,7 @@ struct GemmArgs {
     int splits;            // K splits of the small-tile residual GEMM: partials [splits][M][N]
     float* part;           // split-K partials (also used by short prefills on the LDS-ring kernel)
     size_t part_cap;       // floats available at `part`
+    int wtype = kStoreBf16;
 };
 
 constexpr int kMaxBigSplit = 16;
@@ -113,8 +115,8 @@ struct AttnArgs {
     const float* q;        // [rows][n_heads*hd] fp32 (RoPE applied)
     const void* cache_k;   // layer base
     const void* cache_v;
-    void* out;             // [rows][n_heads*hd], fp32 or bf16 (out_bf16)
-    int out_bf16;
+    void* out;             // [rows][n_heads*hd], fp32, or 16-bit (out_bf16: the cache's storage
+    int out_bf16;          //   type, bf16 or fp16)
     int out_frag_mt;       // bf16 out: > 0 writes it fragment-major for that many row tiles
     float* part;           // [rows][n_heads][n_split][hd + 2] partials when n_split > 1
     int rows, n_heads, n_kv_heads, head_dim, max_seq;
@@ -125,15 +127,16 @@ struct AttnArgs {
     const StepState* st;   // if set, start_pos comes from st->pos
 };
 
-// Causal GQA attention of a prefill (bf16 MFMA): rows b*seqlen + s at positions start_pos + s.
+// Causal GQA attention of a prefill (16-bit MFMA): rows b*seqlen + s at positions start_pos + s.
 struct FlashArgs {
-    const float* q;        // [bsz*seqlen][n_heads*hd] (bf16-valued fp32)
-    const void* cache_k;   // layer base, bf16
+    const float* q;        // [bsz*seqlen][n_heads*hd] (fp32 holding values of the storage type)
+    const void* cache_k;   // layer base, storage type
     const void* cache_v;
-    void* out;             // [bsz*seqlen][n_heads*hd] bf16
+    void* out;             // [bsz*seqlen][n_heads*hd] storage type
     int bsz, seqlen, start_pos;
     int n_heads, n_kv_heads, head_dim, max_seq;
     float scale;
+    int wtype = kStoreBf16;    // kStoreBf16 or kStoreF16
 };
 
 // Temperature + top-p draw, one token per row (vocab <= kMaxSampleVocab); see sampling.hip.
@@ -145,7 +148,7 @@ hipError_t launch_flash_prefill(const FlashArgs& a, hipStream_t s);
 // projections [splits][T][ldy] (summed in split order); row m is row t.row0 + m of the
 // bsz x seqlen rectangle.
 hipError_t launch_rope_scatter_parts(const float* y, int splits, int64_t ldy, int T, const QkvTarget& t,
-                                     hipStream_t s);
+                                     hipStream_t s, int wtype = kStoreBf16);
 // err: if not null, set to 1 when a token id is outside [0, vocab) (the ids are clamped into
 // range either way, so nothing outside the table is read).
 hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, const void* table,
@@ -155,14 +158,15 @@ hipError_t launch_embed(const int32_t* tokens, int64_t ld, int bsz, int seqlen, 
 hipError_t launch_clear_flag(int32_t* flag, hipStream_t s);
 hipError_t launch_set_step(StepState* st, int pos, int64_t ld, const int32_t* tokens, float* logits,
                            hipStream_t s);
-// RMSNorm of fp32 rows to bf16; frag_mt > 0 writes the rows fragment-major (frag_index).
+// RMSNorm of fp32 rows to the 16-bit storage type wtype (norm weights of that type);
+// frag_mt > 0 writes the rows fragment-major (frag_index).
 // nsplit > 1 (at most kMaxNormFold): h[r] += part[0][r] + ... + part[nsplit-1][r] first (the
 // K-split partials [nsplit][rows][dim] of the residual product that precedes the norm),
 // written back to h.
 constexpr int kMaxNormFold = 4;
 hipError_t launch_rmsnorm_bf16(float* h, int64_t ldh, int rows, int dim, const void* w,
                                float eps, void* out, int64_t ldo, int frag_mt, hipStream_t s,
-                               const float* part = nullptr, int nsplit = 0);
+                               const float* part = nullptr, int nsplit = 0, int wtype = kStoreBf16);
 hipError_t launch_gemv(int wtype, int epi, const GemvArgs& a, hipStream_t s);   // wtype: kStore*
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
 hipError_t launch_skinny(int epi, const SkinnyArgs& a, hipStream_t s);

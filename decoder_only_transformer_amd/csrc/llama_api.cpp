@@ -104,9 +104,10 @@ Layout layout_of(const llama_args& a) {
     const size_t nq = (size_t)a.n_heads * hd;
     const size_t maxB = a.max_batch_size, maxS = a.max_seq_len;
     const size_t maxT = maxB * maxS;
-    // the vector path (fp32 and fp16 models) keeps every row's activations in fp32 and needs
-    // none of the MFMA path's bf16 operands or split-K partials
-    const bool fp32 = a.dtype != LLAMA_BF16;
+    // fp32 models run everything on the vector path, which keeps every row's activations in
+    // fp32 and needs none of the MFMA path's 16-bit operands or split-K partials; bf16 and
+    // fp16 models prefill on MFMA and keep fp32 activations for decode rows only
+    const bool fp32 = a.dtype == LLAMA_FP32;
     const size_t rows32 = fp32 ? maxT : maxB;
     L.kv_layer_elems = maxB * maxS * (size_t)a.n_kv_heads * hd;
     size_t off = 0;
@@ -149,7 +150,8 @@ struct llama_ctx {
     Layout L;
     char* ws;
     int hd, nq, nk;
-    bool bf16;      // the MFMA path (bf16 models)
+    bool bf16;      // bf16 model: MFMA prefill and the skinny MFMA decode products
+    bool mfma16;    // bf16 or fp16 model: prefill on the 16-bit MFMA path
     int wtype;      // storage type of weights and KV cache (kStoreF32 / kStoreBf16 / kStoreF16)
 
     // decode graphs: one per (bsz, key splits), captured on a private stream
@@ -438,7 +440,8 @@ llama_status block_skinny(const llama_ctx* c, int l, int M, int start_pos, hipSt
     return LLAMA_OK;
 }
 
-// One transformer block on the bf16 MFMA path for T = bsz*seqlen prefill rows.
+// One transformer block on the 16-bit MFMA path (bf16 or fp16 model) for T = bsz*seqlen prefill
+// rows (or decode rows of a large bf16 batch).
 llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_pos, hipStream_t s,
                         bool decode = false) {
     const llama_layer_weights& W = c->layers[l];
@@ -447,8 +450,9 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
     void* act = c->buf.act16;
     void* g16 = c->buf.g16;
 
-    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.attention_norm, c->a.norm_eps, act, D, 0, s));
+    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.attention_norm, c->a.norm_eps, act, D, 0, s, nullptr, 0, c->wtype));
     GemmArgs g{};
+    g.wtype = c->wtype;
     g.a = act; g.lda = D; g.M = T; g.K = D; g.N = c->nq + 2 * c->nk;
     g.w0 = W.wq; g.w1 = W.wk; g.w2 = W.wv;
     g.qkv = qkv_target(c, l, start_pos, seqlen);
@@ -473,6 +477,7 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
         fa.head_dim = c->hd;
         fa.max_seq = c->a.max_seq_len;
         fa.scale = 1.0f / std::sqrt((float)c->hd);
+        fa.wtype = c->wtype;
         LAUNCH(c, LLAMA_KC_ATTN_PREFILL, s, launch_flash_prefill(fa, s));
     } else {
         llama_status st = run_attention(c, l, T, seqlen, start_pos, act, true, false, s);
@@ -480,19 +485,22 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
     }
 
     g = GemmArgs{};
+    g.wtype = c->wtype;
     g.a = act; g.lda = c->nq; g.M = T; g.K = c->nq; g.N = D;
     g.w0 = W.wo; g.resid = h; g.ldr = D;
     g.splits = residual_splits(c, T, c->nq); g.part = c->buf.splitk; g.part_cap = c->buf.splitk_floats;
     LAUNCH(c, LLAMA_KC_GEMM_WO, s, launch_gemm(EPI_RESID, g, s));
 
-    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.ffn_norm, c->a.norm_eps, act, D, 0, s));
+    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.ffn_norm, c->a.norm_eps, act, D, 0, s, nullptr, 0, c->wtype));
     g = GemmArgs{};
+    g.wtype = c->wtype;
     g.a = act; g.lda = D; g.M = T; g.K = D; g.N = F;
     g.w0 = W.w1; g.w1 = W.w3; g.out16 = g16; g.ldo16 = F;
     g.part = c->buf.splitk; g.part_cap = c->buf.splitk_floats;
     LAUNCH(c, LLAMA_KC_GEMM_W13, s, launch_gemm(EPI_SWIGLU, g, s));
 
     g = GemmArgs{};
+    g.wtype = c->wtype;
     g.a = g16; g.lda = F; g.M = T; g.K = F; g.N = D;
     g.w0 = W.w2; g.resid = h; g.ldr = D;
     g.splits = residual_splits(c, T, F); g.part = c->buf.splitk; g.part_cap = c->buf.splitk_floats;
@@ -565,6 +573,7 @@ llama_status llama_init(const llama_args* a, const llama_weights* w, void* d_wor
     c->nq = a->n_heads * c->hd;
     c->nk = a->n_kv_heads * c->hd;
     c->bf16 = a->dtype == LLAMA_BF16;
+    c->mfma16 = a->dtype != LLAMA_FP32;
     c->buf = Bufs{c->at<float>(L.h32), c->at<float>(L.q32), c->at<float>(L.o32), c->at<float>(L.g32),
                   c->at<float>(L.part), c->at<float>(L.splitk), c->at<void>(L.act16), c->at<void>(L.g16),
                   c->at<StepState>(L.step), L.splitk_floats};
@@ -639,15 +648,16 @@ static llama_status prefill_plan(llama_ctx* c, const int32_t* d_tokens, int64_t 
     HIP_TRY(launch_embed(d_tokens, ld_tokens, bsz, seqlen, c->w.tok_embeddings, c->wtype,
                          c->a.vocab_size, D, h, nullptr, s, c->check_tokens ? c->err : nullptr));
     for (int l = 0; l < c->a.n_layers; ++l) {
-        const llama_status st = c->bf16 ? block_mfma(c, l, T, seqlen, start_pos, s)
-                                        : block_gemv(c, l, T, seqlen, start_pos, false, s);
+        const llama_status st = c->mfma16 ? block_mfma(c, l, T, seqlen, start_pos, s)
+                                          : block_gemv(c, l, T, seqlen, start_pos, false, s);
         if (st != LLAMA_OK) return st;
     }
     if (!all_positions) return final_logits(c, h + (size_t)(seqlen - 1) * D, (int64_t)seqlen * D, bsz, d_logits, s);
-    if (!c->bf16) return final_logits(c, h, D, T, d_logits, s);
+    if (!c->mfma16) return final_logits(c, h, D, T, d_logits, s);
     void* act = c->buf.act16;
-    HIP_TRY(launch_rmsnorm_bf16(h, D, T, D, c->w.norm, c->a.norm_eps, act, D, 0, s));
+    HIP_TRY(launch_rmsnorm_bf16(h, D, T, D, c->w.norm, c->a.norm_eps, act, D, 0, s, nullptr, 0, c->wtype));
     GemmArgs g{};
+    g.wtype = c->wtype;
     g.a = act; g.lda = D; g.M = T; g.K = D; g.N = c->a.vocab_size;
     g.w0 = c->w.output; g.out = d_logits; g.ldo = c->a.vocab_size;
     HIP_TRY(launch_gemm(EPI_STORE, g, s));

@@ -88,8 +88,8 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(float* h, int64_t ldh
     for (int k = threadIdx.x * 4; k < dim; k += 256 * 4) {
         const float4 v = *reinterpret_cast<const float4*>(x + k);
         uint2 p;
-        p.x = pack_bf16x2(div_rn(v.x, den, rcp) * Elem<WT>::load(w, k), div_rn(v.y, den, rcp) * Elem<WT>::load(w, k + 1));
-        p.y = pack_bf16x2(div_rn(v.z, den, rcp) * Elem<WT>::load(w, k + 2), div_rn(v.w, den, rcp) * Elem<WT>::load(w, k + 3));
+        p.x = Mma<WT>::pack2(div_rn(v.x, den, rcp) * Elem<WT>::load(w, k), div_rn(v.y, den, rcp) * Elem<WT>::load(w, k + 1));
+        p.y = Mma<WT>::pack2(div_rn(v.z, den, rcp) * Elem<WT>::load(w, k + 2), div_rn(v.w, den, rcp) * Elem<WT>::load(w, k + 3));
         const size_t o = frag_mt ? frag_index(blockIdx.x, k, frag_mt) : (size_t)blockIdx.x * ldo + k;
         *reinterpret_cast<uint2*>(out + o) = p;
     }
@@ -98,8 +98,8 @@ __global__ __launch_bounds__(256) void rmsnorm_bf16_kernel(float* h, int64_t ldh
 // Same, for rows of at most 1024 * NV elements: every load of the row (and of the weights and
 // NS partials) is issued before the first use and the row stays in registers for the second
 // half, so a row costs one memory round trip instead of one per chunk and pass.
-template <int NV, int NS>
-__global__ __launch_bounds__(256) void rmsnorm_reg_kernel(float* h, int64_t ldh, int dim, const bf16* w,
+template <typename T16, int NV, int NS>
+__global__ __launch_bounds__(256) void rmsnorm_reg_kernel(float* h, int64_t ldh, int dim, const T16* w,
                                                           float eps, uint16_t* out, int64_t ldo, int frag_mt,
                                                           const float* part) {
     __shared__ double red[4];
@@ -143,8 +143,10 @@ __global__ __launch_bounds__(256) void rmsnorm_reg_kernel(float* h, int64_t ldh,
         const int k = (threadIdx.x + 256 * i) * 4;
         if (k >= dim) continue;
         uint2 p;
-        p.x = pack_bf16x2(div_rn(v[i].x, den, rcp) * bf16lo(wv[i].x), div_rn(v[i].y, den, rcp) * bf16hi(wv[i].x));
-        p.y = pack_bf16x2(div_rn(v[i].z, den, rcp) * bf16lo(wv[i].y), div_rn(v[i].w, den, rcp) * bf16hi(wv[i].y));
+        p.x = Mma<T16>::pack2(div_rn(v[i].x, den, rcp) * Elem<T16>::lo(wv[i].x),
+                              div_rn(v[i].y, den, rcp) * Elem<T16>::hi(wv[i].x));
+        p.y = Mma<T16>::pack2(div_rn(v[i].z, den, rcp) * Elem<T16>::lo(wv[i].y),
+                              div_rn(v[i].w, den, rcp) * Elem<T16>::hi(wv[i].y));
         const size_t o = frag_mt ? frag_index(blockIdx.x, k, frag_mt) : (size_t)blockIdx.x * ldo + k;
         *reinterpret_cast<uint2*>(out + o) = p;
     }
@@ -220,6 +222,7 @@ __global__ void select_kernel(const int32_t* next, int32_t* tokens, int64_t ld, 
 
 // RoPE + bf16 storage of q and the K/V cache append from fp32 projections y [T][nq+2nk]
 // (used when the [wq;wk;wv] GEMM stores plainly).  One thread per (row, pair).
+template <typename T16>
 __global__ void rope_scatter_kernel(const float* y, int splits, int64_t ldy, int T, QkvTarget t) {
     const int npairs = (t.nq + 2 * t.nk) / 2;
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -243,22 +246,27 @@ __global__ void rope_scatter_kernel(const float* y, int splits, int64_t ldy, int
         y1 = r1;
     }
     if (n0 < t.nq) {
-        *reinterpret_cast<float2*>(t.q + (size_t)mm * t.nq + n0) = make_float2(round_bf16(y0), round_bf16(y1));
+        *reinterpret_cast<float2*>(t.q + (size_t)mm * t.nq + n0) = make_float2(Mma<T16>::round(y0), Mma<T16>::round(y1));
         return;
     }
     const bool is_k = n0 < t.nq + t.nk;
     const int c = is_k ? n0 - t.nq : n0 - t.nq - t.nk;
     uint16_t* cache = static_cast<uint16_t*>(is_k ? t.cache_k : t.cache_v);
-    *reinterpret_cast<uint32_t*>(cache + ((size_t)b * t.max_seq + pos) * (size_t)t.nk + c) = pack_bf16x2(y0, y1);
+    *reinterpret_cast<uint32_t*>(cache + ((size_t)b * t.max_seq + pos) * (size_t)t.nk + c) = Mma<T16>::pack2(y0, y1);
 }
 
 }  // namespace
 
 hipError_t launch_rope_scatter_parts(const float* y, int splits, int64_t ldy, int T, const QkvTarget& t,
-                                     hipStream_t s) {
+                                     hipStream_t s, int wtype) {
     const size_t n = (size_t)T * ((t.nq + 2 * t.nk) / 2);
-    launch_kernel(rope_scatter_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, y, splits,
-                  ldy, T, t);
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (wtype == kStoreBf16)
+        launch_kernel(rope_scatter_kernel<bf16>, grid, dim3(256), 0, s, y, splits, ldy, T, t);
+    else if (wtype == kStoreF16)
+        launch_kernel(rope_scatter_kernel<f16>, grid, dim3(256), 0, s, y, splits, ldy, T, t);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
@@ -297,36 +305,44 @@ hipError_t launch_set_step(StepState* st, int pos, int64_t ld, const int32_t* to
     return hipGetLastError();
 }
 
-template <int NS>
-void launch_rmsnorm_ns(float* h, int64_t ldh, int rows, int dim, const bf16* wb, float eps, uint16_t* o,
+template <typename T16, int NS>
+void launch_rmsnorm_ns(float* h, int64_t ldh, int rows, int dim, const T16* wb, float eps, uint16_t* o,
                        int64_t ldo, int frag_mt, const float* part, hipStream_t s) {
     switch ((dim + 1023) / 1024) {
-        case 1: launch_kernel((rmsnorm_reg_kernel<1, NS>), dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt, part); break;
-        case 2: launch_kernel((rmsnorm_reg_kernel<2, NS>), dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt, part); break;
+        case 1: launch_kernel((rmsnorm_reg_kernel<T16, 1, NS>), dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt, part); break;
+        case 2: launch_kernel((rmsnorm_reg_kernel<T16, 2, NS>), dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt, part); break;
         case 3:
-        case 4: launch_kernel((rmsnorm_reg_kernel<4, NS>), dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt, part); break;
+        case 4: launch_kernel((rmsnorm_reg_kernel<T16, 4, NS>), dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt, part); break;
         case 5:
-        case 6: launch_kernel((rmsnorm_reg_kernel<6, NS>), dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt, part); break;
-        default: launch_kernel((rmsnorm_reg_kernel<8, NS>), dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt, part); break;
+        case 6: launch_kernel((rmsnorm_reg_kernel<T16, 6, NS>), dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt, part); break;
+        default: launch_kernel((rmsnorm_reg_kernel<T16, 8, NS>), dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt, part); break;
     }
+}
+
+template <typename T16>
+void launch_rmsnorm16(float* h, int64_t ldh, int rows, int dim, const void* w, float eps, uint16_t* o, int64_t ldo,
+                      int frag_mt, hipStream_t s, const float* part, int nsplit) {
+    const T16* wb = static_cast<const T16*>(w);
+    if (dim > 8192 || nsplit > 2)
+        launch_kernel(rmsnorm_bf16_kernel<T16>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt,
+                      part, nsplit);
+    else if (nsplit == 2)
+        launch_rmsnorm_ns<T16, 2>(h, ldh, rows, dim, wb, eps, o, ldo, frag_mt, part, s);
+    else
+        launch_rmsnorm_ns<T16, 0>(h, ldh, rows, dim, wb, eps, o, ldo, frag_mt, nullptr, s);
 }
 
 hipError_t launch_rmsnorm_bf16(float* h, int64_t ldh, int rows, int dim, const void* w,
                                float eps, void* out, int64_t ldo, int frag_mt, hipStream_t s,
-                               const float* part, int nsplit) {
-    const bf16* wb = static_cast<const bf16*>(w);
+                               const float* part, int nsplit, int wtype) {
     uint16_t* o = static_cast<uint16_t*>(out);
     if (nsplit > 1 && (!part || nsplit > kMaxNormFold)) return hipErrorInvalidValue;
-    if (dim > 8192)
-        launch_kernel(rmsnorm_bf16_kernel<bf16>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt,
-                      part, nsplit);
-    else if (nsplit == 2)
-        launch_rmsnorm_ns<2>(h, ldh, rows, dim, wb, eps, o, ldo, frag_mt, part, s);
-    else if (nsplit > 1)
-        launch_kernel(rmsnorm_bf16_kernel<bf16>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt,
-                      part, nsplit);
+    if (wtype == kStoreBf16)
+        launch_rmsnorm16<bf16>(h, ldh, rows, dim, w, eps, o, ldo, frag_mt, s, part, nsplit);
+    else if (wtype == kStoreF16)
+        launch_rmsnorm16<f16>(h, ldh, rows, dim, w, eps, o, ldo, frag_mt, s, part, nsplit);
     else
-        launch_rmsnorm_ns<0>(h, ldh, rows, dim, wb, eps, o, ldo, frag_mt, nullptr, s);
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
