@@ -73,10 +73,19 @@ __device__ __forceinline__ void merge_with_lane(float (&m)[NREP], float (&l)[NRE
     }
 }
 
+// A 16-bit output in the cache's storage type: fp16 for fp16 caches, bf16 otherwise.
+template <typename KT>
+__device__ __forceinline__ uint16_t out16(float x) {
+    if constexpr (std::is_same<KT, f16>::value)
+        return f32_to_f16(x);
+    else
+        return f32_to_bf16(x);
+}
+
 // Second pass of a split launch: output (row t, head h, dim d) from the n_split partials
 // (m, l, acc) of its splits, combined in split order.  One workgroup per (row, head), one
 // thread per dim; the partials were written by the first pass with plain stores.
-template <bool OUT_BF16>
+template <typename KT, bool OUT_BF16>
 __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
     const int t = a.row0 + blockIdx.y, h = blockIdx.x, d = threadIdx.x;
     const int HD = a.head_dim;
@@ -98,18 +107,9 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(AttnArgs a) {
     const size_t qstride = (size_t)a.n_heads * HD;
     if (OUT_BF16)
         static_cast<uint16_t*>(a.out)[a.out_frag_mt ? frag_index(t, h * HD + d, a.out_frag_mt)
-                                                    : (size_t)t * qstride + h * HD + d] = f32_to_bf16(o);
+                                                    : (size_t)t * qstride + h * HD + d] = out16<KT>(o);
     else
         static_cast<float*>(a.out)[(size_t)t * qstride + h * HD + d] = o;
-}
-
-// A 16-bit output in the cache's storage type: fp16 for fp16 caches, bf16 otherwise.
-template <typename KT>
-__device__ __forceinline__ uint16_t out16(float x) {
-    if constexpr (std::is_same<KT, f16>::value)
-        return f32_to_f16(x);
-    else
-        return f32_to_bf16(x);
 }
 
 template <typename KT, int HD, int NREP, bool OUT_BF16, int WAVES>
@@ -468,10 +468,7 @@ hipError_t launch4(const AttnArgs& args, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (a.n_split > 1) {
-            // the merge pass writes bf16 16-bit outputs (fp16 caches split only on the vector
-            // path, whose output is fp32)
-            if (OB && !std::is_same<KT, bf16>::value) return hipErrorInvalidValue;
-            launch_kernel((attn_merge_kernel<OB>), dim3(a.n_heads, n), dim3(128), 0, s, a);
+            launch_kernel((attn_merge_kernel<KT, OB>), dim3(a.n_heads, n), dim3(128), 0, s, a);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -507,7 +504,7 @@ hipError_t launch_attn_rows(int kv_type, const AttnArgs& a, hipStream_t s) {
         case kStoreBf16: return a.out_bf16 ? launch2<bf16, true>(a, s) : launch2<bf16, false>(a, s);
         case kStoreF32: return a.out_bf16 ? launch2<float, true>(a, s) : launch2<float, false>(a, s);
         // fp16 caches: fp32 output on the vector path; 16-bit (fp16) output for the MFMA
-        // prefill's operand (prefill rows never split over keys)
+        // products' operand
         case kStoreF16: return a.out_bf16 ? launch2<f16, true>(a, s) : launch2<f16, false>(a, s);
         default: return hipErrorInvalidValue;
     }

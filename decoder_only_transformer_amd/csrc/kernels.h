@@ -94,7 +94,7 @@ struct GemmArgs {
 
 constexpr int kMaxBigSplit = 16;
 
-// y = x W^T for M <= 32 rows on bf16 MFMA (decode with batch > 4).  x is bf16 in
+// y = x W^T for M <= 32 rows on 16-bit MFMA (decode with batch > 4).  x is 16-bit (wtype) in
 // fragment-major order for MT = ceil(M / 16) row tiles (frag_index).
 struct SkinnyArgs {
     const void* x;
@@ -107,6 +107,7 @@ struct SkinnyArgs {
     float* part;           //   to part[split][M][N] in place of adding it to resid
     QkvTarget qkv;
     const StepState* st;   // if set, the STORE epilogue writes st->logits
+    int wtype = kStoreBf16;    // storage type of the weights and 16-bit activations
 };
 
 // Causal attention for a set of query rows against the KV cache (one query position per

@@ -3,12 +3,14 @@
 //
 // Launch plan ("Llama 2 Reference Implementation -- Administrator & Developer Guide",
 // section 8.4: embed -> n_layers pre-norm blocks -> final norm -> output projection):
-//   prefill, bf16:  embed | per layer: rmsnorm->bf16, MFMA [wq;wk;wv] (+RoPE, KV append),
-//                   attention, MFMA wo (+residual), rmsnorm->bf16, MFMA [w1;w3] (+SiLU gate),
-//                   MFMA w2 (+residual) | final norm fused into the vocab projection.
-//   decode (and the fp32 path): embed | per layer: GEMV [wq;wk;wv] with fused RMSNorm,
-//                   split attention (+merge), GEMV wo (+residual), GEMV [w1;w3] with fused
-//                   RMSNorm (+SiLU gate), GEMV w2 (+residual) | fused final norm + vocab GEMV.
+//   prefill, bf16 and fp16: embed | per layer: rmsnorm->16-bit, MFMA [wq;wk;wv] (+RoPE, KV
+//                   append), attention, MFMA wo (+residual), rmsnorm->16-bit, MFMA [w1;w3]
+//                   (+SiLU gate), MFMA w2 (+residual) | final norm fused into the vocab projection.
+//   decode at batch <= 4 (and the fp32 path): embed | per layer: GEMV [wq;wk;wv] with fused
+//                   RMSNorm, split attention (+merge), GEMV wo (+residual), GEMV [w1;w3] with
+//                   fused RMSNorm (+SiLU gate), GEMV w2 (+residual) | fused final norm + vocab GEMV.
+//   decode at batch 5..32 (16-bit): the same blocks with the products on the skinny MFMA
+//                   kernel; above 32 rows, the prefill GEMMs with the decode attention.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -43,7 +45,7 @@ constexpr int kMaxSplit = 32;
 constexpr int kMaxSplitK = 8;      // K splits of a residual GEMM at small prefill sizes
 constexpr int kSplitKRows = 512;   // prefill rows up to which split-K is considered
 constexpr size_t kSplitKRowsCap = 2048;  // splits x rows the split-K workspace holds
-constexpr int kSkinnyRows = 4;      // bf16 decode batches above this use the skinny MFMA kernel
+constexpr int kSkinnyRows = 4;      // 16-bit decode batches above this use the skinny MFMA kernel
 constexpr int kSkinnyMaxRows = 32;  // ... up to this many rows; larger ones the prefill GEMMs
 constexpr size_t kAlign = 256;
 
@@ -150,8 +152,8 @@ struct llama_ctx {
     Layout L;
     char* ws;
     int hd, nq, nk;
-    bool bf16;      // bf16 model: MFMA prefill and the skinny MFMA decode products
-    bool mfma16;    // bf16 or fp16 model: prefill on the 16-bit MFMA path
+    bool bf16;      // bf16 model: the GQA decode attention on MFMA
+    bool mfma16;    // bf16 or fp16 model: prefill and the skinny decode products on 16-bit MFMA
     int wtype;      // storage type of weights and KV cache (kStoreF32 / kStoreBf16 / kStoreF16)
 
     // decode graphs: one per (bsz, key splits), captured on a private stream
@@ -366,7 +368,7 @@ int w2_splits(const llama_ctx* c, int M) { return skinny_resid_splits(M, c->a.di
 
 // Scratch of one decode step of bsz <= kSkinnyMaxRows rows whose longest row attends over ctx
 // keys, carved from `base` in the order of layout_of: the residual rows, q, the vector path's
-// fp32 operands, the MFMA path's bf16 operands (fragment-major, 32 rows with padding), the
+// fp32 operands, the MFMA path's 16-bit operands (fragment-major, 32 rows with padding), the
 // attention split partials at the split count this step takes, and the skinny residual
 // products' K-split partials.  Returns the bytes needed; fills *out when base is not null.
 size_t decode_scratch(const llama_ctx* c, int bsz, int ctx, char* base, Bufs* out) {
@@ -379,10 +381,10 @@ size_t decode_scratch(const llama_ctx* c, int bsz, int ctx, char* base, Bufs* ou
     const size_t D = c->a.dim, F = c->a.hidden_dim, nq = c->nq, B = bsz;
     const size_t h32 = take(B * D * 4), q32 = take(B * nq * 4), o32 = take(B * nq * 4), g32 = take(B * F * 4);
     const size_t rows16 = kSkinnyMaxRows;
-    const size_t act16 = c->bf16 ? take(rows16 * std::max(D, nq) * 2) : off;
-    const size_t g16 = c->bf16 ? take(rows16 * F * 2) : off;
+    const size_t act16 = c->mfma16 ? take(rows16 * std::max(D, nq) * 2) : off;
+    const size_t g16 = c->mfma16 ? take(rows16 * F * 2) : off;
     const size_t part = take(B * (size_t)c->a.n_heads * decode_splits(c, bsz, ctx) * (c->hd + 2) * 4);
-    const bool skinny = c->bf16 && bsz > kSkinnyRows;
+    const bool skinny = c->mfma16 && bsz > kSkinnyRows;
     const size_t splitk_floats = skinny ? (size_t)std::max(wo_splits(c, bsz), w2_splits(c, bsz)) * B * D : 0;
     const size_t splitk = take(splitk_floats * 4);
     if (base && out) {
@@ -394,9 +396,9 @@ size_t decode_scratch(const llama_ctx* c, int bsz, int ctx, char* base, Bufs* ou
     return off;
 }
 
-// One decode block for a bf16 model at batch > kSkinnyRows: projections on the skinny MFMA
+// One decode block for a 16-bit model at batch > kSkinnyRows: projections on the skinny MFMA
 // kernel, whose activation operands (RMSNorm output, attention output, SiLU gate) are written
-// bf16 in fragment-major order for MT = ceil(M / 16) row tiles.  The attention norm takes in
+// in the storage type, in fragment-major order for MT = ceil(M / 16) row tiles.  The attention norm takes in
 // the previous block's w2 partials, the FFN norm this block's wo partials.
 llama_status block_skinny(const llama_ctx* c, int l, int M, int start_pos, hipStream_t s,
                           const StepState* st, int graph_splits) {
@@ -411,8 +413,9 @@ llama_status block_skinny(const llama_ctx* c, int l, int M, int start_pos, hipSt
     if ((size_t)std::max(s_wo, s_w2) * M * D > c->buf.splitk_floats) return LLAMA_ERR_WORKSPACE;
 
     LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, M, D, W.attention_norm, c->a.norm_eps, act, 0, mt, s,
-                                                       part, l > 0 ? s_w2 : 0));
+                                                       part, l > 0 ? s_w2 : 0, c->wtype));
     SkinnyArgs k{};
+    k.wtype = c->wtype;
     k.x = act; k.M = M; k.K = D; k.N = c->nq + 2 * c->nk;
     k.w0 = W.wq; k.w1 = W.wk; k.w2 = W.wv;
     k.qkv = qkv_target(c, l, start_pos, 1, st);
@@ -422,18 +425,21 @@ llama_status block_skinny(const llama_ctx* c, int l, int M, int start_pos, hipSt
     if (ast != LLAMA_OK) return ast;
 
     k = SkinnyArgs{};
+    k.wtype = c->wtype;
     k.x = act; k.M = M; k.K = c->nq; k.N = D;
     k.w0 = W.wo; k.resid = h; k.ldr = D; k.ksplit = s_wo; k.part = part;
     LAUNCH(c, LLAMA_KC_GEMV_WO, s, launch_skinny(EPI_RESID, k, s));
 
     LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, M, D, W.ffn_norm, c->a.norm_eps, act, 0, mt, s,
-                                                       part, s_wo));
+                                                       part, s_wo, c->wtype));
     k = SkinnyArgs{};
+    k.wtype = c->wtype;
     k.x = act; k.M = M; k.K = D; k.N = F;
     k.w0 = W.w1; k.w1 = W.w3; k.out16 = g16; k.out_frag_mt = mt;
     LAUNCH(c, LLAMA_KC_GEMV_W13, s, launch_skinny(EPI_SWIGLU, k, s));
 
     k = SkinnyArgs{};
+    k.wtype = c->wtype;
     k.x = g16; k.M = M; k.K = F; k.N = D;
     k.w0 = W.w2; k.resid = h; k.ldr = D; k.ksplit = s_w2; k.part = part;
     LAUNCH(c, LLAMA_KC_GEMV_W2, s, launch_skinny(EPI_RESID, k, s));
@@ -441,7 +447,7 @@ llama_status block_skinny(const llama_ctx* c, int l, int M, int start_pos, hipSt
 }
 
 // One transformer block on the 16-bit MFMA path (bf16 or fp16 model) for T = bsz*seqlen prefill
-// rows (or decode rows of a large bf16 batch).
+// rows (or decode rows of a large 16-bit batch).
 llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_pos, hipStream_t s,
                         bool decode = false) {
     const llama_layer_weights& W = c->layers[l];
@@ -673,7 +679,7 @@ static llama_status decode_plan(llama_ctx* c, const int32_t* d_tokens, int64_t l
     float* h = c->buf.h32;
     HIP_TRY(launch_embed(d_tokens, ld_tokens, bsz, 1, c->w.tok_embeddings, c->wtype,
                          c->a.vocab_size, D, h, st, s, c->check_tokens ? c->err : nullptr));
-    if (c->bf16 && bsz > kSkinnyMaxRows) {
+    if (c->mfma16 && bsz > kSkinnyMaxRows) {
         // more rows than the skinny kernels take: the prefill GEMMs with the decode attention
         // (launch arguments only, so not under graph capture)
         if (st) return LLAMA_ERR_UNSUPPORTED;
@@ -683,7 +689,7 @@ static llama_status decode_plan(llama_ctx* c, const int32_t* d_tokens, int64_t l
         }
         return final_logits(c, h, D, bsz, d_logits, s);
     }
-    const bool skinny = c->bf16 && bsz > kSkinnyRows;
+    const bool skinny = c->mfma16 && bsz > kSkinnyRows;
     for (int l = 0; l < c->a.n_layers; ++l) {
         const llama_status r = skinny ? block_skinny(c, l, bsz, start_pos, s, st, graph_splits)
                                       : block_gemv(c, l, bsz, 1, start_pos, true, s, st, graph_splits);
@@ -693,8 +699,9 @@ static llama_status decode_plan(llama_ctx* c, const int32_t* d_tokens, int64_t l
     void* act = c->buf.act16;
     // the final norm takes in the last block's w2 partials
     LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, bsz, D, c->w.norm, c->a.norm_eps, act, 0, (bsz + 15) / 16, s,
-                                                       c->buf.splitk, w2_splits(c, bsz)));
+                                                       c->buf.splitk, w2_splits(c, bsz), c->wtype));
     SkinnyArgs k{};
+    k.wtype = c->wtype;
     k.x = act; k.M = bsz; k.K = D; k.N = c->a.vocab_size;
     k.w0 = c->w.output; k.out = d_logits; k.ldo = c->a.vocab_size; k.st = st;
     LAUNCH(c, LLAMA_KC_GEMV_OUT, s, launch_skinny(EPI_STORE, k, s));
@@ -741,7 +748,7 @@ llama_status llama_decode_step(llama_ctx* c, const int32_t* d_tokens, int64_t ld
         HIP_TRY(launch_clear_flag(c->err, s));
         return finish_token_check(c, decode_plan(c, d_tokens, ld_tokens, bsz, start_pos, d_logits, s, nullptr, 0), s);
     }
-    if (!c->use_graphs || c->prof_class != 0 || (c->bf16 && bsz > kSkinnyMaxRows))
+    if (!c->use_graphs || c->prof_class != 0 || (c->mfma16 && bsz > kSkinnyMaxRows))
         return decode_plan(c, d_tokens, ld_tokens, bsz, start_pos, d_logits, s, nullptr, 0);
     // graph replay: per-step values go to the device step state, then one graph launch
     const int splits = decode_splits(c, bsz, start_pos + 1);

@@ -1,4 +1,5 @@
-// Weight-streaming products for a few activation rows on bf16 MFMA (decode with batch > 4).
+// Weight-streaming products for a few activation rows on 16-bit MFMA (decode with batch > 4;
+// bf16 or fp16, the storage type T16 of the weights and the 16-bit activations).
 //
 // y[m][n] = sum_k x[m][k] * W[n][k] for M <= 32 rows.  The vector-ALU GEMV would spend M FMAs
 // per weight element; here the weights are the MFMA A operand (16 output rows) and the
@@ -28,7 +29,6 @@
 namespace llk {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
@@ -36,10 +36,14 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 constexpr int kSkBK = 64;          // k per stage: 128 bytes of every row
 constexpr int kSkWBytes = 2048;    // one matrix's stage for one wave: 16 rows x 128 bytes
 
-__device__ __forceinline__ bf16x8_t frag(const uint4& v) {
-    return __builtin_bit_cast(bf16x8_t, u32x4_t{v.x, v.y, v.z, v.w});
+template <typename T16>
+__device__ __forceinline__ typename Mma<T16>::v8 frag(const uint4& v) {
+    return __builtin_bit_cast(typename Mma<T16>::v8, u32x4_t{v.x, v.y, v.z, v.w});
 }
-__device__ __forceinline__ bf16x8_t frag(const u32x4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
+template <typename T16>
+__device__ __forceinline__ typename Mma<T16>::v8 frag(const u32x4_t& v) {
+    return __builtin_bit_cast(typename Mma<T16>::v8, v);
+}
 
 // Byte offset, inside a block of 8 rows x 128 bytes, of 16-byte chunk c of row r.
 __device__ __forceinline__ int sk_slot(int r, int c) { return (8 * r + (c ^ r)) * 16; }
@@ -69,7 +73,7 @@ __device__ __forceinline__ const uint16_t* sk_row(const SkinnyArgs& a, int w, in
 }
 
 // Epilogue of one 16 x 16 result tile: acc[w][e] = y[m][n = nb + 4g + e] of matrix w.
-template <int NW, int EPI>
+template <typename T16, int NW, int EPI>
 __device__ __forceinline__ void sk_epilogue(const SkinnyArgs& a, const f32x4 (&acc)[NW], int m, int nb, int g) {
     if (m >= a.M) return;
     if (EPI == EPI_QKV) {
@@ -89,14 +93,14 @@ __device__ __forceinline__ void sk_epilogue(const SkinnyArgs& a, const f32x4 (&a
                 y1 = r1;
             }
             if (n < q.nq) {
-                q.q[(size_t)m * q.nq + n] = round_bf16(y0);
-                q.q[(size_t)m * q.nq + n + 1] = round_bf16(y1);
+                q.q[(size_t)m * q.nq + n] = Mma<T16>::round(y0);
+                q.q[(size_t)m * q.nq + n + 1] = Mma<T16>::round(y1);
             } else {
                 const bool is_k = n < q.nq + q.nk;
                 const int c = is_k ? n - q.nq : n - q.nq - q.nk;
                 uint16_t* cache = static_cast<uint16_t*>(is_k ? q.cache_k : q.cache_v);
                 *reinterpret_cast<uint32_t*>(cache + ((size_t)b * q.max_seq + pos) * (size_t)q.nk + c) =
-                    pack_bf16x2(y0, y1);
+                    Mma<T16>::pack2(y0, y1);
             }
         }
     } else {
@@ -111,7 +115,7 @@ __device__ __forceinline__ void sk_epilogue(const SkinnyArgs& a, const f32x4 (&a
                     a.resid[(size_t)m * a.ldr + n] += acc[0][e];
             } else if (EPI == EPI_SWIGLU) {
                 const size_t o = a.out_frag_mt ? frag_index(m, n, a.out_frag_mt) : (size_t)m * a.ldo + n;
-                static_cast<uint16_t*>(a.out16)[o] = f32_to_bf16(silu(acc[0][e]) * acc[NW - 1][e]);
+                static_cast<uint16_t*>(a.out16)[o] = Mma<T16>::bits(silu(acc[0][e]) * acc[NW - 1][e]);
             } else {
                 (a.st ? a.st->logits : a.out)[(size_t)m * a.ldo + n] = acc[0][e];
             }
@@ -119,7 +123,7 @@ __device__ __forceinline__ void sk_epilogue(const SkinnyArgs& a, const f32x4 (&a
     }
 }
 
-template <int NW, int NT, int MT, int EPI, int D, int NWV>
+template <typename T16, int NW, int NT, int MT, int EPI, int D, int NWV>
 __global__ __launch_bounds__(64 * NWV) void skinny_kernel(SkinnyArgs a) {
     constexpr int NB = NT * NW;                   // weight blocks (16 rows each) per stage
     constexpr int kStage = NB * kSkWBytes;        // one wave's ring slot
@@ -202,7 +206,7 @@ __global__ __launch_bounds__(64 * NWV) void skinny_kernel(SkinnyArgs a) {
             for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
-                    acc[b][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag(ra[b][j]), frag(xr[u][j][t]), acc[b][t], 0, 0, 0);
+                    acc[b][t] = Mma<T16>::mma(frag<T16>(ra[b][j]), frag<T16>(xr[u][j][t]), acc[b][t]);
     };
 
 #pragma unroll
@@ -240,13 +244,13 @@ __global__ __launch_bounds__(64 * NWV) void skinny_kernel(SkinnyArgs a) {
 #pragma unroll
         for (int q = 0; q < NWV; ++q) sum[w] += red[((q * NB + tb * NW + w) * MT + tm) * 64 + lane];
     }
-    sk_epilogue<NW, EPI>(a, sum, 16 * tm + fr, n0 + 16 * tb, g);
+    sk_epilogue<T16, NW, EPI>(a, sum, 16 * tm + fr, n0 + 16 * tb, g);
 }
 
-template <int NW, int NT, int MT, int EPI, int D, int NWV>
+template <typename T16, int NW, int NT, int MT, int EPI, int D, int NWV>
 hipError_t launch_waves(const SkinnyArgs& a, hipStream_t s) {
     const dim3 grid((a.N + 16 * NT - 1) / (16 * NT), EPI == EPI_RESID && a.ksplit > 1 ? a.ksplit : 1);
-    launch_kernel((skinny_kernel<NW, NT, MT, EPI, D, NWV>), grid, dim3(64 * NWV), 0, s, a);
+    launch_kernel((skinny_kernel<T16, NW, NT, MT, EPI, D, NWV>), grid, dim3(64 * NWV), 0, s, a);
     return hipGetLastError();
 }
 
@@ -262,24 +266,24 @@ hipError_t launch_waves(const SkinnyArgs& a, hipStream_t s) {
 //    13B ones at 16 filled half the chip or less): 4 waves, NT = 1 for up to 16 rows, NT = 2
 //    for more (7B w2 at 32 rows 27.8 -> 21.6 us, 13B wo at 16 rows 19.5 -> 15.7 us).
 // The LDS of a workgroup stays at or under 128 KB.
-template <int EPI>
+template <typename T16, int EPI>
 hipError_t launch_epi(const SkinnyArgs& a, hipStream_t s) {
     const int tiles = (a.N + 15) / 16;
     const bool m16 = a.M <= 16;     // one 16-row batch tile (MT = 1) or two
     if constexpr (EPI == EPI_RESID) {
-        if (a.ksplit > 1) return m16 ? launch_waves<1, 1, 1, EPI, 4, 4>(a, s) : launch_waves<1, 2, 2, EPI, 4, 4>(a, s);
+        if (a.ksplit > 1) return m16 ? launch_waves<T16, 1, 1, 1, EPI, 4, 4>(a, s) : launch_waves<T16, 1, 2, 2, EPI, 4, 4>(a, s);
     }
     if constexpr (EPI == EPI_SWIGLU) {
-        if (tiles >= 512) return m16 ? launch_waves<2, 1, 1, EPI, 4, 4>(a, s) : launch_waves<2, 1, 2, EPI, 4, 4>(a, s);
-        return m16 ? launch_waves<2, 1, 1, EPI, 4, 8>(a, s) : launch_waves<2, 1, 2, EPI, 4, 8>(a, s);
+        if (tiles >= 512) return m16 ? launch_waves<T16, 2, 1, 1, EPI, 4, 4>(a, s) : launch_waves<T16, 2, 1, 2, EPI, 4, 4>(a, s);
+        return m16 ? launch_waves<T16, 2, 1, 1, EPI, 4, 8>(a, s) : launch_waves<T16, 2, 1, 2, EPI, 4, 8>(a, s);
     } else {
         if (tiles >= 640) {
-            if (m16) return launch_waves<1, 4, 1, EPI, 4, 4>(a, s);
+            if (m16) return launch_waves<T16, 1, 4, 1, EPI, 4, 4>(a, s);
             // about one workgroup per CU: 3 row blocks, 8 waves, a 2-slot ring each
-            if (tiles <= 1024) return launch_waves<1, 3, 2, EPI, 2, 8>(a, s);
-            return launch_waves<1, 2, 2, EPI, 4, 4>(a, s);
+            if (tiles <= 1024) return launch_waves<T16, 1, 3, 2, EPI, 2, 8>(a, s);
+            return launch_waves<T16, 1, 2, 2, EPI, 4, 4>(a, s);
         }
-        return m16 ? launch_waves<1, 2, 1, EPI, 4, 8>(a, s) : launch_waves<1, 1, 2, EPI, 6, 4>(a, s);
+        return m16 ? launch_waves<T16, 1, 2, 1, EPI, 4, 8>(a, s) : launch_waves<T16, 1, 1, 2, EPI, 6, 4>(a, s);
     }
 }
 
@@ -294,11 +298,20 @@ int skinny_resid_splits(int M, int N, int K) {
 hipError_t launch_skinny(int epi, const SkinnyArgs& a, hipStream_t s) {
     if (a.M < 1 || a.M > 32 || a.K % kSkBK != 0 || a.K < kSkBK) return hipErrorInvalidValue;
     if (a.ksplit > 1 && (epi != EPI_RESID || !a.part || a.ksplit > a.K / kSkBK)) return hipErrorInvalidValue;
+    if (a.wtype == kStoreF16) {
+        switch (epi) {
+            case EPI_QKV: return launch_epi<f16, EPI_QKV>(a, s);
+            case EPI_RESID: return launch_epi<f16, EPI_RESID>(a, s);
+            case EPI_SWIGLU: return launch_epi<f16, EPI_SWIGLU>(a, s);
+            default: return launch_epi<f16, EPI_STORE>(a, s);
+        }
+    }
+    if (a.wtype != kStoreBf16) return hipErrorInvalidValue;
     switch (epi) {
-        case EPI_QKV: return launch_epi<EPI_QKV>(a, s);
-        case EPI_RESID: return launch_epi<EPI_RESID>(a, s);
-        case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(a, s);
-        default: return launch_epi<EPI_STORE>(a, s);
+        case EPI_QKV: return launch_epi<bf16, EPI_QKV>(a, s);
+        case EPI_RESID: return launch_epi<bf16, EPI_RESID>(a, s);
+        case EPI_SWIGLU: return launch_epi<bf16, EPI_SWIGLU>(a, s);
+        default: return launch_epi<bf16, EPI_STORE>(a, s);
     }
 }
 

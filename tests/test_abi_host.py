@@ -66,12 +66,14 @@ def test_check_args(lib, kw, expect):
     assert (abi.llama_workspace_bytes(a) > 0) == (expect == abi.LLAMA_OK)
 
 
-def test_fp16_models_take_two_byte_caches_on_the_vector_path(lib):
-    """An fp16 model's workspace is the fp32 model's with the KV cache at 2 bytes an element:
-    K and V, 4 layers x 2 rows x 128 positions x 2 kv heads x 32 dims, 2 bytes fewer each."""
+def test_fp16_models_take_the_bf16_workspace_layout(lib):
+    """An fp16 model runs the bf16 model's kernels (MFMA prefill, 16-bit operands, split-K
+    partials) with the other 16-bit type, so its workspace is the bf16 one byte for byte; the
+    fp32 model keeps fp32 activations for every prefill row and a 4-byte cache instead."""
     f32 = abi.llama_workspace_bytes(tiny(dtype="fp32"))
     f16 = abi.llama_workspace_bytes(tiny(dtype="fp16"))
-    assert f32 - f16 == 2 * 4 * 2 * 128 * 2 * 32 * 2
+    b16 = abi.llama_workspace_bytes(tiny(dtype="bf16"))
+    assert f16 == b16 and f16 != f32 and f16 > 0
     bad = tiny()
     bad.dtype = 3
     assert abi.llama_check_args(bad) == abi.LLAMA_ERR_INVALID_ARG

@@ -352,7 +352,9 @@ SMALL_BF16 = {
 
 # ----------------------------------------------------------------------------- fp16 models
 
-# fp16 (the reference's dtype) runs the vector path with every 16-bit storage point rounded to
+# fp16 (the reference's dtype) takes the same kernels as bf16 (vector path at decode batch <= 4,
+# skinny MFMA products at 5..32 rows, MFMA GEMMs for prefill and above 32 rows; only the GQA
+# decode attention stays on the vector kernel) with every 16-bit storage point rounded to
 # binary16.  Its 11 significant bits are 3 more than bf16's, so the bar is the stated bf16 bar
 # scaled by the ulp ratio, 2^-3.
 FP16_TOL = BF16_TOL / 8
@@ -361,12 +363,23 @@ FP16 = {
     "gqa": synth.WORKLOADS["tiny_fp32"].with_(name="tiny_fp16_gqa", dtype="fp16", batch=3,
                                               prompt_len=0, prompt_len_range=(8, 40), gen_steps=16,
                                               weight_seed=19, prompt_seed=119, max_seq_len=96),
-    # 6 decode rows (bf16 would take the skinny MFMA products; fp16 stays on the vector path),
-    # MHA with head_dim 64
+    # 6 decode rows on the skinny fp16 MFMA products, MHA with head_dim 64
     "mha_b6": synth.WORKLOADS["tiny_fp32"].with_(name="tiny_fp16_mha_b6", dtype="fp16", n_heads=8,
                                                  n_kv_heads=8, dim=512, hidden_dim=1536, vocab_size=1000,
                                                  batch=6, prompt_len=0, prompt_len_range=(12, 50),
                                                  gen_steps=12, weight_seed=20, prompt_seed=120, max_seq_len=96),
+    # 20 decode rows with wo and w2 split over K (the partials of a second, 4-row tile added by
+    # the next RMSNorm), GQA 8:1 with head_dim 128 on the vector decode attention
+    "b20": synth.WORKLOADS["tiny_fp32"].with_(name="tiny_fp16_b20", dtype="fp16", n_heads=8,
+                                              n_kv_heads=1, dim=1024, hidden_dim=2816, vocab_size=1000,
+                                              batch=20, prompt_len=0, prompt_len_range=(10, 30),
+                                              gen_steps=10, weight_seed=22, prompt_seed=122, max_seq_len=64),
+    # 40 decode rows: more than the skinny kernels take, so decode runs the prefill GEMMs with
+    # the decode attention (and its key splits merged into fp16 operands)
+    "b40": synth.WORKLOADS["tiny_fp32"].with_(name="tiny_fp16_b40", dtype="fp16", n_heads=8,
+                                              n_kv_heads=4, dim=512, hidden_dim=1536, vocab_size=1000,
+                                              batch=40, prompt_len=0, prompt_len_range=(8, 24),
+                                              gen_steps=8, weight_seed=23, prompt_seed=123, max_seq_len=48),
 }
 
 
@@ -395,12 +408,14 @@ def test_llama2_7b_b1_fp16_generate_matches_oracle():
     check_generate_rows(wl, W, prompts, tokens, logits, [0], storage="fp16", stated=FP16_TOL)
 
 
-@pytest.mark.parametrize("widths,batch", [("llama2_7b_b1_fp16", 2), ("llama2_13b_b16", 1)])
+@pytest.mark.parametrize("widths,batch", [("llama2_7b_b1_fp16", 2), ("llama2_7b_b1_fp16", 8), ("llama2_13b_b16", 1)])
 def test_fp16_full_width_one_layer_generate_matches_oracle(widths, batch):
-    """One fp16 layer at full width: 7B at two rows (the two-row GEMV), 13B at one row (dim
-    5120 > one 4096-element segment: the fused norm's statistics take a pass of their own)."""
+    """One fp16 layer at full width: 7B at two rows (the two-row GEMV) and at eight (the skinny
+    fp16 MFMA products, wo and w2 split over K), 13B at one row (dim 5120 > one 4096-element
+    segment: the fused norm's statistics take a pass of their own)."""
+    plen, gen = (96, 24) if batch <= 4 else (48, 12)
     wl = synth.WORKLOADS[widths].with_(name=f"{widths}_fp16_one_layer_b{batch}", dtype="fp16", n_layers=1,
-                                       batch=batch, prompt_len=96, gen_steps=24, prompt_seed=140 + batch)
+                                       batch=batch, prompt_len=plen, gen_steps=gen, prompt_seed=140 + batch)
     say(f"case {wl.name}")
     W = synth.gen_weights(wl, device="cuda")
     prompts = synth.prompts(wl)
@@ -545,12 +560,13 @@ def test_llama2_7b_widths_one_layer_chunked_prefill_all_positions():
                  passes["plain"].reshape(-1, V))
 
 
-@pytest.mark.parametrize("name", ["gqa8", "mha", "b6", "b20", "fp16_mha_b6", "tiny_fp32"])
+@pytest.mark.parametrize("name", ["gqa8", "mha", "b6", "b20", "fp16_mha_b6", "fp16_b20", "tiny_fp32"])
 def test_decode_graph_replays_match_eager_launches(name):
     """Decode steps replay one captured graph per split count; the generate loop puts eager
     work (argmax, select, step-state writes) between replays.  Every replay's logits must
     equal the eagerly launched step bit for bit (same kernels, same arithmetic).  Cases: bf16
-    on the vector and skinny paths (b20: with the wo/w2 K split), fp16 and fp32 models."""
+    on the vector and skinny paths (b20: with the wo/w2 K split), fp16 on the skinny path, and
+    fp32 models."""
     if name in SMALL_BF16:
         wl = SMALL_BF16[name]
     elif name.startswith("fp16_"):
