@@ -303,9 +303,14 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
     const int n_tn = (a.N + ncols - 1) / ncols, n_tm = (a.M + BM - 1) / BM;
     const int per_xcd = (n_tn * n_tm + kXcds - 1) / kXcds;
     const dim3 grid(per_xcd * kXcds, 1, splits);
+    if (a.deferred) *a.deferred = 0;
     launch_kernel((gemm_kernel<T16, BM, BN, WGM, WGN, EPI>), grid, dim3(64 * WGM * WGN), 0, s, a, n_tm, n_tn);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
+    if (a.deferred && splits <= kMaxNormFold) {   // partials [splits][M][N], folded by the next norm
+        *a.deferred = splits;
+        return hipSuccess;
+    }
     const size_t n = (size_t)a.M * a.N;
     launch_kernel(splitk_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                   a.part, splits, a.M, a.N, (int64_t)a.N, a.resid, a.ldr);
@@ -659,6 +664,7 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
         splits = std::min(splits, kMaxBigSplit);
         while (splits > 1 && (size_t)splits * a.M * ldp > a.part_cap) --splits;
     }
+    if (a.deferred) *a.deferred = 0;
     launch_kernel((gemm_big_kernel<T16, BM, EPI>), dim3(per_xcd * kXcds, 1, splits), dim3(512), 0, s, a,
                   n_tm, n_tn);
     hipError_t e = hipGetLastError();
@@ -666,6 +672,10 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
     const size_t n = (size_t)a.M * a.N;
     const dim3 rgrid((unsigned)((n + 255) / 256));
     if constexpr (EPI == EPI_RESID) {
+        if (a.deferred && ldp == (size_t)a.N && splits <= kMaxNormFold) {   // [splits][M][N]: the next norm folds them
+            *a.deferred = splits;
+            return hipSuccess;
+        }
         launch_kernel(splitk_reduce_kernel, rgrid, dim3(256), 0, s, a.part, splits, a.M, a.N,
                       (int64_t)ldp, a.resid, a.ldr);
     } else if constexpr (EPI == EPI_SWIGLU) {
@@ -714,13 +724,18 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
                 }
             }
             if (best_t > 0) {
+                // two launches over row ranges: each adds its result to resid itself (deferred
+                // partials must cover every row of the product in one [splits][M][N] block)
+                if (a.deferred) *a.deferred = 0;
                 const int M1 = (n_tm - best_t) * 256, M2 = a.M - M1;
                 GemmArgs a1 = a;
                 a1.M = M1;
+                a1.deferred = nullptr;
                 const hipError_t e = launch_big<T16, 256, EPI>(a1, s);
                 if (e != hipSuccess) return e;
                 GemmArgs a2 = a;
                 a2.M = M2;
+                a2.deferred = nullptr;
                 a2.a = static_cast<const uint16_t*>(a.a) + (size_t)M1 * a.lda;
                 if constexpr (EPI == EPI_RESID) a2.resid = a.resid + (size_t)M1 * a.ldr;
                 if constexpr (EPI == EPI_SWIGLU) a2.out16 = static_cast<uint16_t*>(a.out16) + (size_t)M1 * a.ldo16;

@@ -89,6 +89,11 @@ struct GemmArgs {
     int splits;            // K splits of the small-tile residual GEMM: partials [splits][M][N]
     float* part;           // split-K partials (also used by short prefills on the LDS-ring kernel)
     size_t part_cap;       // floats available at `part`
+    // RESID only, host pointer: if set, a product split over K leaves its fp32 partials
+    // [splits][M][N] at `part` instead of adding them to resid, and stores the split count
+    // here (0 when it added its result to resid itself); the caller has the RMSNorm that
+    // follows fold them in (launch_rmsnorm_bf16's part / nsplit).
+    int* deferred;
     int wtype = kStoreBf16;
 };
 
@@ -164,7 +169,7 @@ hipError_t launch_set_step(StepState* st, int pos, int64_t ld, const int32_t* to
 // nsplit > 1 (at most kMaxNormFold): h[r] += part[0][r] + ... + part[nsplit-1][r] first (the
 // K-split partials [nsplit][rows][dim] of the residual product that precedes the norm),
 // written back to h.
-constexpr int kMaxNormFold = 4;
+constexpr int kMaxNormFold = 16;
 hipError_t launch_rmsnorm_bf16(float* h, int64_t ldh, int rows, int dim, const void* w,
                                float eps, void* out, int64_t ldo, int frag_mt, hipStream_t s,
                                const float* part = nullptr, int nsplit = 0, int wtype = kStoreBf16);

@@ -447,16 +447,25 @@ llama_status block_skinny(const llama_ctx* c, int l, int M, int start_pos, hipSt
 }
 
 // One transformer block on the 16-bit MFMA path (bf16 or fp16 model) for T = bsz*seqlen prefill
-// rows (or decode rows of a large 16-bit batch).
+// rows (or decode rows of a large 16-bit batch).  Residual products split over K (short
+// prefills) leave their partials for the RMSNorm that follows to fold into h: wo's for the FFN
+// norm; w2's for the next block's attention norm.  *pending: in, the K splits of the previous
+// block's w2 partials (0: none); out, this block's (0 for the last block, whose w2 adds its
+// result itself: the final norm reads h directly).
 llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_pos, hipStream_t s,
-                        bool decode = false) {
+                        int* pending, bool decode = false) {
     const llama_layer_weights& W = c->layers[l];
     const int D = c->a.dim, F = c->a.hidden_dim;
     float* h = c->buf.h32;
     void* act = c->buf.act16;
     void* g16 = c->buf.g16;
 
-    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.attention_norm, c->a.norm_eps, act, D, 0, s, nullptr, 0, c->wtype));
+    // deferred partials are [splits][T][dim] in the split-K region
+    auto fits = [&](int parts) { return (size_t)parts * T * D <= c->buf.splitk_floats; };
+    if (!fits(*pending)) return LLAMA_ERR_WORKSPACE;
+    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.attention_norm, c->a.norm_eps, act, D, 0, s,
+                                                       *pending > 0 ? c->buf.splitk : nullptr, *pending, c->wtype));
+    *pending = 0;
     GemmArgs g{};
     g.wtype = c->wtype;
     g.a = act; g.lda = D; g.M = T; g.K = D; g.N = c->nq + 2 * c->nk;
@@ -495,9 +504,13 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
     g.a = act; g.lda = c->nq; g.M = T; g.K = c->nq; g.N = D;
     g.w0 = W.wo; g.resid = h; g.ldr = D;
     g.splits = residual_splits(c, T, c->nq); g.part = c->buf.splitk; g.part_cap = c->buf.splitk_floats;
+    int wo_parts = 0;
+    g.deferred = &wo_parts;
     LAUNCH(c, LLAMA_KC_GEMM_WO, s, launch_gemm(EPI_RESID, g, s));
 
-    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.ffn_norm, c->a.norm_eps, act, D, 0, s, nullptr, 0, c->wtype));
+    if (!fits(wo_parts)) return LLAMA_ERR_WORKSPACE;
+    LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(h, D, T, D, W.ffn_norm, c->a.norm_eps, act, D, 0, s,
+                                                       wo_parts > 0 ? c->buf.splitk : nullptr, wo_parts, c->wtype));
     g = GemmArgs{};
     g.wtype = c->wtype;
     g.a = act; g.lda = D; g.M = T; g.K = D; g.N = F;
@@ -510,6 +523,7 @@ llama_status block_mfma(const llama_ctx* c, int l, int T, int seqlen, int start_
     g.a = g16; g.lda = F; g.M = T; g.K = F; g.N = D;
     g.w0 = W.w2; g.resid = h; g.ldr = D;
     g.splits = residual_splits(c, T, F); g.part = c->buf.splitk; g.part_cap = c->buf.splitk_floats;
+    if (l + 1 < c->a.n_layers) g.deferred = pending;
     LAUNCH(c, LLAMA_KC_GEMM_W2, s, launch_gemm(EPI_RESID, g, s));
     return LLAMA_OK;
 }
@@ -653,8 +667,9 @@ static llama_status prefill_plan(llama_ctx* c, const int32_t* d_tokens, int64_t 
     float* h = c->buf.h32;
     HIP_TRY(launch_embed(d_tokens, ld_tokens, bsz, seqlen, c->w.tok_embeddings, c->wtype,
                          c->a.vocab_size, D, h, nullptr, s, c->check_tokens ? c->err : nullptr));
+    int pending = 0;   // K splits of the last w2 partials not yet folded into h
     for (int l = 0; l < c->a.n_layers; ++l) {
-        const llama_status st = c->mfma16 ? block_mfma(c, l, T, seqlen, start_pos, s)
+        const llama_status st = c->mfma16 ? block_mfma(c, l, T, seqlen, start_pos, s, &pending)
                                           : block_gemv(c, l, T, seqlen, start_pos, false, s);
         if (st != LLAMA_OK) return st;
     }
@@ -683,8 +698,9 @@ static llama_status decode_plan(llama_ctx* c, const int32_t* d_tokens, int64_t l
         // more rows than the skinny kernels take: the prefill GEMMs with the decode attention
         // (launch arguments only, so not under graph capture)
         if (st) return LLAMA_ERR_UNSUPPORTED;
+        int pending = 0;
         for (int l = 0; l < c->a.n_layers; ++l) {
-            const llama_status r = block_mfma(c, l, bsz, 1, start_pos, s, true);
+            const llama_status r = block_mfma(c, l, bsz, 1, start_pos, s, &pending, true);
             if (r != LLAMA_OK) return r;
         }
         return final_logits(c, h, D, bsz, d_logits, s);

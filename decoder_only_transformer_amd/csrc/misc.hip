@@ -152,6 +152,69 @@ __global__ __launch_bounds__(256) void rmsnorm_reg_kernel(float* h, int64_t ldh,
     }
 }
 
+// Same, for rows of at most 8192 elements that first take in nsplit <= NSM K-split partials
+// (the split-K residual products of short prefills: up to 16 splits of a few hundred rows).
+// One 1024-thread workgroup per row, two float4 positions per thread at most; all partial
+// loads of a position are issued before the first is added (splits past nsplit re-read the
+// last one and are not added), so the row costs one memory round trip.  Partials are summed
+// in split order and then added to h, as the reduce pass of the products does.
+template <typename T16, int NSM>
+__global__ __launch_bounds__(1024) void rmsnorm_fold_kernel(float* h, int64_t ldh, int dim, const T16* w,
+                                                           float eps, uint16_t* out, int64_t ldo, int frag_mt,
+                                                           const float* part, int nsplit) {
+    __shared__ double red[16];
+    const int rows = gridDim.x, row = blockIdx.x;
+    float* x = h + (size_t)row * ldh;
+    float4 v[2];
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int k = (threadIdx.x + 1024 * i) * 4;
+        v[i] = float4{0.f, 0.f, 0.f, 0.f};
+        if (k < dim) {
+            float4 q[NSM];
+#pragma unroll
+            for (int sp = 0; sp < NSM; ++sp) {
+                const int z = min(sp, nsplit - 1);
+                q[sp] = *reinterpret_cast<const float4*>(part + ((size_t)z * rows + row) * dim + k);
+            }
+            float4 hv = *reinterpret_cast<const float4*>(x + k);
+            float4 t = q[0];
+#pragma unroll
+            for (int sp = 1; sp < NSM; ++sp) {
+                if (sp < nsplit) {
+                    t.x += q[sp].x; t.y += q[sp].y; t.z += q[sp].z; t.w += q[sp].w;
+                }
+            }
+            hv.x += t.x; hv.y += t.y; hv.z += t.z; hv.w += t.w;
+            *reinterpret_cast<float4*>(x + k) = hv;
+            v[i] = hv;
+        }
+        ss += sq64(v[i].x) + sq64(v[i].y) + sq64(v[i].z) + sq64(v[i].w);
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    double tot = 0.0;
+#pragma unroll
+    for (int wv = 0; wv < 16; ++wv) tot += red[wv];
+    const float den = sqrtf((float)(tot / (double)dim) + eps);
+    const float rcp = 1.0f / den;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int k = (threadIdx.x + 1024 * i) * 4;
+        if (k >= dim) continue;
+        const uint2 wv = *reinterpret_cast<const uint2*>(w + k);
+        uint2 p;
+        p.x = Mma<T16>::pack2(div_rn(v[i].x, den, rcp) * Elem<T16>::lo(wv.x),
+                              div_rn(v[i].y, den, rcp) * Elem<T16>::hi(wv.x));
+        p.y = Mma<T16>::pack2(div_rn(v[i].z, den, rcp) * Elem<T16>::lo(wv.y),
+                              div_rn(v[i].w, den, rcp) * Elem<T16>::hi(wv.y));
+        const size_t o = frag_mt ? frag_index(row, k, frag_mt) : (size_t)row * ldo + k;
+        *reinterpret_cast<uint2*>(out + o) = p;
+    }
+}
+
 // Better of two (value, index) candidates: larger value wins, ties -> lower index, NaN never wins.
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
     if (i2 < 0) return;
@@ -323,7 +386,17 @@ template <typename T16>
 void launch_rmsnorm16(float* h, int64_t ldh, int rows, int dim, const void* w, float eps, uint16_t* o, int64_t ldo,
                       int frag_mt, hipStream_t s, const float* part, int nsplit) {
     const T16* wb = static_cast<const T16*>(w);
-    if (dim > 8192 || nsplit > 2)
+    if (nsplit > 2 && dim <= 8192) {
+        if (nsplit <= 4)
+            launch_kernel((rmsnorm_fold_kernel<T16, 4>), dim3(rows), dim3(1024), 0, s, h, ldh, dim, wb, eps, o, ldo,
+                          frag_mt, part, nsplit);
+        else if (nsplit <= 8)
+            launch_kernel((rmsnorm_fold_kernel<T16, 8>), dim3(rows), dim3(1024), 0, s, h, ldh, dim, wb, eps, o, ldo,
+                          frag_mt, part, nsplit);
+        else
+            launch_kernel((rmsnorm_fold_kernel<T16, 16>), dim3(rows), dim3(1024), 0, s, h, ldh, dim, wb, eps, o, ldo,
+                          frag_mt, part, nsplit);
+    } else if (dim > 8192 || nsplit > 2)
         launch_kernel(rmsnorm_bf16_kernel<T16>, dim3(rows), dim3(256), 0, s, h, ldh, dim, wb, eps, o, ldo, frag_mt,
                       part, nsplit);
     else if (nsplit == 2)

@@ -645,8 +645,9 @@ def test_llama2_7b_widths_one_layer_tail_rows_match_oracle():
     """33 x 256 prefill rows at the 7B widths: the 256x256 tiles of the first 8192 rows fill
     whole rounds of one tile per CU, so the last 256 rows of every projection (q/k/v with
     RoPE and the cache append, wo and w2 with the residual add, the SiLU gate) run on the
-    split-K path with its reduce passes.  The first and the last batch row (all of whose
-    prompt rows are in that tail) are checked against the oracle."""
+    split-K path with its reduce passes (a product launched in two row ranges adds its results
+    itself rather than leaving partials for the next norm).  The first and the last batch row
+    (all of whose prompt rows are in that tail) are checked against the oracle."""
     wl = synth.WORKLOADS["llama2_7b_b1"].with_(name="llama2_7b_b33_one_layer", n_layers=1, batch=33,
                                                prompt_len=256, gen_steps=4)
     say(f"case {wl.name}")
