@@ -673,7 +673,22 @@ static llama_status prefill_plan(llama_ctx* c, const int32_t* d_tokens, int64_t 
                                           : block_gemv(c, l, T, seqlen, start_pos, false, s);
         if (st != LLAMA_OK) return st;
     }
-    if (!all_positions) return final_logits(c, h + (size_t)(seqlen - 1) * D, (int64_t)seqlen * D, bsz, d_logits, s);
+    float* last = h + (size_t)(seqlen - 1) * D;   // the last position of every row, seqlen * D apart
+    if (!all_positions && c->mfma16 && bsz > kSkinnyRows && bsz <= kSkinnyMaxRows) {
+        // 5..32 rows: the norm to fragment-major 16-bit operands and the vocab product on the
+        // skinny MFMA kernel, which streams the output matrix once (the vector GEMV would
+        // stream it once per 4 rows)
+        void* act = c->buf.act16;
+        LAUNCH(c, LLAMA_KC_RMSNORM, s, launch_rmsnorm_bf16(last, (int64_t)seqlen * D, bsz, D, c->w.norm, c->a.norm_eps,
+                                                           act, 0, (bsz + 15) / 16, s, nullptr, 0, c->wtype));
+        SkinnyArgs k{};
+        k.wtype = c->wtype;
+        k.x = act; k.M = bsz; k.K = D; k.N = c->a.vocab_size;
+        k.w0 = c->w.output; k.out = d_logits; k.ldo = c->a.vocab_size;
+        LAUNCH(c, LLAMA_KC_GEMV_OUT, s, launch_skinny(EPI_STORE, k, s));
+        return LLAMA_OK;
+    }
+    if (!all_positions) return final_logits(c, last, (int64_t)seqlen * D, bsz, d_logits, s);
     if (!c->mfma16) return final_logits(c, h, D, T, d_logits, s);
     void* act = c->buf.act16;
     HIP_TRY(launch_rmsnorm_bf16(h, D, T, D, c->w.norm, c->a.norm_eps, act, D, 0, s, nullptr, 0, c->wtype));
