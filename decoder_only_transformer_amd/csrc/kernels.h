@@ -83,7 +83,7 @@ struct GemmArgs {
     int M, K, N;           // N = output columns (SWIGLU: hidden units)
     const void* w0; const void* w1; const void* w2;
     float* out; int64_t ldo;       // STORE (fp32)
-    void* out16; int64_t ldo16;    // SWIGLU (bf16)
+    void* out16; int64_t ldo16;    // SWIGLU (16-bit, wtype)
     float* resid; int64_t ldr;
     QkvTarget qkv;
     int splits;            // K splits of the small-tile residual GEMM: partials [splits][M][N]
@@ -105,7 +105,7 @@ struct SkinnyArgs {
     const void* x;
     int M, K, N;           // N = output rows (SWIGLU: hidden units)
     const void* w0; const void* w1; const void* w2;
-    float* out; void* out16; int64_t ldo;   // STORE (fp32) / SWIGLU (bf16)
+    float* out; void* out16; int64_t ldo;   // STORE (fp32) / SWIGLU (16-bit, wtype)
     int out_frag_mt;       // SWIGLU: > 0 writes out16 fragment-major for that many row tiles
     float* resid; int64_t ldr;
     int ksplit;            // RESID: > 1 splits K over gridDim.y, each split writing its sum
@@ -123,7 +123,7 @@ struct AttnArgs {
     const void* cache_v;
     void* out;             // [rows][n_heads*hd], fp32, or 16-bit (out_bf16: the cache's storage
     int out_bf16;          //   type, bf16 or fp16)
-    int out_frag_mt;       // bf16 out: > 0 writes it fragment-major for that many row tiles
+    int out_frag_mt;       // 16-bit out: > 0 writes it fragment-major for that many row tiles
     float* part;           // [rows][n_heads][n_split][hd + 2] partials when n_split > 1
     int rows, n_heads, n_kv_heads, head_dim, max_seq;
     int row0;              // first row of this launch (launches are split at 65535 rows)

@@ -125,7 +125,7 @@ Layout layout_of(const llama_args& a) {
     L.q32 = take(maxT * nq * sizeof(float));
     L.o32 = take(rows32 * nq * sizeof(float));
     L.g32 = take(rows32 * (size_t)a.hidden_dim * sizeof(float));
-    // bf16 activations: row-major prefill rows, or fragment-major decode rows (up to 32,
+    // 16-bit activations: row-major prefill rows, or fragment-major decode rows (up to 32,
     // padding included)
     const size_t rows16 = std::max(maxT, (size_t)32);
     L.act16 = fp32 ? off : take(rows16 * (size_t)(a.dim > (int)nq ? a.dim : (int)nq) * 2);
