@@ -27,7 +27,7 @@ def model_of(wl, max_batch, weights=None):
     return runtime.LlamaModel(args, W)
 
 
-@pytest.mark.parametrize("dtype,batches", [("bf16", (20, 3)), ("bf16", (32, 6)), ("fp32", (2, 1))])
+@pytest.mark.parametrize("dtype,batches", [("bf16", (20, 3)), ("bf16", (32, 6)), ("fp16", (24, 5)), ("fp32", (2, 1))])
 def test_noalloc_decode_equals_decode_step(dtype, batches):
     """Prefill the batch, then at the next two positions: llama_decode_step, then
     llama_decode_step_noalloc on the same tokens and position (it rewrites the same K/V),
