@@ -54,10 +54,13 @@ typedef enum llama_dtype {
     LLAMA_BF16 = 0,  /* bf16 weights and KV cache; fp32 residual stream and accumulation */
     LLAMA_FP32 = 1,  /* fp32 weights, KV cache and arithmetic */
     LLAMA_FP16 = 2   /* fp16 weights and KV cache (the reference implementation's dtype): the
-                        fp32 model's vector-ALU kernels, fp32 residual stream and accumulation,
-                        and the tensors the method stores in 16 bits (normalised operands, q,
-                        K/V, attention output, gated FFN activation) rounded to fp16 (nearest
-                        even) where they are produced.  Weights 16-byte aligned, as for bf16 */
+                        bf16 model's kernels in their fp16 form (MFMA prefill GEMMs and flash
+                        attention, MFMA products for decode batches above 4, the vector GEMV
+                        for batches of 1..4; GQA decode attention on the vector kernel), fp32
+                        residual stream and accumulation, and the tensors the method stores in
+                        16 bits (normalised operands, q, K/V, attention output, gated FFN
+                        activation) rounded to fp16 (nearest even) where they are produced.
+                        Weights 16-byte aligned, as for bf16 */
 } llama_dtype;
 
 /*
@@ -153,9 +156,9 @@ llama_status llama_prefill(llama_ctx *c, const int32_t *d_tokens, int64_t ld_tok
 /* One single-token step, Transformer.forward(tokens[:, None], start_pos): row b's token is
  * d_tokens[b*ld_tokens].  Writes K/V at position start_pos, attends over
  * [0, start_pos] (no mask: every cached key is visible), and writes fp32 logits
- * [bsz][vocab_size] to d_logits.  Any bsz up to max_batch_size is served: bf16 batches of
- * 5..32 rows stream the weights through the skinny MFMA kernels, larger ones run the
- * prefill GEMMs with the single-token attention kernel.
+ * [bsz][vocab_size] to d_logits.  Any bsz up to max_batch_size is served: 16-bit (bf16 or
+ * fp16) batches of 5..32 rows stream the weights through the skinny MFMA kernels, larger
+ * ones run the prefill GEMMs with the single-token attention kernel.
  * Errors: INVALID_ARG if bsz < 1, bsz > max_batch_size, start_pos < 0,
  * start_pos >= max_seq_len, ld_tokens < 1, or a NULL pointer. */
 llama_status llama_decode_step(llama_ctx *c, const int32_t *d_tokens, int64_t ld_tokens,
@@ -175,7 +178,7 @@ llama_status llama_decode_step(llama_ctx *c, const int32_t *d_tokens, int64_t ld
  * the caller.
  * Errors: as llama_decode_step; UNSUPPORTED if bsz > 32; WORKSPACE if the step's scratch
  * exceeds the 32 MiB array (it needs about bsz * (3 * n_heads * head_dim + dim + hidden_dim)
- * * 4 bytes plus 64 * (dim + hidden_dim) bytes for bf16 models and the attention partials);
+ * * 4 bytes plus 64 * (dim + hidden_dim) bytes for 16-bit models and the attention partials);
  * HIP if the array's device address could not be taken at llama_init. */
 llama_status llama_decode_step_noalloc(llama_ctx *c, const int32_t *d_tokens, int64_t ld_tokens,
                                        int32_t bsz, int32_t start_pos, float *d_logits, void *stream);
@@ -239,7 +242,7 @@ enum llama_kernel_class {
     LLAMA_KC_GEMM_WO = 9,     /* prefill: MFMA wo + residual */
     LLAMA_KC_GEMM_W13 = 10,   /* prefill: MFMA [w1;w3] + SiLU gate */
     LLAMA_KC_GEMM_W2 = 11,    /* prefill: MFMA w2 + residual */
-    LLAMA_KC_RMSNORM = 12,    /* prefill: RMSNorm to bf16 */
+    LLAMA_KC_RMSNORM = 12,    /* prefill: RMSNorm to the 16-bit storage type */
     LLAMA_KC_COUNT = 13
 };
 llama_status llama_profile_select(llama_ctx *c, int32_t kernel_class);
