@@ -322,7 +322,9 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
 // LDS-ring variant: BM x 256 tiles (BM = 256: 8 waves as 4 x 2 of 64 x 128; BM = 128: 8 waves
 // as 2 x 4 of 64 x 64), K in stages of 32 through an LDS ring (4 slots at BM = 256, 6 at 128)
 // filled by global_load_lds_dwordx4 (global -> LDS without registers), loads issued NS - 1
-// stages ahead.  Long prefills use it with the LDS-staged epilogue below; short ones (a few
+// stages ahead; at BM = 256 the two waves of each SIMD alternate between reading fragments
+// and issuing MFMAs (ping-pong, below), so the MFMA unit is not idle while both wait on LDS.
+// Long prefills use it with the LDS-staged epilogue below; short ones (a few
 // hundred rows, where the weights are the traffic) split K over gridDim.z so enough
 // workgroups stream the weights: each split stores its raw fp32 tile [z][M][B row] and a
 // reduce pass applies the epilogue.  A wave's load instruction fills 1 KB of LDS
@@ -602,18 +604,89 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
 #pragma unroll
     for (int i = 0; i < NS - 1; ++i) issue(min(kt0 + i, kt1 - 1), ring + i * kSlot, ring + i * kSlot + BM * BKS);
 
-    // Step for stage kt held in slot S: wait for this wave's loads of that stage (those of the
-    // NS - 2 later stages may stay in flight) and for its LDS reads of the previous slot,
-    // barrier (now every wave's are done), refill the previous slot with stage kt + NS - 1,
-    // compute.
-    for (int kt = kt0; kt < kt1; kt += NS) {
+    if constexpr (BM == 256) {
+        // Ping-pong over the two waves of each SIMD (waves w and w + 4 of the workgroup; the
+        // dispatcher places wave w on SIMD w % 4): every wave takes each stage X as a memory
+        // phase (read this wave's 12 fragments of stage X into registers, refill the ring slot
+        // of stage X - 1 with stage X + NS - 1) and then a compute phase (its 32 MFMAs from
+        // those registers), with a barrier after each phase.
+        // The second group starts one barrier late and the first ends one barrier later, so
+        // phase 2X - 1 holds group 0's reads of stage X and group 1's MFMAs of stage X - 1, and
+        // phase 2X group 0's MFMAs of stage X and group 1's reads of it: on each SIMD one wave
+        // issues MFMAs while the other waits on LDS, and every wave passes the same number of
+        // barriers.  A slot is refilled only after both groups' reads of it have completed
+        // (each memory phase waits for its reads before its barrier); stage X + 1 is complete
+        // in every wave before the barrier that opens its first read (each wave's wait at the
+        // end of phase 2X leaves only the NS - 2 later stages in flight).
+        static_assert(TM == 4 && TN == 8, "12 fragment reads per stage");
+        const int grp = __builtin_amdgcn_readfirstlane(wid) >> 2;
+        const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)ring));
+        // fragment i of a wave sits 16 rows (1 KB) after fragment i - 1, with the same swizzle
+        const uint32_t va0 = lds0 + 2 * a_off[0], vb0 = lds0 + 2 * (BM * BKS + b_off[0]);
+        const int n = kt1 - kt0;
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWait) : "memory");    // stage 0 is in
+        if (grp) asm volatile("s_barrier" ::: "memory");
+        for (int x0 = 0; x0 < n; x0 += NS) {
 #pragma unroll
-        for (int S = 0; S < NS; ++S) {
-            if (kt + S < kt1) {
-                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kWait) : "memory");
-                uint16_t* prev = ring + ((S + NS - 1) % NS) * kSlot;
-                issue(min(kt + S + NS - 1, kt1 - 1), prev, prev + BM * BKS);
-                compute(ring + S * kSlot, ring + S * kSlot + BM * BKS);
+            for (int S = 0; S < NS; ++S) {
+                const int X = x0 + S;
+                if (X < n) {
+                    uint16_t* refill = ring + ((S + NS - 1) % NS) * kSlot;
+                    const uint32_t va = va0 + S * kSlot * 2, vb = vb0 + S * kSlot * 2;
+                    u32x4_t fa[TM], fb[TN];
+                    asm volatile(
+                        "ds_read_b128 %0, %12\n\t"
+                        "ds_read_b128 %1, %12 offset:1024\n\t"
+                        "ds_read_b128 %2, %12 offset:2048\n\t"
+                        "ds_read_b128 %3, %12 offset:3072\n\t"
+                        "ds_read_b128 %4, %13\n\t"
+                        "ds_read_b128 %5, %13 offset:1024\n\t"
+                        "ds_read_b128 %6, %13 offset:2048\n\t"
+                        "ds_read_b128 %7, %13 offset:3072\n\t"
+                        "ds_read_b128 %8, %13 offset:4096\n\t"
+                        "ds_read_b128 %9, %13 offset:5120\n\t"
+                        "ds_read_b128 %10, %13 offset:6144\n\t"
+                        "ds_read_b128 %11, %13 offset:7168\n\t"
+                        "s_waitcnt lgkmcnt(0)"
+                        : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3]), "=&v"(fb[0]), "=&v"(fb[1]),
+                          "=&v"(fb[2]), "=&v"(fb[3]), "=&v"(fb[4]), "=&v"(fb[5]), "=&v"(fb[6]), "=&v"(fb[7])
+                        : "v"(va), "v"(vb)
+                        : "memory");
+                    // the refill goes out after the reads, which then do not queue behind it
+                    issue(min(kt0 + X + NS - 1, kt1 - 1), refill, refill + BM * BKS);
+                    if (grp) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWait) : "memory");
+                    __builtin_amdgcn_sched_barrier(0);
+                    asm volatile("s_barrier" ::: "memory");
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        const v8_t bf = __builtin_bit_cast(v8_t, fb[j]);
+#pragma unroll
+                        for (int i = 0; i < TM; ++i)
+                            acc[i][j] = Mma<T16>::mma(__builtin_bit_cast(v8_t, fa[i]), bf, acc[i][j]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (!grp) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWait) : "memory");
+                    asm volatile("s_barrier" ::: "memory");
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+        if (!grp) asm volatile("s_barrier" ::: "memory");
+    } else {
+        // Step for stage kt held in slot S: wait for this wave's loads of that stage (those of
+        // the NS - 2 later stages may stay in flight) and for its LDS reads of the previous
+        // slot, barrier (now every wave's are done), refill the previous slot with stage
+        // kt + NS - 1, compute.
+        for (int kt = kt0; kt < kt1; kt += NS) {
+#pragma unroll
+            for (int S = 0; S < NS; ++S) {
+                if (kt + S < kt1) {
+                    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kWait) : "memory");
+                    uint16_t* prev = ring + ((S + NS - 1) % NS) * kSlot;
+                    issue(min(kt + S + NS - 1, kt1 - 1), prev, prev + BM * BKS);
+                    compute(ring + S * kSlot, ring + S * kSlot + BM * BKS);
+                }
             }
         }
     }
