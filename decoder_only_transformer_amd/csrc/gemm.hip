@@ -319,19 +319,17 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
 
 
 // ---------------------------------------------------------------------------------------
-// LDS-ring variant: BM x 256 tiles (BM = 256: 8 waves as 4 x 2 of 64 x 128; BM = 128: 8 waves
-// as 2 x 4 of 64 x 64), K in stages of 32 through an LDS ring (4 slots at BM = 256, 6 at 128)
-// filled by global_load_lds_dwordx4 (global -> LDS without registers), loads issued NS - 1
-// stages ahead; at BM = 256 the two waves of each SIMD alternate between reading fragments
-// and issuing MFMAs (ping-pong, below), so the MFMA unit is not idle while both wait on LDS.
-// Long prefills use it with the LDS-staged epilogue below; short ones (a few
-// hundred rows, where the weights are the traffic) split K over gridDim.z so enough
-// workgroups stream the weights: each split stores its raw fp32 tile [z][M][B row] and a
-// reduce pass applies the epilogue.  A wave's load instruction fills 1 KB of LDS
-// contiguously (lane i -> bytes 16i..16i+15), i.e. 16 rows x 4 chunks of a 64-byte row; each
-// lane fetches the global chunk (chunk ^ swz(row)), so a fragment read of (row, chunk) finds
-// it at slot chunk ^ swz(row) and the rows of a fragment land on distinct banks without
-// padding.
+// LDS-ring kernel of the 128-row tile (short prefills): 8 waves as 2 x 4 of 64 x 64, K in
+// stages of 32 through a 6-slot LDS ring filled by global_load_lds_dwordx4 (global -> LDS
+// without registers), loads issued NS - 1 stages ahead.  The 256-row tile (gemm_pp_kernel
+// below) fills its rings the same way, with stages of 64.  Short prefills (a few hundred rows,
+// where the weights are the traffic) split K over gridDim.z so enough workgroups stream the
+// weights: each split stores its raw fp32 tile [z][M][B row] and a reduce pass applies the
+// epilogue (or the next RMSNorm folds the residual products' partials).  A wave's load
+// instruction fills 1 KB of LDS contiguously (lane i -> bytes 16i..16i+15), i.e. 16 rows x 4
+// chunks of a 64-byte row; each lane fetches the global chunk (chunk ^ swz(row)), so a
+// fragment read of (row, chunk) finds it at slot chunk ^ swz(row) and the rows of a fragment
+// land on distinct banks without padding.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
@@ -487,7 +485,7 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[
 }
 
 template <int BM> struct BigShape;
-template <> struct BigShape<256> { static constexpr int WGN = 2, TN = 8, NS = 4; };   // 4 x 2 waves of 64 x 128; 128 KB
+template <> struct BigShape<256> { static constexpr int WGN = 2; };   // gemm_pp_kernel: 4 x 2 waves of 64 x 128
 template <> struct BigShape<128> { static constexpr int WGN = 4, TN = 4, NS = 6; };   // 2 x 4 waves of 64 x 64; 144 KB
 
 template <typename T16, int BM, int EPI>
@@ -604,89 +602,18 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
 #pragma unroll
     for (int i = 0; i < NS - 1; ++i) issue(min(kt0 + i, kt1 - 1), ring + i * kSlot, ring + i * kSlot + BM * BKS);
 
-    if constexpr (BM == 256) {
-        // Ping-pong over the two waves of each SIMD (waves w and w + 4 of the workgroup; the
-        // dispatcher places wave w on SIMD w % 4): every wave takes each stage X as a memory
-        // phase (read this wave's 12 fragments of stage X into registers, refill the ring slot
-        // of stage X - 1 with stage X + NS - 1) and then a compute phase (its 32 MFMAs from
-        // those registers), with a barrier after each phase.
-        // The second group starts one barrier late and the first ends one barrier later, so
-        // phase 2X - 1 holds group 0's reads of stage X and group 1's MFMAs of stage X - 1, and
-        // phase 2X group 0's MFMAs of stage X and group 1's reads of it: on each SIMD one wave
-        // issues MFMAs while the other waits on LDS, and every wave passes the same number of
-        // barriers.  A slot is refilled only after both groups' reads of it have completed
-        // (each memory phase waits for its reads before its barrier); stage X + 1 is complete
-        // in every wave before the barrier that opens its first read (each wave's wait at the
-        // end of phase 2X leaves only the NS - 2 later stages in flight).
-        static_assert(TM == 4 && TN == 8, "12 fragment reads per stage");
-        const int grp = __builtin_amdgcn_readfirstlane(wid) >> 2;
-        const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)ring));
-        // fragment i of a wave sits 16 rows (1 KB) after fragment i - 1, with the same swizzle
-        const uint32_t va0 = lds0 + 2 * a_off[0], vb0 = lds0 + 2 * (BM * BKS + b_off[0]);
-        const int n = kt1 - kt0;
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kWait) : "memory");    // stage 0 is in
-        if (grp) asm volatile("s_barrier" ::: "memory");
-        for (int x0 = 0; x0 < n; x0 += NS) {
+    // Step for stage kt held in slot S: wait for this wave's loads of that stage (those of
+    // the NS - 2 later stages may stay in flight) and for its LDS reads of the previous
+    // slot, barrier (now every wave's are done), refill the previous slot with stage
+    // kt + NS - 1, compute.
+    for (int kt = kt0; kt < kt1; kt += NS) {
 #pragma unroll
-            for (int S = 0; S < NS; ++S) {
-                const int X = x0 + S;
-                if (X < n) {
-                    uint16_t* refill = ring + ((S + NS - 1) % NS) * kSlot;
-                    const uint32_t va = va0 + S * kSlot * 2, vb = vb0 + S * kSlot * 2;
-                    u32x4_t fa[TM], fb[TN];
-                    asm volatile(
-                        "ds_read_b128 %0, %12\n\t"
-                        "ds_read_b128 %1, %12 offset:1024\n\t"
-                        "ds_read_b128 %2, %12 offset:2048\n\t"
-                        "ds_read_b128 %3, %12 offset:3072\n\t"
-                        "ds_read_b128 %4, %13\n\t"
-                        "ds_read_b128 %5, %13 offset:1024\n\t"
-                        "ds_read_b128 %6, %13 offset:2048\n\t"
-                        "ds_read_b128 %7, %13 offset:3072\n\t"
-                        "ds_read_b128 %8, %13 offset:4096\n\t"
-                        "ds_read_b128 %9, %13 offset:5120\n\t"
-                        "ds_read_b128 %10, %13 offset:6144\n\t"
-                        "ds_read_b128 %11, %13 offset:7168\n\t"
-                        "s_waitcnt lgkmcnt(0)"
-                        : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3]), "=&v"(fb[0]), "=&v"(fb[1]),
-                          "=&v"(fb[2]), "=&v"(fb[3]), "=&v"(fb[4]), "=&v"(fb[5]), "=&v"(fb[6]), "=&v"(fb[7])
-                        : "v"(va), "v"(vb)
-                        : "memory");
-                    // the refill goes out after the reads, which then do not queue behind it
-                    issue(min(kt0 + X + NS - 1, kt1 - 1), refill, refill + BM * BKS);
-                    if (grp) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWait) : "memory");
-                    __builtin_amdgcn_sched_barrier(0);
-                    asm volatile("s_barrier" ::: "memory");
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        const v8_t bf = __builtin_bit_cast(v8_t, fb[j]);
-#pragma unroll
-                        for (int i = 0; i < TM; ++i)
-                            acc[i][j] = Mma<T16>::mma(__builtin_bit_cast(v8_t, fa[i]), bf, acc[i][j]);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (!grp) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWait) : "memory");
-                    asm volatile("s_barrier" ::: "memory");
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        }
-        if (!grp) asm volatile("s_barrier" ::: "memory");
-    } else {
-        // Step for stage kt held in slot S: wait for this wave's loads of that stage (those of
-        // the NS - 2 later stages may stay in flight) and for its LDS reads of the previous
-        // slot, barrier (now every wave's are done), refill the previous slot with stage
-        // kt + NS - 1, compute.
-        for (int kt = kt0; kt < kt1; kt += NS) {
-#pragma unroll
-            for (int S = 0; S < NS; ++S) {
-                if (kt + S < kt1) {
-                    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kWait) : "memory");
-                    uint16_t* prev = ring + ((S + NS - 1) % NS) * kSlot;
-                    issue(min(kt + S + NS - 1, kt1 - 1), prev, prev + BM * BKS);
-                    compute(ring + S * kSlot, ring + S * kSlot + BM * BKS);
-                }
+        for (int S = 0; S < NS; ++S) {
+            if (kt + S < kt1) {
+                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kWait) : "memory");
+                uint16_t* prev = ring + ((S + NS - 1) % NS) * kSlot;
+                issue(min(kt + S + NS - 1, kt1 - 1), prev, prev + BM * BKS);
+                compute(ring + S * kSlot, ring + S * kSlot + BM * BKS);
             }
         }
     }
@@ -710,8 +637,175 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
             }
         return;
     }
-    if constexpr (BM == 256 && EPI != EPI_STORE) {
-        static_assert(TN == 8 && WN == 128 && NS * kSlot >= 8 * 64 * 64 * 2, "16 KB of ring per wave");
+    static_assert(BM == 128, "the 256-row tile runs gemm_pp_kernel");
+    epilogue<T16, BN, WGN, TM, TN, EPI>(a, acc, m0, tile_n, wm, wn, lane);
+}
+
+// 256 x 256 tile with K in stages of 64 (the 256-row tile of both the long and the short
+// path).  Same wave grid and accumulators as gemm_big_kernel<256> (8 waves as 4 x 2 of
+// 64 x 128), but a stage row is 128 bytes, a whole cache line: one load instruction fills 8
+// rows x 128 B, where 32-element stages fill 16 rows x 64 B and need twice the L2 requests for
+// the same bytes (the request rate, not the bytes, bounded the 32-element ring).
+//
+// LDS: an A ring of 3 slots and a B ring of 2, 32 KB each (160 KB).  Waves w and w + 4 share a
+// SIMD; group 0 (waves 0..3) computes A rows 0..127 of the tile and group 1 rows 128..255, so
+// each group reads, and itself loads, only its half of an A slot, while both read every B row.
+// Every wave takes each half-stage u (stage u / 2, K elements 32 (u % 2) .. + 31 of it) as a
+// memory phase (its 12 fragments into registers, then 4 ring loads: B of stage u / 2 + 1 on
+// even u, its group's A half of stage u / 2 + 2 on odd u) and then a compute phase (32 MFMAs),
+// with a barrier after each phase; group 1 runs one phase behind group 0, so on each SIMD one
+// wave issues MFMAs while the other reads LDS.  A slot is refilled only after every reader
+// has finished with its previous stage (B: both groups' last reads are one and two phases
+// before the refills; A: the group's own last read is two phases before), and each wave waits
+// at the end of half-stage 2Y + 1 for all its loads but the newest batch, so stage Y + 1 is
+// complete in every wave before the barrier that opens its first read.
+template <typename T16, int EPI>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a, int n_tm, int n_tn) {
+    typedef typename Mma<T16>::v8 v8_t;
+    constexpr int BM = 256, BN = kBigBN, BK = 64, WGN = 2, TM = 4, TN = 8, WM = 64, WN = BN / WGN;
+    constexpr int kSlot = 256 * BK;          // elements of one A or B slot (256 rows x 128 B)
+    constexpr int NA = 3, NB = 2;
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[(NA + NB) * kSlot];
+    uint16_t* const aring = ring;
+    uint16_t* const bring = ring + NA * kSlot;
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int wm = wid / WGN, wn = wid % WGN;
+    const int grp = __builtin_amdgcn_readfirstlane(wid) >> 2;
+    int tile_m, tile_n;
+    if (!tile_of(blockIdx.x, n_tm, n_tn, tile_m, tile_n)) return;
+    const int m0 = tile_m * BM;
+
+    // Loads: lane -> row lane / 8 of the instruction's 8 rows and LDS chunk lane % 8, which
+    // holds the row's global chunk (lane % 8) ^ (row % 8) (rows start at multiples of 8).
+    const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lane >> 3);
+    const uint16_t* ap[4];
+    const uint16_t* bp[4];
+    int a_dst[4], b_dst[4];      // first row of each load instruction, as slot element offsets
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r0 = grp * 128 + ((wid & 3) * 4 + i) * 8;
+        const int gm = min(m0 + r0 + lrow, a.M - 1);
+        ap[i] = static_cast<const uint16_t*>(a.a) + (size_t)gm * a.lda + lchunk * 8;
+        a_dst[i] = r0 * BK;
+        const int rb = (wid * 4 + i) * 8;
+        bool ok = true;
+        bp[i] = b_row_ptr<BN, WGN, EPI>(a, tile_n, rb + lrow, ok) + lchunk * 8;
+        b_dst[i] = rb * BK;
+    }
+    const int nk_all = a.K / BK;
+    const int kt0 = (int)((int64_t)nk_all * blockIdx.z / gridDim.z);
+    const int kt1 = (int)((int64_t)nk_all * (blockIdx.z + 1) / gridDim.z);
+    const int n = kt1 - kt0;
+    auto issue_a = [&](int kt, int slot) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_void_t*)(ap[i] + (size_t)kt * BK),
+                                             (lds_void_t*)(aring + slot * kSlot + a_dst[i]), 16, 0, 0);
+    };
+    auto issue_b = [&](int kt, int slot) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_void_t*)(bp[i] + (size_t)kt * BK),
+                                             (lds_void_t*)(bring + slot * kSlot + b_dst[i]), 16, 0, 0);
+    };
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // This lane's fragment 0 in a slot, half-stage h: row * 128 + ((4h + g) ^ (row % 8)) * 16
+    // bytes, row = (first row of the wave) + lane % 16; fragment i sits 16 rows (2 KB) further
+    // with the same chunk (the rows differ by multiples of 8).
+    const int fr = lane & 15, g = lane >> 4;
+    const uint32_t la = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)aring));
+    const uint32_t lb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)bring));
+    const uint32_t fa0 = la + (wm * WM + fr) * 128 + ((g ^ (fr & 7)) << 4);
+    const uint32_t fa1 = la + (wm * WM + fr) * 128 + (((4 + g) ^ (fr & 7)) << 4);
+    const uint32_t fb0 = lb + (wn * WN + fr) * 128 + ((g ^ (fr & 7)) << 4);
+    const uint32_t fb1 = lb + (wn * WN + fr) * 128 + (((4 + g) ^ (fr & 7)) << 4);
+
+    auto half_stage = [&](uint32_t va, uint32_t vb, bool odd, int next_kt, int next_slot) {
+        u32x4_t fa[TM], fb[TN];
+        asm volatile(
+            "ds_read_b128 %0, %12\n\t"
+            "ds_read_b128 %1, %12 offset:2048\n\t"
+            "ds_read_b128 %2, %12 offset:4096\n\t"
+            "ds_read_b128 %3, %12 offset:6144\n\t"
+            "ds_read_b128 %4, %13\n\t"
+            "ds_read_b128 %5, %13 offset:2048\n\t"
+            "ds_read_b128 %6, %13 offset:4096\n\t"
+            "ds_read_b128 %7, %13 offset:6144\n\t"
+            "ds_read_b128 %8, %13 offset:8192\n\t"
+            "ds_read_b128 %9, %13 offset:10240\n\t"
+            "ds_read_b128 %10, %13 offset:12288\n\t"
+            "ds_read_b128 %11, %13 offset:14336\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3]), "=&v"(fb[0]), "=&v"(fb[1]),
+              "=&v"(fb[2]), "=&v"(fb[3]), "=&v"(fb[4]), "=&v"(fb[5]), "=&v"(fb[6]), "=&v"(fb[7])
+            : "v"(va), "v"(vb)
+            : "memory");
+        if (odd) {
+            issue_a(next_kt, next_slot);
+            // all of this wave's loads but the newest batch (A of stage Y + 2) are in
+            if (grp) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        } else {
+            issue_b(next_kt, next_slot);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const v8_t bf = __builtin_bit_cast(v8_t, fb[j]);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                acc[i][j] = Mma<T16>::mma(__builtin_bit_cast(v8_t, fa[i]), bf, acc[i][j]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (odd && !grp) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Prologue: A(0), B(0), A(1) (past the end: duplicates of the last stage, so every wave
+    // always has the same loads outstanding); wait for A(0) and B(0).
+    issue_a(kt0, 0);
+    issue_b(kt0, 0);
+    issue_a(min(kt0 + 1, kt1 - 1), 1);
+    asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    if (grp) asm volatile("s_barrier" ::: "memory");
+    int sa = 0, sb = 0;     // slots of stage Y
+    for (int Y = 0; Y < n; ++Y) {
+        const int sa2 = sa == 0 ? 2 : sa - 1;   // slot of stage Y + 2: (Y + 2) % 3
+        half_stage(fa0 + sa * (kSlot * 2), fb0 + sb * (kSlot * 2), false, min(kt0 + Y + 1, kt1 - 1), sb ^ 1);
+        half_stage(fa1 + sa * (kSlot * 2), fb1 + sb * (kSlot * 2), true, min(kt0 + Y + 2, kt1 - 1), sa2);
+        sa = sa == 2 ? 0 : sa + 1;
+        sb ^= 1;
+    }
+    if (!grp) asm volatile("s_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // the duplicate tail loads
+    if (gridDim.z > 1) {
+        // split K: raw fp32 tile of this split, [z][M][B row] with B rows n_tn * BN wide
+        const int rq = (lane >> 4) * 4;
+        const size_t ldp = (size_t)n_tn * BN;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int p = tile_n * BN + wn * WN + j * 16 + fr;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = m0 + wm * WM + i * 16 + rq + e;
+                    if (m < a.M) a.part[((size_t)blockIdx.z * a.M + m) * ldp + p] = acc[i][j][e];
+                }
+            }
+        return;
+    }
+    if constexpr (EPI != EPI_STORE) {
+        static_assert((NA + NB) * kSlot >= 8 * 64 * 64 * 2, "16 KB of ring per wave");
         epilogue_staged<T16, EPI>(a, acc, m0, tile_n, wm, wn, lane, reinterpret_cast<float*>(ring) + wid * 64 * 64);
     } else {
         epilogue<T16, BN, WGN, TM, TN, EPI>(a, acc, m0, tile_n, wm, wn, lane);
@@ -738,8 +832,11 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
         while (splits > 1 && (size_t)splits * a.M * ldp > a.part_cap) --splits;
     }
     if (a.deferred) *a.deferred = 0;
-    launch_kernel((gemm_big_kernel<T16, BM, EPI>), dim3(per_xcd * kXcds, 1, splits), dim3(512), 0, s, a,
-                  n_tm, n_tn);
+    if constexpr (BM == 256)
+        launch_kernel((gemm_pp_kernel<T16, EPI>), dim3(per_xcd * kXcds, 1, splits), dim3(512), 0, s, a, n_tm, n_tn);
+    else
+        launch_kernel((gemm_big_kernel<T16, BM, EPI>), dim3(per_xcd * kXcds, 1, splits), dim3(512), 0, s, a,
+                      n_tm, n_tn);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     const size_t n = (size_t)a.M * a.N;
