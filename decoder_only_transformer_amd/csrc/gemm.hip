@@ -320,26 +320,25 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
 
 // ---------------------------------------------------------------------------------------
 // LDS-ring kernel of the 128-row tile (short prefills): 8 waves as 2 x 4 of 64 x 64, K in
-// stages of 32 through a 6-slot LDS ring filled by global_load_lds_dwordx4 (global -> LDS
+// stages of 64 through a 3-slot LDS ring filled by global_load_lds_dwordx4 (global -> LDS
 // without registers), loads issued NS - 1 stages ahead.  The 256-row tile (gemm_pp_kernel
-// below) fills its rings the same way, with stages of 64.  Short prefills (a few hundred rows,
+// below) fills its rings the same way.  Short prefills (a few hundred rows,
 // where the weights are the traffic) split K over gridDim.z so enough workgroups stream the
 // weights: each split stores its raw fp32 tile [z][M][B row] and a reduce pass applies the
 // epilogue (or the next RMSNorm folds the residual products' partials).  A wave's load
-// instruction fills 1 KB of LDS contiguously (lane i -> bytes 16i..16i+15), i.e. 16 rows x 4
-// chunks of a 64-byte row; each lane fetches the global chunk (chunk ^ swz(row)), so a
-// fragment read of (row, chunk) finds it at slot chunk ^ swz(row) and the rows of a fragment
-// land on distinct banks without padding.
+// instruction fills 1 KB of LDS contiguously (lane i -> bytes 16i..16i+15), i.e. 8 whole
+// 128-byte rows: rows of half a cache line would cost twice the L2 requests for the same
+// bytes, and the request rate is what bounds these loads.
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-constexpr int kBigBN = 256, kBigBK = 32;
+constexpr int kBigBN = 256;
 
-// The LDS serves a 16-byte read 8 lanes at a time from a 128-byte bank window; rows are 64
-// bytes, so rows r and r + 2 share a window offset.  XOR-ing the chunk with (row / 2) % 4
-// puts the 8 rows of a lane group on 8 distinct 16-byte slots (measured: the previous
-// (row / 4) % 4 gave every fragment read a 2-way conflict).
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+// LDS rows are 128 bytes (64 K elements).  The LDS serves a 16-byte read 8 lanes at a time;
+// the 8 lanes of a fragment read take 8 consecutive rows at one logical chunk, and storing
+// chunk c of row r at slot c ^ (r % 8) puts them on 8 distinct 16-byte slots of the banks
+// (without it all 8 would share one).  The load instructions write 1 KB contiguously, so
+// each lane fetches the global chunk that belongs at its LDS slot.
 
 // Tile shapes: wave grid, accumulator tiles per wave, LDS ring slots (NS - 1 stages of
 // loads in flight).  The 128-row tile is for short prefills, where the weights are the
@@ -486,19 +485,19 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[
 
 template <int BM> struct BigShape;
 template <> struct BigShape<256> { static constexpr int WGN = 2; };   // gemm_pp_kernel: 4 x 2 waves of 64 x 128
-template <> struct BigShape<128> { static constexpr int WGN = 4, TN = 4, NS = 6; };   // 2 x 4 waves of 64 x 64; 144 KB
+template <> struct BigShape<128> { static constexpr int WGN = 4, TN = 4, NS = 3; };   // 2 x 4 waves of 64 x 64; 3 x 48 KB
 
 template <typename T16, int BM, int EPI>
 __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int n_tn) {
+    static_assert(BM == 128, "the 256-row tile runs gemm_pp_kernel");
     typedef typename Mma<T16>::v8 v8_t;
-    constexpr int BN = kBigBN, BKS = kBigBK;
+    constexpr int BN = kBigBN, BK = 64;                    // K elements per stage (128 B a row)
     constexpr int WGN = BigShape<BM>::WGN, TM = 4, TN = BigShape<BM>::TN, WM = 64, WN = BN / WGN;
-    constexpr int A_INS = BM / 128, B_INS = BN / 128;    // 16-row load instructions per wave
+    constexpr int A_INS = BM / 64, B_INS = BN / 64;      // 8-row load instructions per wave
     constexpr int NS = BigShape<BM>::NS;
     constexpr int kWait = (NS - 2) * (A_INS + B_INS);    // loads of the later stages in flight
-    constexpr int kSlot = (BM + BN) * BKS;                 // elements of one ring slot (A then B)
-    // The fragment reads are asm blocks that wait for their own results, so the compiler
-    // sees no LDS read it would have to order after the ring's DMA writes.
+    constexpr int kSlot = (BM + BN) * BK;                  // elements of one ring slot (A then B)
+    constexpr uint32_t kSlotBytes = kSlot * 2;
     __shared__ __attribute__((aligned(1024))) uint16_t ring[NS * kSlot];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -507,25 +506,23 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
     if (!tile_of(blockIdx.x, n_tm, n_tn, tile_m, tile_n)) return;
     const int m0 = tile_m * BM;
 
-    // This lane's A rows and B rows (one per load instruction of the wave: rows
-    // (INS * wid + i) * 16 + lane / 4 of the tile).
+    // Loads: one instruction fills 8 rows x 128 B; lane -> row lane / 8 of them and LDS chunk
+    // lane % 8, which holds the row's global chunk (lane % 8) ^ (row % 8) (rows start at
+    // multiples of 8).  Instruction i of wave w covers rows (INS * w + i) * 8 ...
+    const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lane >> 3);
     const uint16_t* ap[A_INS];
     const uint16_t* bp[B_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
-        const int row = (A_INS * wid + i) * 16 + (lane >> 2);
-        const int gc = (lane & 3) ^ swz(row);
-        const int gm = min(m0 + row, a.M - 1);
-        ap[i] = static_cast<const uint16_t*>(a.a) + (size_t)gm * a.lda + gc * 8;
+        const int gm = min(m0 + (A_INS * wid + i) * 8 + lrow, a.M - 1);
+        ap[i] = static_cast<const uint16_t*>(a.a) + (size_t)gm * a.lda + lchunk * 8;
     }
 #pragma unroll
     for (int i = 0; i < B_INS; ++i) {
-        const int row = (B_INS * wid + i) * 16 + (lane >> 2);
-        const int gc = (lane & 3) ^ swz(row);
         bool ok = true;
-        bp[i] = b_row_ptr<BN, WGN, EPI>(a, tile_n, row, ok) + gc * 8;
+        bp[i] = b_row_ptr<BN, WGN, EPI>(a, tile_n, (B_INS * wid + i) * 8 + lrow, ok) + lchunk * 8;
     }
-    const int nk_all = a.K / BKS;
+    const int nk_all = a.K / BK;
     const int kt0 = (int)((int64_t)nk_all * blockIdx.z / gridDim.z);
     const int kt1 = (int)((int64_t)nk_all * (blockIdx.z + 1) / gridDim.z);
 
@@ -535,85 +532,72 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // This lane's fragment 0 of a slot for the K half h of a stage: row * 128 +
+    // ((4h + g) ^ (row % 8)) * 16 bytes, row = (first row of the wave) + lane % 16; fragment i
+    // sits 16 rows (2 KB) further with the same chunk.
     const int fr = lane & 15, g = lane >> 4;
-    int a_off[TM], b_off[TN];      // element offsets of this lane's fragments in a slot
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int row = wm * WM + i * 16 + fr;
-        a_off[i] = row * BKS + ((g ^ swz(row)) * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int row = wn * WN + j * 16 + fr;
-        b_off[j] = row * BKS + ((g ^ swz(row)) * 8);
-    }
+    const uint32_t lr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)ring));
+    const uint32_t fa[2] = {lr + (wm * WM + fr) * 128 + ((g ^ (fr & 7)) << 4),
+                            lr + (wm * WM + fr) * 128 + (((4 + g) ^ (fr & 7)) << 4)};
+    const uint32_t fb[2] = {lr + (BM + wn * WN + fr) * 128 + ((g ^ (fr & 7)) << 4),
+                            lr + (BM + wn * WN + fr) * 128 + (((4 + g) ^ (fr & 7)) << 4)};
 
-    auto issue = [&](int kt, uint16_t* Ad, uint16_t* Bd) {
+    auto issue = [&](int kt, uint16_t* slot) {
 #pragma unroll
         for (int i = 0; i < A_INS; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_void_t*)(ap[i] + (size_t)kt * BKS),
-                                             (lds_void_t*)(Ad + (A_INS * wid + i) * 16 * BKS), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_void_t*)(ap[i] + (size_t)kt * BK),
+                                             (lds_void_t*)(slot + (A_INS * wid + i) * 8 * BK), 16, 0, 0);
 #pragma unroll
         for (int i = 0; i < B_INS; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_void_t*)(bp[i] + (size_t)kt * BKS),
-                                             (lds_void_t*)(Bd + (B_INS * wid + i) * 16 * BKS), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_void_t*)(bp[i] + (size_t)kt * BK),
+                                             (lds_void_t*)(slot + BM * BK + (B_INS * wid + i) * 8 * BK), 16, 0, 0);
     };
-    auto compute = [&](const uint16_t* As_, const uint16_t* Bs_) {
+    auto compute = [&](uint32_t va, uint32_t vb) {
         // Fragment reads go out in asm blocks that wait for their own results: the compiler
         // then sees no LDS read it would have to order after the ring's DMA writes (it cannot
-        // tell the slots apart across the loop and would drain every load).  Four groups,
-        // each followed by the MFMAs it feeds, so a group's reads overlap the MFMAs before it.
-        const uint32_t ab = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)As_));
-        const uint32_t bb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)Bs_));
+        // tell the slots apart across the loop and would drain every load).  The four A and
+        // first two B fragments, then 8 MFMAs with the last two B reads in flight, then 8.
+        static_assert(TM == 4 && TN == 4, "one mfma8_read2 group and one plain group");
         u32x4_t ra[TM], rb[TN];
         asm volatile(
             "ds_read_b128 %0, %6\n\t"
-            "ds_read_b128 %1, %7\n\t"
-            "ds_read_b128 %2, %8\n\t"
-            "ds_read_b128 %3, %9\n\t"
-            "ds_read_b128 %4, %10\n\t"
-            "ds_read_b128 %5, %11\n\t"
+            "ds_read_b128 %1, %6 offset:2048\n\t"
+            "ds_read_b128 %2, %6 offset:4096\n\t"
+            "ds_read_b128 %3, %6 offset:6144\n\t"
+            "ds_read_b128 %4, %7\n\t"
+            "ds_read_b128 %5, %7 offset:2048\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(ra[0]), "=&v"(ra[1]), "=&v"(ra[2]), "=&v"(ra[3]), "=&v"(rb[0]), "=&v"(rb[1])
-            : "v"(ab + 2 * a_off[0]), "v"(ab + 2 * a_off[1]), "v"(ab + 2 * a_off[2]),
-              "v"(ab + 2 * a_off[3]), "v"(bb + 2 * b_off[0]), "v"(bb + 2 * b_off[1])
+            : "v"(va), "v"(vb)
             : "memory");
-        static_assert(TM == 4, "mfma8_read2 covers four A fragments");
-        // groups 0 .. TN/2 - 2: MFMAs of group jg with group jg + 1's B reads in flight
+        mfma8_read2<T16>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], acc[0][1], acc[1][1], acc[2][1], acc[3][1],
+                         ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3], vb + 4096, vb + 6144);
 #pragma unroll
-        for (int jg = 0; jg + 1 < TN / 2; ++jg)
-            mfma8_read2<T16>(acc[0][2 * jg], acc[1][2 * jg], acc[2][2 * jg], acc[3][2 * jg],
-                        acc[0][2 * jg + 1], acc[1][2 * jg + 1], acc[2][2 * jg + 1], acc[3][2 * jg + 1],
-                        ra[0], ra[1], ra[2], ra[3], rb[2 * jg], rb[2 * jg + 1], rb[2 * jg + 2], rb[2 * jg + 3],
-                        bb + 2 * b_off[2 * jg + 2], bb + 2 * b_off[2 * jg + 3]);
-        // last group
-        constexpr int jl = TN / 2 - 1;
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const v8_t bf = __builtin_bit_cast(v8_t, rb[2 * jl + jj]);
+        for (int jj = 2; jj < 4; ++jj) {
+            const v8_t bf = __builtin_bit_cast(v8_t, rb[jj]);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
-                acc[i][2 * jl + jj] = Mma<T16>::mma(__builtin_bit_cast(v8_t, ra[i]), bf, acc[i][2 * jl + jj]);
+                acc[i][jj] = Mma<T16>::mma(__builtin_bit_cast(v8_t, ra[i]), bf, acc[i][jj]);
         }
     };
 
     // Prologue: stages 0..NS-2 (past the end: duplicates of the last stage, so every step has
     // the same number of loads outstanding).
 #pragma unroll
-    for (int i = 0; i < NS - 1; ++i) issue(min(kt0 + i, kt1 - 1), ring + i * kSlot, ring + i * kSlot + BM * BKS);
+    for (int i = 0; i < NS - 1; ++i) issue(min(kt0 + i, kt1 - 1), ring + i * kSlot);
 
     // Step for stage kt held in slot S: wait for this wave's loads of that stage (those of
     // the NS - 2 later stages may stay in flight) and for its LDS reads of the previous
     // slot, barrier (now every wave's are done), refill the previous slot with stage
-    // kt + NS - 1, compute.
+    // kt + NS - 1, compute both K halves of the stage.
     for (int kt = kt0; kt < kt1; kt += NS) {
 #pragma unroll
         for (int S = 0; S < NS; ++S) {
             if (kt + S < kt1) {
                 asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kWait) : "memory");
-                uint16_t* prev = ring + ((S + NS - 1) % NS) * kSlot;
-                issue(min(kt + S + NS - 1, kt1 - 1), prev, prev + BM * BKS);
-                compute(ring + S * kSlot, ring + S * kSlot + BM * BKS);
+                issue(min(kt + S + NS - 1, kt1 - 1), ring + ((S + NS - 1) % NS) * kSlot);
+                compute(fa[0] + S * kSlotBytes, fb[0] + S * kSlotBytes);
+                compute(fa[1] + S * kSlotBytes, fb[1] + S * kSlotBytes);
             }
         }
     }
@@ -622,7 +606,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
     asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     if (gridDim.z > 1) {
         // split K: raw fp32 tile of this split, [z][M][B row] with B rows n_tn * BN wide
-        const int fr = lane & 15, rq = (lane >> 4) * 4;
+        const int rq = (lane >> 4) * 4;
         const size_t ldp = (size_t)n_tn * BN;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -637,7 +621,6 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
             }
         return;
     }
-    static_assert(BM == 128, "the 256-row tile runs gemm_pp_kernel");
     epilogue<T16, BN, WGN, TM, TN, EPI>(a, acc, m0, tile_n, wm, wn, lane);
 }
 
@@ -812,9 +795,11 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a, int n_tm, int 
     }
 }
 
-// K splits for a short prefill (M <= kShortRows) on the LDS-ring kernel: about one
-// workgroup per CU, at least 8 k-stages per split, partials within the workspace.
+// K splits for a short prefill (M <= kShortRows) on the LDS-ring kernels: about one
+// workgroup per CU, at least kMinSplitK K elements (4 stages) per split, partials within the
+// workspace.
 constexpr int kShortRows = 512;
+constexpr int kMinSplitK = 256;
 
 template <typename T16, int BM, int EPI>
 hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
@@ -827,7 +812,7 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
         // one workgroup per CU (its LDS ring takes most of the CU), all in one round
         const int tiles = n_tn * n_tm;
         splits = std::max(1, 256 / tiles);
-        splits = std::min(splits, std::max(1, a.K / kBigBK / 8));
+        splits = std::min(splits, std::max(1, a.K / kMinSplitK));
         splits = std::min(splits, kMaxBigSplit);
         while (splits > 1 && (size_t)splits * a.M * ldp > a.part_cap) --splits;
     }
