@@ -319,7 +319,7 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
 
 
 // ---------------------------------------------------------------------------------------
-// LDS-ring kernel of the 128-row tile (short prefills): 8 waves as 2 x 4 of 64 x 64, K in
+// LDS-ring kernel of the 128 x 128 tile (short prefills): 8 waves as 2 x 4 of 64 x 32, K in
 // stages of 64 through a 3-slot LDS ring filled by global_load_lds_dwordx4 (global -> LDS
 // without registers), loads issued NS - 1 stages ahead.  The 256-row tile (gemm_pp_kernel
 // below) fills its rings the same way.  Short prefills (a few hundred rows,
@@ -339,57 +339,6 @@ constexpr int kBigBN = 256;
 // chunk c of row r at slot c ^ (r % 8) puts them on 8 distinct 16-byte slots of the banks
 // (without it all 8 would share one).  The load instructions write 1 KB contiguously, so
 // each lane fetches the global chunk that belongs at its LDS slot.
-
-// Tile shapes: wave grid, accumulator tiles per wave, LDS ring slots (NS - 1 stages of
-// loads in flight).  The 128-row tile is for short prefills, where the weights are the
-// traffic: its smaller A tile leaves room for a deeper ring.
-// Eight MFMAs of one fragment group, c[i][jj] += a[i] * b[jj] (i < 4, jj < 2), with the two
-// B fragment reads of the next group issued ahead of them and waited for at the end of the
-// block: the reads are in flight while the MFMAs run, and no asm output is left pending.
-// The accumulators chain MFMA to MFMA on the same registers (no wait states needed); the
-// new fragments go to registers no MFMA of this block reads (early clobber).
-template <typename T16>
-__device__ __forceinline__ void mfma8_read2(f32x4& c00, f32x4& c10, f32x4& c20, f32x4& c30,
-                                            f32x4& c01, f32x4& c11, f32x4& c21, f32x4& c31,
-                                            const u32x4_t& a0, const u32x4_t& a1, const u32x4_t& a2,
-                                            const u32x4_t& a3, const u32x4_t& b0, const u32x4_t& b1,
-                                            u32x4_t& n0, u32x4_t& n1, uint32_t addr0, uint32_t addr1) {
-    if constexpr (std::is_same<T16, f16>::value) {
-        asm volatile(
-            "ds_read_b128 %8, %10\n\t"
-            "ds_read_b128 %9, %11\n\t"
-            "v_mfma_f32_16x16x32_f16 %0, %12, %16, %0\n\t"
-            "v_mfma_f32_16x16x32_f16 %1, %13, %16, %1\n\t"
-            "v_mfma_f32_16x16x32_f16 %2, %14, %16, %2\n\t"
-            "v_mfma_f32_16x16x32_f16 %3, %15, %16, %3\n\t"
-            "v_mfma_f32_16x16x32_f16 %4, %12, %17, %4\n\t"
-            "v_mfma_f32_16x16x32_f16 %5, %13, %17, %5\n\t"
-            "v_mfma_f32_16x16x32_f16 %6, %14, %17, %6\n\t"
-            "v_mfma_f32_16x16x32_f16 %7, %15, %17, %7\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "+v"(c00), "+v"(c10), "+v"(c20), "+v"(c30), "+v"(c01), "+v"(c11), "+v"(c21), "+v"(c31),
-              "=&v"(n0), "=&v"(n1)
-            : "v"(addr0), "v"(addr1), "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b0), "v"(b1)
-            : "memory");
-    } else {
-        asm volatile(
-            "ds_read_b128 %8, %10\n\t"
-            "ds_read_b128 %9, %11\n\t"
-            "v_mfma_f32_16x16x32_bf16 %0, %12, %16, %0\n\t"
-            "v_mfma_f32_16x16x32_bf16 %1, %13, %16, %1\n\t"
-            "v_mfma_f32_16x16x32_bf16 %2, %14, %16, %2\n\t"
-            "v_mfma_f32_16x16x32_bf16 %3, %15, %16, %3\n\t"
-            "v_mfma_f32_16x16x32_bf16 %4, %12, %17, %4\n\t"
-            "v_mfma_f32_16x16x32_bf16 %5, %13, %17, %5\n\t"
-            "v_mfma_f32_16x16x32_bf16 %6, %14, %17, %6\n\t"
-            "v_mfma_f32_16x16x32_bf16 %7, %15, %17, %7\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "+v"(c00), "+v"(c10), "+v"(c20), "+v"(c30), "+v"(c01), "+v"(c11), "+v"(c21), "+v"(c31),
-              "=&v"(n0), "=&v"(n1)
-            : "v"(addr0), "v"(addr1), "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b0), "v"(b1)
-            : "memory");
-    }
-}
 
 // Epilogue of the 256 x 256 kernel through LDS.  A wave's accumulators (64 rows x 128
 // columns, 4 consecutive rows of one column per lane and tile) go to its own 16 KB of the
@@ -483,18 +432,20 @@ __device__ __forceinline__ void epilogue_staged(const GemmArgs& a, f32x4 (&acc)[
     }
 }
 
-template <int BM> struct BigShape;
-template <> struct BigShape<256> { static constexpr int WGN = 2; };   // gemm_pp_kernel: 4 x 2 waves of 64 x 128
-template <> struct BigShape<128> { static constexpr int WGN = 4, TN = 4, NS = 3; };   // 2 x 4 waves of 64 x 64; 3 x 48 KB
+// Tile shapes: wave grid, accumulator tiles per wave, LDS ring slots (NS - 1 stages of
+// loads in flight).
+template <int BM, int BN> struct BigShape;
+template <> struct BigShape<256, 256> { static constexpr int WGN = 2; };   // gemm_pp_kernel: 4 x 2 waves of 64 x 128
+template <> struct BigShape<128, 128> { static constexpr int WGN = 4, TN = 2, NS = 3; };   // 2 x 4 waves of 64 x 32; 3 x 32 KB
 
-template <typename T16, int BM, int EPI>
+template <typename T16, int BM, int BN, int EPI>
 __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int n_tn) {
     static_assert(BM == 128, "the 256-row tile runs gemm_pp_kernel");
     typedef typename Mma<T16>::v8 v8_t;
-    constexpr int BN = kBigBN, BK = 64;                    // K elements per stage (128 B a row)
-    constexpr int WGN = BigShape<BM>::WGN, TM = 4, TN = BigShape<BM>::TN, WM = 64, WN = BN / WGN;
+    constexpr int BK = 64;                                 // K elements per stage (128 B a row)
+    constexpr int WGN = BigShape<BM, BN>::WGN, TM = 4, TN = BigShape<BM, BN>::TN, WM = 64, WN = BN / WGN;
     constexpr int A_INS = BM / 64, B_INS = BN / 64;      // 8-row load instructions per wave
-    constexpr int NS = BigShape<BM>::NS;
+    constexpr int NS = BigShape<BM, BN>::NS;
     constexpr int kWait = (NS - 2) * (A_INS + B_INS);    // loads of the later stages in flight
     constexpr int kSlot = (BM + BN) * BK;                  // elements of one ring slot (A then B)
     constexpr uint32_t kSlotBytes = kSlot * 2;
@@ -556,8 +507,8 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
         // Fragment reads go out in asm blocks that wait for their own results: the compiler
         // then sees no LDS read it would have to order after the ring's DMA writes (it cannot
         // tell the slots apart across the loop and would drain every load).  The four A and
-        // first two B fragments, then 8 MFMAs with the last two B reads in flight, then 8.
-        static_assert(TM == 4 && TN == 4, "one mfma8_read2 group and one plain group");
+        // two B fragments of the K half, then its 8 MFMAs.
+        static_assert(TM == 4 && TN == 2, "4 x 2 fragments");
         u32x4_t ra[TM], rb[TN];
         asm volatile(
             "ds_read_b128 %0, %6\n\t"
@@ -570,10 +521,8 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a, int n_tm, int
             : "=&v"(ra[0]), "=&v"(ra[1]), "=&v"(ra[2]), "=&v"(ra[3]), "=&v"(rb[0]), "=&v"(rb[1])
             : "v"(va), "v"(vb)
             : "memory");
-        mfma8_read2<T16>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], acc[0][1], acc[1][1], acc[2][1], acc[3][1],
-                         ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3], vb + 4096, vb + 6144);
 #pragma unroll
-        for (int jj = 2; jj < 4; ++jj) {
+        for (int jj = 0; jj < TN; ++jj) {
             const v8_t bf = __builtin_bit_cast(v8_t, rb[jj]);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -801,12 +750,19 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a, int n_tm, int 
 constexpr int kShortRows = 512;
 constexpr int kMinSplitK = 256;
 
-template <typename T16, int BM, int EPI>
+// Tile width of the 128-row short-prefill kernel: 128 columns.  Against 256-column tiles
+// (measured on the 128-row 7B prefill, 5.35 -> 4.97 ms) the [w1; w3] product needs no K split
+// (172 tiles, its SiLU gate applied in the kernel's own epilogue, no reduce pass), q/k/v two
+// splits instead of five and wo / w2 eight instead of sixteen, so half or less of the fp32
+// partials are written and read back.
+constexpr int kShortBN = 128;
+
+template <typename T16, int BM, int BN, int EPI>
 hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
-    const int ncols = (EPI == EPI_SWIGLU) ? kBigBN / 2 : kBigBN;
+    const int ncols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
     const int n_tn = (a.N + ncols - 1) / ncols, n_tm = (a.M + BM - 1) / BM;
     const int per_xcd = (n_tn * n_tm + kXcds - 1) / kXcds;
-    const size_t ldp = (size_t)n_tn * kBigBN;
+    const size_t ldp = (size_t)n_tn * BN;
     int splits = 1;
     if (a.M <= kShortRows && a.part && (EPI == EPI_QKV || EPI == EPI_RESID || EPI == EPI_SWIGLU)) {
         // one workgroup per CU (its LDS ring takes most of the CU), all in one round
@@ -817,11 +773,13 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
         while (splits > 1 && (size_t)splits * a.M * ldp > a.part_cap) --splits;
     }
     if (a.deferred) *a.deferred = 0;
-    if constexpr (BM == 256)
+    if constexpr (BM == 256) {
+        static_assert(BN == kBigBN, "the 256-row tile is 256 x 256");
         launch_kernel((gemm_pp_kernel<T16, EPI>), dim3(per_xcd * kXcds, 1, splits), dim3(512), 0, s, a, n_tm, n_tn);
-    else
-        launch_kernel((gemm_big_kernel<T16, BM, EPI>), dim3(per_xcd * kXcds, 1, splits), dim3(512), 0, s, a,
+    } else {
+        launch_kernel((gemm_big_kernel<T16, BM, BN, EPI>), dim3(per_xcd * kXcds, 1, splits), dim3(512), 0, s, a,
                       n_tm, n_tn);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     const size_t n = (size_t)a.M * a.N;
@@ -835,7 +793,7 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
                       (int64_t)ldp, a.resid, a.ldr);
     } else if constexpr (EPI == EPI_SWIGLU) {
         launch_kernel(swiglu_reduce_kernel<T16>, rgrid, dim3(256), 0, s, a.part, splits, a.M, a.N,
-                      (int64_t)ldp, kBigBN, kBigBN / BigShape<BM>::WGN, static_cast<uint16_t*>(a.out16),
+                      (int64_t)ldp, BN, BN / BigShape<BM, BN>::WGN, static_cast<uint16_t*>(a.out16),
                       a.ldo16);
     } else {
         return launch_rope_scatter_parts(a.part, splits, (int64_t)ldp, a.M, a.qkv, s, a.wtype);
@@ -851,8 +809,8 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
     // one workgroup per CU streams them, the epilogue applied by a reduce pass.
     if constexpr (EPI == EPI_QKV || EPI == EPI_RESID || EPI == EPI_SWIGLU) {
         if (a.M <= kShortRows && a.part) {
-            if (a.M <= 128) return launch_big<T16, 128, EPI>(a, s);
-            return launch_big<T16, 256, EPI>(a, s);
+            if (a.M <= 128) return launch_big<T16, 128, kShortBN, EPI>(a, s);
+            return launch_big<T16, 256, kBigBN, EPI>(a, s);
         }
     }
     if (a.M <= 256) return launch_tile<T16, 128, 64, 2, 2, EPI>(a, s);
@@ -886,7 +844,7 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
                 GemmArgs a1 = a;
                 a1.M = M1;
                 a1.deferred = nullptr;
-                const hipError_t e = launch_big<T16, 256, EPI>(a1, s);
+                const hipError_t e = launch_big<T16, 256, kBigBN, EPI>(a1, s);
                 if (e != hipSuccess) return e;
                 GemmArgs a2 = a;
                 a2.M = M2;
@@ -895,11 +853,12 @@ hipError_t launch_epi(const GemmArgs& a, hipStream_t s) {
                 if constexpr (EPI == EPI_RESID) a2.resid = a.resid + (size_t)M1 * a.ldr;
                 if constexpr (EPI == EPI_SWIGLU) a2.out16 = static_cast<uint16_t*>(a.out16) + (size_t)M1 * a.ldo16;
                 if constexpr (EPI == EPI_QKV) a2.qkv.row0 = a.qkv.row0 + M1;
-                return M2 <= 128 ? launch_big<T16, 128, EPI>(a2, s) : launch_big<T16, 256, EPI>(a2, s);
+                return M2 <= 128 ? launch_big<T16, 128, kShortBN, EPI>(a2, s)
+                                 : launch_big<T16, 256, kBigBN, EPI>(a2, s);
             }
         }
     }
-    return launch_big<T16, 256, EPI>(a, s);
+    return launch_big<T16, 256, kBigBN, EPI>(a, s);
 }
 
 template <typename T16>
