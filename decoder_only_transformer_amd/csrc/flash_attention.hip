@@ -88,20 +88,24 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
     const int qstride = a.n_heads * HD;
     const int64_t kv_row = (int64_t)a.n_kv_heads * HD;
 
-    // This lane's query rows: column fr of the wave's S^T tiles qt = 0, 1.  Rows past the
-    // prompt compute with the last position's keys and are not stored.
+    // This lane's query rows: column fr of the wave's S^T tiles qt = 0, 1.  The tiles end at
+    // the last row, so when the rows are not a whole number of tiles the partial tile is the
+    // first one (rows -pad .. kRows - pad - 1), which sees the fewest keys.  Its rows before
+    // the prompt compute with the first position's keys and are not stored.
+    const int pad = n_qt * kRows - a.seqlen * n_rep;
     int s_idx[kQT], head[kQT], qpos[kQT];
     bool row_ok[kQT];
     v8_t qf[kQT][KS];
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
-        const int r_local = qtile * kRows + wid * 16 * kQT + qt * 16 + fr;
+        const int r_raw = qtile * kRows + wid * 16 * kQT + qt * 16 + fr - pad;
+        row_ok[qt] = r_raw >= 0;
+        const int r_local = row_ok[qt] ? r_raw : 0;
         s_idx[qt] = r_local / n_rep;                       // position within the prompt
         head[qt] = kvh * n_rep + r_local % n_rep;
-        row_ok[qt] = s_idx[qt] < a.seqlen;
-        qpos[qt] = a.start_pos + (row_ok[qt] ? s_idx[qt] : a.seqlen - 1);   // absolute position
+        qpos[qt] = a.start_pos + s_idx[qt];                // absolute position
         // Q fragments (fp32 holding 16-bit values in the q buffer -> exact conversion)
-        const float* qp = a.q + ((size_t)b * a.seqlen + (row_ok[qt] ? s_idx[qt] : 0)) * qstride + head[qt] * HD;
+        const float* qp = a.q + ((size_t)b * a.seqlen + s_idx[qt]) * qstride + head[qt] * HD;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u16x8_t v;
@@ -112,9 +116,9 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
     }
 
     // Keys visible to the workgroup: up to the largest position among its rows.
-    const int last_row = min(qtile * kRows + kRows - 1, a.seqlen * n_rep - 1);
+    const int last_row = qtile * kRows + kRows - 1 - pad;
     const int kend = a.start_pos + last_row / n_rep + 1;     // exclusive
-    const int first_row = qtile * kRows;
+    const int first_row = max(qtile * kRows - pad, 0);
     const int kfull = a.start_pos + first_row / n_rep + 1;   // keys < kfull are visible to all rows
 
     // Online softmax in base 2: scores are scaled by scale * log2(e), p = 2^(s - m).  The
@@ -169,22 +173,34 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
         __syncthreads();
         if (k0 + kKeys < kend) load_tile(k0 + kKeys);
 
-        // ---- S^T for 4 key tiles of 16: lane holds keys k0 + 16j + 4g + e of query column fr
+        // ---- S^T for 4 key tiles of 16: lane holds keys k0 + 16j + 4g + e of query column fr.
+        //      The K fragments of key tile j + 1 are read while the MFMAs of tile j run.
         f32x4 st[kQT][4];
+        v8_t kf[2][KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[0][ks] = *reinterpret_cast<const v8_t*>(&Ks[buf][fr][ks * 32 + g * 8]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+            if (j < 3) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    kf[(j + 1) & 1][ks] = *reinterpret_cast<const v8_t*>(&Ks[buf][16 * (j + 1) + fr][ks * 32 + g * 8]);
+            }
 #pragma unroll
             for (int qt = 0; qt < kQT; ++qt) st[qt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const v8_t kf = *reinterpret_cast<const v8_t*>(&Ks[buf][16 * j + fr][ks * 32 + g * 8]);
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int qt = 0; qt < kQT; ++qt)
-                    st[qt][j] = Mma<T16>::mma(kf, qf[qt][ks], st[qt][j]);
-            }
+                    st[qt][j] = Mma<T16>::mma(kf[j & 1][ks], qf[qt][ks], st[qt][j]);
         }
-        // ---- scale, causal mask (tiles reaching past the first row's position only), online
-        //      softmax per query (= per lane column; lanes l, l^16, l^32, l^48 share one)
+        // first V fragment of the O^T product, read while the softmax runs
+        v8_t vf[2];
+        vf[0] = *reinterpret_cast<const v8_t*>(&Vt[buf][fr][8 * g]);
+        // ---- causal mask (tiles reaching past the first row's position only), online softmax
+        //      per query (= per lane column; lanes l, l^16, l^32, l^48 share one).  The row
+        //      maximum is taken over the raw scores; the scale enters the exponent through one
+        //      FMA: p = 2^(s c2 - m).
         const bool diag = k0 + kKeys > kfull;
         u32x4_t phi[kQT][2], plo[kQT][2];
 #pragma unroll
@@ -196,7 +212,7 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int key = k0 + 16 * j + 4 * g + e;
-                        const float v = key > qpos[qt] ? -INFINITY : st[qt][j][e] * c2;
+                        const float v = key > qpos[qt] ? -INFINITY : st[qt][j][e];
                         st[qt][j][e] = v;
                         tmax = fmaxf(tmax, v);
                     }
@@ -204,14 +220,11 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float v = st[qt][j][e] * c2;
-                        st[qt][j][e] = v;
-                        tmax = fmaxf(tmax, v);
-                    }
+                    for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, st[qt][j][e]);
             }
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+            tmax *= c2;
             if (__any(tmax > m[qt] + 8.f)) {
                 const float mn = fmaxf(m[qt], tmax);
                 const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn);   // 0 on the first tile
@@ -225,8 +238,8 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; e += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(st[qt][j][e] - m[qt]);
-                    const float p1 = __builtin_amdgcn_exp2f(st[qt][j][e + 1] - m[qt]);
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[qt][j][e], c2, -m[qt]));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[qt][j][e + 1], c2, -m[qt]));
                     psum += p0 + p1;
                     // P = hi + lo, both 16-bit; k-slot of key (j, e) in the permuted PV order:
                     // half kk = j / 2, slot (j % 2) * 4 + e of the lane group's 8
@@ -241,18 +254,20 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
             l[qt] += psum;
         }
 
-        // ---- O^T += V^T P^T over the two 32-key halves (permuted k order)
+        // ---- O^T += V^T P^T over the two 32-key halves (permuted k order); fragment i + 1 is
+        //      read while the MFMAs of fragment i run
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-            for (int t = 0; t < DT; ++t) {
+        for (int i = 0; i < 2 * DT; ++i) {
+            const int kk = i / DT, t = i % DT;
+            if (i + 1 < 2 * DT) {
+                const int kn = (i + 1) / DT, tn = (i + 1) % DT;
                 // the 8 keys of lane group g in this half, already in k-slot order
-                const v8_t vf = *reinterpret_cast<const v8_t*>(&Vt[buf][16 * t + fr][32 * kk + 8 * g]);
+                vf[(i + 1) & 1] = *reinterpret_cast<const v8_t*>(&Vt[buf][16 * tn + fr][32 * kn + 8 * g]);
+            }
 #pragma unroll
-                for (int qt = 0; qt < kQT; ++qt) {
-                    o[qt][t] = Mma<T16>::mma(vf, __builtin_bit_cast(v8_t, phi[qt][kk]), o[qt][t]);
-                    o[qt][t] = Mma<T16>::mma(vf, __builtin_bit_cast(v8_t, plo[qt][kk]), o[qt][t]);
-                }
+            for (int qt = 0; qt < kQT; ++qt) {
+                o[qt][t] = Mma<T16>::mma(vf[i & 1], __builtin_bit_cast(v8_t, phi[qt][kk]), o[qt][t]);
+                o[qt][t] = Mma<T16>::mma(vf[i & 1], __builtin_bit_cast(v8_t, plo[qt][kk]), o[qt][t]);
             }
         }
     }
