@@ -88,52 +88,16 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
     const int qstride = a.n_heads * HD;
     const int64_t kv_row = (int64_t)a.n_kv_heads * HD;
 
-    // This lane's query rows: column fr of the wave's S^T tiles qt = 0, 1.  The tiles end at
-    // the last row, so when the rows are not a whole number of tiles the partial tile is the
-    // first one (rows -pad .. kRows - pad - 1), which sees the fewest keys.  Its rows before
-    // the prompt compute with the first position's keys and are not stored.
+    // Query rows of the workgroup: the tiles end at the last row, so when the rows are not a
+    // whole number of tiles the partial tile is the first one (rows -pad .. kRows - pad - 1),
+    // which sees the fewest keys.
     const int pad = n_qt * kRows - a.seqlen * n_rep;
-    int s_idx[kQT], head[kQT], qpos[kQT];
-    bool row_ok[kQT];
-    v8_t qf[kQT][KS];
-#pragma unroll
-    for (int qt = 0; qt < kQT; ++qt) {
-        const int r_raw = qtile * kRows + wid * 16 * kQT + qt * 16 + fr - pad;
-        row_ok[qt] = r_raw >= 0;
-        const int r_local = row_ok[qt] ? r_raw : 0;
-        s_idx[qt] = r_local / n_rep;                       // position within the prompt
-        head[qt] = kvh * n_rep + r_local % n_rep;
-        qpos[qt] = a.start_pos + s_idx[qt];                // absolute position
-        // Q fragments (fp32 holding 16-bit values in the q buffer -> exact conversion)
-        const float* qp = a.q + ((size_t)b * a.seqlen + s_idx[qt]) * qstride + head[qt] * HD;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u16x8_t v;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = Mma<T16>::bits(qp[ks * 32 + g * 8 + e]);
-            qf[qt][ks] = __builtin_bit_cast(v8_t, v);
-        }
-    }
 
     // Keys visible to the workgroup: up to the largest position among its rows.
     const int last_row = qtile * kRows + kRows - 1 - pad;
     const int kend = a.start_pos + last_row / n_rep + 1;     // exclusive
     const int first_row = max(qtile * kRows - pad, 0);
     const int kfull = a.start_pos + first_row / n_rep + 1;   // keys < kfull are visible to all rows
-
-    // Online softmax in base 2: scores are scaled by scale * log2(e), p = 2^(s - m).  The
-    // running max m is raised (and O, l rescaled) only when some row's tile max exceeds it by
-    // more than 8, so p <= 2^8 between raises; the final O / l is the same quotient.
-    const float c2 = a.scale * 1.4426950408889634f;
-    float m[kQT], l[kQT];
-    f32x4 o[kQT][DT];
-#pragma unroll
-    for (int qt = 0; qt < kQT; ++qt) {
-        m[qt] = -INFINITY;
-        l[qt] = 0.f;
-#pragma unroll
-        for (int t = 0; t < DT; ++t) o[qt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
 
     const uint16_t* kbase = static_cast<const uint16_t*>(a.cache_k) + (size_t)b * a.max_seq * kv_row + (size_t)kvh * HD;
     const uint16_t* vbase = static_cast<const uint16_t*>(a.cache_v) + (size_t)b * a.max_seq * kv_row + (size_t)kvh * HD;
@@ -166,7 +130,48 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
         }
     };
 
+    // the first K/V tile is in flight while the Q fragments load
     if (kend > 0) load_tile(0);
+
+    // This lane's query rows: column fr of the wave's S^T tiles qt = 0, 1.  Rows before the
+    // prompt (in a partial first tile) compute with the first position's keys and are not
+    // stored.
+    int s_idx[kQT], head[kQT], qpos[kQT];
+    bool row_ok[kQT];
+    v8_t qf[kQT][KS];
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
+        const int r_raw = qtile * kRows + wid * 16 * kQT + qt * 16 + fr - pad;
+        row_ok[qt] = r_raw >= 0;
+        const int r_local = row_ok[qt] ? r_raw : 0;
+        s_idx[qt] = r_local / n_rep;                       // position within the prompt
+        head[qt] = kvh * n_rep + r_local % n_rep;
+        qpos[qt] = a.start_pos + s_idx[qt];                // absolute position
+        // Q fragments (fp32 holding 16-bit values in the q buffer -> exact conversion)
+        const float* qp = a.q + ((size_t)b * a.seqlen + s_idx[qt]) * qstride + head[qt] * HD;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u16x8_t v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = Mma<T16>::bits(qp[ks * 32 + g * 8 + e]);
+            qf[qt][ks] = __builtin_bit_cast(v8_t, v);
+        }
+    }
+
+    // Online softmax in base 2: with c2 = scale * log2(e), p = 2^(s c2 - m).  The
+    // running max m is raised (and O, l rescaled) only when some row's tile max exceeds it by
+    // more than 8, so p <= 2^8 between raises; the final O / l is the same quotient.
+    const float c2 = a.scale * 1.4426950408889634f;
+    float m[kQT], l[kQT];
+    f32x4 o[kQT][DT];
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
+        m[qt] = -INFINITY;
+        l[qt] = 0.f;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) o[qt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
     for (int k0 = 0, it = 0; k0 < kend; k0 += kKeys, ++it) {
         const int buf = it & 1;
         store_tile(buf);
