@@ -341,6 +341,14 @@ SMALL_BF16 = {
                                                 batch=2, prompt_len=0, prompt_len_range=(40, 180),
                                                 gen_steps=20, weight_seed=17, prompt_seed=117,
                                                 max_seq_len=256, rope_theta=500000.0),
+    # widths that are not whole 128-column tiles: dim 576 (9 heads of 64), so q/k/v (1728 rows)
+    # and wo / w2 (576) end in half tiles of the 128 x 128 short-prefill kernel, and the
+    # 80..126 prompt rows a partial 128-row tile (also the first, partial, query tile of the
+    # attention)
+    "ragged_n": synth.WORKLOADS["tiny_fp32"].with_(name="small_bf16_ragged_n", dtype="bf16", n_heads=9,
+                                                   n_kv_heads=9, dim=576, hidden_dim=1600, vocab_size=1000,
+                                                   batch=2, prompt_len=0, prompt_len_range=(40, 63),
+                                                   gen_steps=16, weight_seed=24, prompt_seed=124, max_seq_len=128),
     # long prompts: 4 x 600 = 2400 prefill rows take the 256x256 GEMM path (ragged tiles)
     # with its fused RoPE / cache-append epilogue
     "long": synth.WORKLOADS["tiny_fp32"].with_(name="small_bf16_long", dtype="bf16", n_heads=4,
