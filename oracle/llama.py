@@ -14,7 +14,8 @@ Sources (cited by page title and section):
 
 Readings taken where the pages leave a step open:
   R1  RoPE frequency of pair i is theta**(-2i/head_dim)  (the pages fix only theta and
-      "one frequency per pair"; parity unpinned beyond that convention).
+      "one frequency per pair"; pinned against transformers' LlamaRotaryEmbedding, an
+      independent implementation of the same model family, in tests/test_oracle_pins.py).
   R2  RoPE pairs are adjacent elements (2i, 2i+1) of each head = (real, imag).
   R4  grouped-query head h reads kv head floor(h / n_rep) (repeat-interleave).
   R5  softmax in the working precision with max subtraction.

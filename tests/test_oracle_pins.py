@@ -165,6 +165,37 @@ def test_rope_preserves_norms_and_dot_depends_on_offset_only():
     assert abs(e - d[0]) > 1e-6
 
 
+@pytest.mark.parametrize("hd,theta", [(32, 10000.0), (64, 10000.0), (128, 10000.0), (128, 500000.0)])
+def test_rope_schedule_matches_transformers_llama_rotary_embedding(hd, theta):
+    """Reading R1 (pair i of a head turns at theta^(-2i/head_dim)) against an independent
+    implementation of the same model family: transformers' LlamaRotaryEmbedding and
+    apply_rotary_pos_emb.  That implementation pairs element i with element i + head_dim/2
+    ("rotate half") where the pages pair adjacent elements (2i, 2i+1), so a head is compared
+    through the permutation that maps adjacent pair i to (i, i + head_dim/2).  Its tables are
+    fp32 (the frequencies, then angles t * f rounded once), hence the tolerances."""
+    transformers = pytest.importorskip("transformers")
+    from transformers.models.llama.modeling_llama import LlamaRotaryEmbedding, apply_rotary_pos_emb
+    cfg = transformers.LlamaConfig(hidden_size=4 * hd, num_attention_heads=4, rope_theta=theta,
+                                   max_position_embeddings=4096)
+    emb = LlamaRotaryEmbedding(config=cfg)
+    # the frequency schedule itself
+    np.testing.assert_allclose(emb.inv_freq.double().numpy(), oracle.rope_frequencies(hd, theta), rtol=2e-7)
+    # the rotation of whole heads at a few positions
+    rng = np.random.default_rng(hd)
+    pos = np.array([0, 1, 2, 5, 17, 64, 100])
+    x = rng.standard_normal((1, len(pos), 3, hd))                    # (B, S, H, hd), adjacent pairs
+    perm = np.concatenate([np.arange(0, hd, 2), np.arange(1, hd, 2)])
+    xt = torch.from_numpy(x[..., perm]).float().transpose(1, 2)      # (B, H, S, hd), rotate-half layout
+    cos, sin = emb(xt, torch.from_numpy(pos)[None])
+    q, _ = apply_rotary_pos_emb(xt, xt, cos, sin)
+    y_lib = q.transpose(1, 2).double().numpy()
+    y = oracle.apply_rope(x, pos, theta)[..., perm]
+    np.testing.assert_allclose(y, y_lib, atol=1e-4, rtol=1e-4)
+    # a sign slip or a pairing slip would be far outside that: the other rotation direction
+    y_wrong = oracle.apply_rope(x, -pos, theta)[..., perm]
+    assert np.abs(y_wrong - y_lib).max() > 0.1
+
+
 # ----------------------------------------------------------------------------- attention
 
 def _sdpa(q, k, v, start_pos):
