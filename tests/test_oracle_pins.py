@@ -315,6 +315,52 @@ def test_model_matches_torch_library_composition(kvh):
                                rtol=1e-10, atol=1e-10)
 
 
+@pytest.mark.parametrize("kvh", [4, 2])
+def test_model_matches_transformers_llama(kvh):
+    """The whole forward against an independent implementation of the same model family:
+    transformers' LlamaForCausalLM (eager attention) with the same weights.  Its RoPE pairs
+    element i with i + head_dim/2 where the pages pair adjacent elements, so the rows of
+    wq and wk are permuted within each head (adjacent pair i -> rows i and i + head_dim/2);
+    the scores, and everything after them, are unchanged by that relabelling.  Its RMSNorm
+    and RoPE tables run in fp32 whatever the model dtype, hence the tolerance."""
+    transformers = pytest.importorskip("transformers")
+    a = small_args(n_kv_heads=kvh)
+    W = random_weights(a, seed=21)
+    hd = a.head_dim
+    cfg = transformers.LlamaConfig(vocab_size=a.vocab_size, hidden_size=a.dim, intermediate_size=a.hidden_dim,
+                                   num_hidden_layers=a.n_layers, num_attention_heads=a.n_heads,
+                                   num_key_value_heads=a.kv_heads, rms_norm_eps=a.norm_eps,
+                                   rope_theta=a.rope_theta, max_position_embeddings=64,
+                                   tie_word_embeddings=False, attention_bias=False, mlp_bias=False)
+    cfg._attn_implementation = "eager"
+    model = transformers.LlamaForCausalLM(cfg).double().eval()
+    perm_head = np.concatenate([np.arange(0, hd, 2), np.arange(1, hd, 2)])
+
+    def heads(w, n):   # rows of each head reordered from adjacent pairs to rotate-half
+        return np.concatenate([w[h * hd:(h + 1) * hd][perm_head] for h in range(n)])
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))  # noqa: E731
+    with torch.no_grad():
+        model.model.embed_tokens.weight.copy_(t(W["tok_embeddings"]))
+        for L, layer in zip(W["layers"], model.model.layers):
+            layer.input_layernorm.weight.copy_(t(L["attention_norm"]))
+            layer.self_attn.q_proj.weight.copy_(t(heads(L["wq"], a.n_heads)))
+            layer.self_attn.k_proj.weight.copy_(t(heads(L["wk"], a.kv_heads)))
+            layer.self_attn.v_proj.weight.copy_(t(L["wv"]))
+            layer.self_attn.o_proj.weight.copy_(t(L["wo"]))
+            layer.post_attention_layernorm.weight.copy_(t(L["ffn_norm"]))
+            layer.mlp.gate_proj.weight.copy_(t(L["w1"]))
+            layer.mlp.up_proj.weight.copy_(t(L["w3"]))
+            layer.mlp.down_proj.weight.copy_(t(L["w2"]))
+        model.model.norm.weight.copy_(t(W["norm"]))
+        model.lm_head.weight.copy_(t(W["output"]))
+        tokens = np.random.default_rng(22).integers(0, a.vocab_size, size=(2, 11))
+        ref = model(torch.from_numpy(tokens)).logits.numpy()
+    got = oracle.Oracle(a, W, 2, dtype=np.float64).forward(tokens, 0)
+    scale = np.abs(ref).max()
+    assert scale > 0.5
+    np.testing.assert_allclose(got, ref, rtol=0, atol=2e-6 * scale)   # measured 1.3e-7 * scale
+
+
 @pytest.mark.parametrize("storage", ["bf16", "bf16_kv", "fp16"])
 def test_storage_modes_round_exactly_at_the_stated_points(storage):
     """The storage modes against the torch composition with the roundings placed by hand at
