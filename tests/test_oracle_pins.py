@@ -648,3 +648,26 @@ def test_sample_top_p_temperature_closed_form_and_logprob():
     # the log-prob is of the untempered softmax
     tok, lp = oracle.sample_top_p(logits, 2.0, 1.0, np.array([0.0]))
     assert abs(lp[0] - np.log(p1[tok[0]])) < 1e-12
+
+
+@pytest.mark.parametrize("temperature,top_p", [(0.7, 0.8), (1.0, 0.5), (0.6, 0.95), (1.3, 0.3)])
+def test_sample_top_p_distribution_matches_transformers_warpers(temperature, top_p):
+    """Readings R20 and R22 (which tokens top-p keeps, the renormalised draw) against an
+    independent implementation: transformers' TemperatureLogitsWarper + TopPLogitsWarper.
+    The oracle's inverse-CDF draw at the uniforms (k + 1/2) / N, k < N, takes each kept
+    token for its share of N within 1, so the draw counts give the renormalised kept
+    distribution, which must equal the softmax of the warped logits (tokens the library drops
+    never drawn).  Random logits, so no two cumulative masses tie with top_p."""
+    transformers = pytest.importorskip("transformers")
+    from transformers.generation.logits_process import TemperatureLogitsWarper, TopPLogitsWarper
+    rng = np.random.default_rng(int(top_p * 100))
+    V, N = 50, 4000
+    logits = rng.standard_normal(V)
+    warped = TopPLogitsWarper(top_p)(None, TemperatureLogitsWarper(temperature)(None, torch.from_numpy(logits)[None]))
+    p_lib = torch.softmax(warped, dim=-1)[0].numpy()
+    u = (np.arange(N) + 0.5) / N
+    tok, _ = oracle.sample_top_p(np.repeat(logits[None], N, axis=0), temperature, top_p, u)
+    freq = np.bincount(tok, minlength=V) / N
+    assert set(np.flatnonzero(freq)) <= set(np.flatnonzero(p_lib > 0))
+    np.testing.assert_allclose(freq, p_lib, atol=2.0 / N)
+    assert 1 < (p_lib > 0).sum() < V     # the case keeps some tokens and drops others
