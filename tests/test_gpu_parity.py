@@ -666,6 +666,23 @@ def test_llama2_7b_widths_one_layer_tail_rows_match_oracle():
     check_generate_rows(wl, W, prompts, tokens, logits, [0, 32])
 
 
+@pytest.mark.timeout(600)
+def test_llama2_7b_widths_one_layer_128_row_tail_matches_oracle():
+    """65 x 128 prefill rows at the 7B widths: after 32 whole rounds of 256-row tiles, the last
+    128 rows of every projection run as a second launch on the 128 x 128 short-prefill tile
+    (row offset into the q / cache rows, the residual and the gated output; q/k/v and wo / w2
+    split over K with their reduce passes, the gate unsplit).  The first row and the last
+    (whose whole prompt is in that tail) are checked against the oracle."""
+    wl = synth.WORKLOADS["llama2_7b_b1"].with_(name="llama2_7b_b65_one_layer", n_layers=1, batch=65,
+                                               prompt_len=128, gen_steps=4)
+    say(f"case {wl.name}")
+    W = synth.gen_weights(wl, device="cuda")
+    prompts = synth.prompts(wl)
+    assert len(prompts) * min(len(p) for p in prompts) == 65 * 128
+    tokens, logits, _ = gpu_generate(wl, W, prompts)
+    check_generate_rows(wl, W, prompts, tokens, logits, [0, 64])
+
+
 @pytest.mark.timeout(900)
 def test_llama2_7b_b1_generate_matches_oracle():
     """The 7B batch-1 workload at full depth, in the launch configuration bench.py times.
